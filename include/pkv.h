@@ -1,0 +1,217 @@
+/* pkv.h -- C ABI of libpkv: paged KV-cache decode attention on MI355X (gfx950).
+ *
+ * What the library computes (page title, section):
+ *  - "无 vLLM 环境下的 Paged-KV 与连续批处理调度" §1.2: the KV cache is cut into
+ *    fixed-size blocks (16 tokens by default) handed out from one global pool;
+ *    a sequence of length l holds ceil(l / block_size) blocks and wastes less
+ *    than one block. §2: the KV-bytes formula 2*L*H*d*s*B*bytes.
+ *  - "vLLM核心概念：PagedAttention、Continuous Batching、KV Cache等原理" §3.1: a
+ *    decode step attends the new token's query to every cached key/value;
+ *    §3.2: a per-sequence block table maps logical blocks to any physical
+ *    block, and sequences may share blocks, copied on the first divergent
+ *    write (copy-on-write).
+ *  - "连续批处理与KV缓存" §4.2: free blocks sit in one queue; allocation takes
+ *    from the front and freeing returns to the back, O(1) per block;
+ *    allocate fails when the queue is short, append reports "wait".
+ *  - "轻量级推理引擎实战：KV Cache 量化与连续批处理的底层优化" §三: symmetric
+ *    INT8 with one scale per (block, KV head): scale = max|x|/127 (1.0 for an
+ *    all-zero head), code = clamp(round(x/scale), -127, 127), x = code*scale.
+ *
+ * Conventions for every call:
+ *  - Status: PKV_OK (0) or a negative pkv_status. Argument and shape errors
+ *    are found on the host before anything is changed or launched; the
+ *    message is available from pkv_last_error() (thread-local).
+ *  - Allocator calls are host-only, all-or-nothing and O(1) per block.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream). Their pointer arguments are device
+ *    pointers on the pool's device unless marked "host".
+ *  - A pool is not thread-safe: one host thread (or a lock) per pool.
+ *  - Layout of the cache is private; pkv_read_block exports one block in a
+ *    canonical order for checks.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* bad argument or shape; nothing changed */
+  PKV_ERR_OOM = -2,          /* allocate: not enough free blocks; nothing changed */
+  PKV_ERR_NO_FREE_BLOCK = -3,/* append: pool empty, caller must wait or evict; nothing changed */
+  PKV_ERR_UNKNOWN_SEQ = -4,  /* a sequence id that the pool does not hold */
+  PKV_ERR_SEQ_EXISTS = -5,   /* allocate/fork onto an id already in use */
+  PKV_ERR_DEVICE = -6,       /* a HIP call failed (message has the HIP error) */
+  PKV_ERR_UNSUPPORTED = -7   /* valid but not implemented (e.g. head_dim 96) */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
+
+typedef struct pkv_pool pkv_pool;
+
+typedef struct {
+  int32_t num_layers;    /* L >= 1: each layer has its own K and V slice of every block */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t block_size;    /* bs: 16, 32 or 64 tokens per block */
+  int32_t num_blocks;    /* N >= 1 blocks in the pool (shared by all layers' slices) */
+  pkv_dtype kv_dtype;    /* PKV_F16 or PKV_I8 */
+  const int32_t* initial_free_order; /* host, optional: permutation of [0, N) giving the
+                                        initial queue front to back; NULL = 0..N-1.
+                                        Copied at create time. */
+  void* device_arena;    /* optional caller-owned device memory of at least
+                            pkv_pool_required_bytes(); the pool never frees it.
+                            NULL = the library allocates (hipMalloc) and frees. */
+  size_t arena_bytes;    /* size of device_arena */
+  int32_t host_only;     /* 1 = allocator only, no device memory or HIP calls
+                            (device entry points then return PKV_ERR_UNSUPPORTED) */
+} pkv_pool_config;
+
+typedef struct {
+  int64_t free_blocks;   /* blocks in the free queue */
+  int64_t used_blocks;   /* blocks with reference count > 0 */
+  int64_t shared_blocks; /* blocks with reference count > 1 */
+  int64_t cow_copies;    /* copy-on-write copies made since creation */
+  int64_t num_seqs;      /* live sequences */
+  int64_t total_blocks;  /* N */
+} pkv_stats;
+
+/* Device bytes a pool with this configuration needs (codes for all layers,
+ * K and V, plus the fp32 scales for INT8), rounded up to 256 bytes. */
+size_t pkv_pool_required_bytes(const pkv_pool_config* cfg);
+
+/* Create a pool. Validates the configuration (including that
+ * initial_free_order is a permutation). On success *out owns host state and,
+ * unless host_only or device_arena is given, device memory on the current
+ * HIP device. */
+pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out);
+
+/* Destroy a pool and free what it owns. NULL is a no-op. The caller makes
+ * sure no device work that uses the pool is still in flight. */
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* ---------------- host allocator ("连续批处理与KV缓存" §4.2) ---------------- */
+
+/* New sequence `seq` of n_tokens >= 0 tokens: ceil(n_tokens/bs) blocks from
+ * the front of the free queue, in order. slots_out (host, n_tokens entries,
+ * may be NULL) receives slot = block*bs + (t % bs) for t = 0..n_tokens-1.
+ * PKV_ERR_SEQ_EXISTS if seq is live; PKV_ERR_OOM if the queue is short. */
+pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out);
+
+/* Reserve n_new[i] >= 0 new token positions at the end of each seqs[i]
+ * (distinct, live ids), processed in argument order and increasing
+ * position. A position that starts a new logical block pops the queue
+ * front; the first write into a partly filled block whose reference count
+ * is above one pops a fresh block and copies the shared block's contents
+ * (all layers, K and V, codes and scales) into it, enqueued on `stream`
+ * (copy-on-write, "vLLM核心概念" §3.2). slots_out (host, sum(n_new) entries,
+ * may be NULL) receives the slots in the same order. All-or-nothing:
+ * PKV_ERR_NO_FREE_BLOCK if the queue cannot serve the whole call. */
+pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                                const int32_t* n_new, int64_t* slots_out, void* stream);
+
+/* Make `child` share every block of `parent` (reference counts + 1) with the
+ * same length. PKV_ERR_UNKNOWN_SEQ / PKV_ERR_SEQ_EXISTS as named. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child);
+
+/* Drop `seq`: each of its blocks loses one reference, in table order, and a
+ * block reaching zero goes to the BACK of the free queue. An unknown id is a
+ * no-op returning PKV_OK (the page's pop(request_id, [])). */
+pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Host export of block tables: table_out (host) [n][max_blocks] int32, row i
+ * = physical blocks of seqs[i] in logical order, padded with -1; lens_out
+ * (host) [n] = lengths. PKV_ERR_INVALID_ARG if a sequence holds more than
+ * max_blocks blocks. */
+pkv_status pkv_seq_block_table(const pkv_pool* pool, const int64_t* seqs, int32_t n,
+                               int32_t max_blocks, int32_t* table_out, int32_t* lens_out);
+
+/* Length in tokens of a live sequence (host). */
+pkv_status pkv_seq_length(const pkv_pool* pool, int64_t seq, int64_t* len_out);
+
+pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out);
+
+/* Host copy of the free queue, front first (for checks). cap >= N. *n_out =
+ * number of entries written. */
+pkv_status pkv_pool_free_queue(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* ------------------------------ device work ------------------------------ */
+
+/* Store new tokens' K and V of one layer at their slots
+ * ("轻量级推理引擎实战" §三 quantize_block, per (block, KV head)).
+ * k, v: [n_tokens][num_kv_heads][head_dim] of in_dtype (F32, F16, BF16),
+ * contiguous. slot_mapping: [n_tokens] int64 (device). Tokens that map to
+ * one block must be adjacent in the token order with consecutive rows, the
+ * first of them at row r meaning the block already holds rows [0, r) -- as
+ * produced by pkv_seq_allocate / pkv_seq_append_slots. Slots are not
+ * otherwise checked on the device.
+ *   F16 cache: each value is rounded to binary16, ties to even.
+ *   I8 cache: for each touched (block, head, K|V) with new values X and r
+ *   rows already present: if r == 0 the scale is max|X|/127 (1.0 when
+ *   max|X| <= 1e-6) and X is encoded with it; else, with m_old =
+ *   max|old code| * old scale, X is encoded with the old scale when
+ *   max|X| <= m_old, otherwise the scale becomes max|X|/127 and the old
+ *   codes are re-encoded from their dequantized values. Encoding divides by
+ *   the scale (IEEE binary32) and rounds half to even. */
+pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const void* v,
+                         pkv_dtype in_dtype, const int64_t* slot_mapping, int32_t n_tokens,
+                         void* stream);
+
+/* Workspace bytes pkv_decode_attention needs for these sizes (partition
+ * partials m, l and o/l in fp32). partition_tokens 0 = the automatic choice. */
+size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+/* The partition size (tokens) pkv_decode_attention uses for these sizes when
+ * partition_tokens is 0. */
+int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len);
+
+/* Single-token decode attention over one layer ("vLLM核心概念" §3.1):
+ *   out[s][h][:] = sum_t softmax_t(softmax_scale * q[s][h] . K[s,t]) V[s,t]
+ * over t < context_lens[s], where token t of sequence s lives in block
+ * block_tables[s][t / bs], row t % bs, of KV head h / (num_q_heads /
+ * num_kv_heads).
+ *   q: [num_seqs][num_q_heads][head_dim] of q_dtype (F32, F16, BF16).
+ *   block_tables: [num_seqs][max_blocks_per_seq] int32; entries past a
+ *     sequence's last block are ignored. context_lens: [num_seqs] int32 with
+ *     1 <= len <= max_blocks_per_seq*bs and len <= max_context_len (not
+ *     checked on the device: the caller uploads what pkv_seq_block_table gave).
+ *   out: [num_seqs][num_q_heads][head_dim] fp32.
+ *   partition_tokens: context split (multiple of bs; 0 = automatic); each
+ *     (sequence, KV head, partition) is one workgroup serving all query heads
+ *     of the group; a sequence with more than one partition is finished by a
+ *     log-sum-exp merge launch.
+ *   workspace: at least pkv_decode_workspace_bytes(...) bytes (device).
+ * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4,8}. */
+pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, float softmax_scale,
+                                int32_t partition_tokens, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Synchronous host export of blocks of one layer in canonical order:
+ * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as
+ * uint16 for an F16 cache); scales_out (host, may be NULL; INT8 only)
+ * [n][2][Hkv] fp32. */
+pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
+                           void* codes_out, float* scales_out);
+
+/* The KV-bytes formula 2*L*H*d*s*B*bytes ("无 vLLM 环境下的 Paged-KV" §2). */
+uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,
+                      uint64_t seqs, uint64_t bytes);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,506 @@
+// pool.cpp -- host side of libpkv: the block pool, its allocator and the C ABI.
+//
+// Allocator ("连续批处理与KV缓存" §4.2): the free blocks form one FIFO queue,
+// kept here as a fixed ring of N entries -- allocation takes from the front,
+// freeing appends to the back, O(1) per block and no fragmentation. Each
+// sequence owns its block table (logical -> physical, "vLLM核心概念" §3.2)
+// and a length; each block carries a reference count so forked sequences
+// can share a prefix, and the first write into a shared, partly filled
+// block copies it first (copy-on-write, same section).
+//
+// Device memory (one arena): codes [L][2][N][Hkv][bs][d] followed, for an
+// INT8 cache, by scales [L][2][N][Hkv] fp32.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t elem_bytes(pkv_dtype t) { return t == PKV_I8 ? 1 : 2; }
+
+struct Seq {
+  std::vector<int32_t> blocks;
+  int64_t len = 0;
+};
+
+}  // namespace
+
+struct pkv_pool {
+  pkv_pool_config cfg{};
+  // FIFO free queue as a ring buffer: entries [head, head + count) mod N.
+  std::vector<int32_t> ring;
+  int64_t head = 0, count = 0;
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t cow_total = 0;
+  // device side
+  int device = -1;
+  char* arena = nullptr;
+  bool owns_arena = false;
+  size_t tile_elems = 0;    // bs * d
+  size_t slice_bytes = 0;   // one (layer, K|V) slice of codes: N*Hkv*bs*d*elem
+  size_t codes_bytes = 0;   // all layers
+  float* scales = nullptr;  // [L][2][N][Hkv] (int8)
+
+  int32_t pop_front() {
+    const int32_t b = ring[head];
+    head = (head + 1) % cfg.num_blocks;
+    --count;
+    refcount[b] = 1;
+    return b;
+  }
+  void push_back(int32_t b) {
+    ring[(head + count) % cfg.num_blocks] = b;
+    ++count;
+  }
+  pkv::LayerView layer_view(int32_t layer) const {
+    pkv::LayerView lv{};
+    lv.k_codes = arena + (size_t)(2 * layer) * slice_bytes;
+    lv.v_codes = arena + (size_t)(2 * layer + 1) * slice_bytes;
+    const size_t sc_slice = (size_t)cfg.num_blocks * cfg.num_kv_heads;
+    lv.k_scales = scales ? scales + (size_t)(2 * layer) * sc_slice : nullptr;
+    lv.v_scales = scales ? scales + (size_t)(2 * layer + 1) * sc_slice : nullptr;
+    lv.num_blocks = cfg.num_blocks;
+    lv.num_kv_heads = cfg.num_kv_heads;
+    lv.head_dim = cfg.head_dim;
+    lv.block_size = cfg.block_size;
+    lv.kv_dtype = cfg.kv_dtype;
+    return lv;
+  }
+};
+
+namespace {
+
+pkv_status check_config(const pkv_pool_config* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARG, "config is NULL");
+  if (c->num_layers < 1 || c->num_kv_heads < 1 || c->num_blocks < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_layers, num_kv_heads and num_blocks must be >= 1");
+  if (c->kv_dtype != PKV_F16 && c->kv_dtype != PKV_I8)
+    return fail(PKV_ERR_INVALID_ARG, "kv_dtype must be PKV_F16 or PKV_I8");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", c->head_dim);
+  if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: supported are 16, 32 and 64", c->block_size);
+  return PKV_OK;
+}
+
+size_t required_bytes(const pkv_pool_config* c) {
+  const size_t slice = (size_t)c->num_blocks * c->num_kv_heads * c->block_size * c->head_dim *
+                       elem_bytes(c->kv_dtype);
+  size_t total = round_up(slice * 2 * c->num_layers, 256);
+  if (c->kv_dtype == PKV_I8)
+    total += round_up((size_t)c->num_layers * 2 * c->num_blocks * c->num_kv_heads * sizeof(float), 256);
+  return total;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t nblocks_for(int64_t len, int64_t bs) { return (len + bs - 1) / bs; }
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_pool_required_bytes(const pkv_pool_config* cfg) {
+  if (check_config(cfg) != PKV_OK) return 0;
+  return required_bytes(cfg);
+}
+
+pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pkv_status st = check_config(cfg);
+  if (st != PKV_OK) return st;
+  const int32_t N = cfg->num_blocks;
+  std::vector<int32_t> order(N);
+  if (cfg->initial_free_order) {
+    std::vector<char> seen(N, 0);
+    for (int32_t i = 0; i < N; ++i) {
+      const int32_t b = cfg->initial_free_order[i];
+      if (b < 0 || b >= N || seen[b])
+        return fail(PKV_ERR_INVALID_ARG, "initial_free_order is not a permutation of [0, %d)", N);
+      seen[b] = 1;
+      order[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < N; ++i) order[i] = i;
+  }
+  const size_t need = required_bytes(cfg);
+  if (!cfg->host_only && cfg->device_arena && cfg->arena_bytes < need)
+    return fail(PKV_ERR_INVALID_ARG, "device_arena holds %zu bytes, the pool needs %zu",
+                cfg->arena_bytes, need);
+
+  auto* p = new pkv_pool;
+  p->cfg = *cfg;
+  p->cfg.initial_free_order = nullptr;  // copied below, not retained
+  p->ring = order;
+  p->head = 0;
+  p->count = N;
+  p->refcount.assign(N, 0);
+  p->tile_elems = (size_t)cfg->block_size * cfg->head_dim;
+  p->slice_bytes = (size_t)N * cfg->num_kv_heads * p->tile_elems * elem_bytes(cfg->kv_dtype);
+  p->codes_bytes = p->slice_bytes * 2 * cfg->num_layers;
+  if (!cfg->host_only) {
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
+    if (cfg->device_arena) {
+      p->arena = (char*)cfg->device_arena;
+    } else {
+      e = hipMalloc((void**)&p->arena, need);
+      if (e != hipSuccess) { delete p; return hip_fail(e, "hipMalloc(pool arena)"); }
+      p->owns_arena = true;
+    }
+    if (cfg->kv_dtype == PKV_I8) p->scales = (float*)(p->arena + round_up(p->codes_bytes, 256));
+  }
+  *out = p;
+  return ok();
+}
+
+void pkv_pool_destroy(pkv_pool* pool) {
+  if (!pool) return;
+  if (pool->owns_arena && pool->arena) (void)hipFree(pool->arena);
+  delete pool;
+}
+
+pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens %d < 0", n_tokens);
+  if (pool->seqs.count(seq)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld already exists", (long long)seq);
+  const int64_t bs = pool->cfg.block_size;
+  const int64_t need = nblocks_for(n_tokens, bs);
+  if (need > pool->count)
+    return fail(PKV_ERR_OOM, "sequence %lld needs %lld blocks, %lld free", (long long)seq,
+                (long long)need, (long long)pool->count);
+  Seq s;
+  s.blocks.reserve(need);
+  for (int64_t j = 0; j < need; ++j) s.blocks.push_back(pool->pop_front());
+  s.len = n_tokens;
+  if (slots_out)
+    for (int64_t t = 0; t < n_tokens; ++t) slots_out[t] = (int64_t)s.blocks[t / bs] * bs + t % bs;
+  pool->seqs.emplace(seq, std::move(s));
+  return ok();
+}
+
+pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                                const int32_t* n_new, int64_t* slots_out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !n_new)))
+    return fail(PKV_ERR_INVALID_ARG, "bad sequence list");
+  const int64_t bs = pool->cfg.block_size;
+  // Validate, and count the blocks the whole call will take (new blocks plus
+  // copy-on-write targets), tracking reference counts that earlier sequences
+  // of this call release by copying.
+  std::vector<Seq*> ss(n_seqs);
+  std::unordered_map<int64_t, int> seen;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (n_new[i] < 0) return fail(PKV_ERR_INVALID_ARG, "n_new[%d] = %d < 0", i, n_new[i]);
+    if (!seen.emplace(seqs[i], i).second)
+      return fail(PKV_ERR_INVALID_ARG, "sequence %lld listed twice", (long long)seqs[i]);
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seqs[i]);
+    ss[i] = &it->second;
+  }
+  int64_t need = 0;
+  std::unordered_map<int32_t, int32_t> released;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (n_new[i] == 0) continue;
+    const Seq& s = *ss[i];
+    const int64_t have = (int64_t)s.blocks.size();
+    if (s.len % bs != 0) {  // first new token lands in the partly filled last block
+      const int32_t b = s.blocks[have - 1];
+      if (pool->refcount[b] - released[b] > 1) { ++need; ++released[b]; }
+    }
+    need += nblocks_for(s.len + n_new[i], bs) - have;
+  }
+  if (need > pool->count)
+    return fail(PKV_ERR_NO_FREE_BLOCK, "append needs %lld blocks, %lld free", (long long)need,
+                (long long)pool->count);
+
+  const hipStream_t st = (hipStream_t)stream;
+  int64_t o = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    Seq& s = *ss[i];
+    if (n_new[i] == 0) continue;
+    if (s.len % bs != 0) {
+      const int64_t j = (int64_t)s.blocks.size() - 1;
+      const int32_t old = s.blocks[j];
+      if (pool->refcount[old] > 1) {
+        const int32_t fresh = pool->pop_front();
+        pool->refcount[old] -= 1;
+        s.blocks[j] = fresh;
+        pool->cow_total += 1;
+        if (pool->arena) {
+          // whole (block, head) tiles of every layer and K/V: a 2-D copy with
+          // one row per (layer, K|V) slice; then the scales the same way
+          const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems *
+                                    elem_bytes(pool->cfg.kv_dtype);
+          hipError_t e = hipMemcpy2DAsync(pool->arena + (size_t)fresh * tile_bytes, pool->slice_bytes,
+                                          pool->arena + (size_t)old * tile_bytes, pool->slice_bytes,
+                                          tile_bytes, 2 * (size_t)pool->cfg.num_layers,
+                                          hipMemcpyDeviceToDevice, st);
+          if (e == hipSuccess && pool->scales) {
+            const size_t sc_row = (size_t)pool->cfg.num_kv_heads * sizeof(float);
+            const size_t sc_pitch = (size_t)pool->cfg.num_blocks * sc_row;
+            e = hipMemcpy2DAsync((char*)pool->scales + (size_t)fresh * sc_row, sc_pitch,
+                                 (char*)pool->scales + (size_t)old * sc_row, sc_pitch, sc_row,
+                                 2 * (size_t)pool->cfg.num_layers, hipMemcpyDeviceToDevice, st);
+          }
+          if (e != hipSuccess) return hip_fail(e, "copy-on-write copy");
+        }
+      }
+    }
+    for (int64_t t = s.len; t < s.len + n_new[i]; ++t) {
+      if (t / bs == (int64_t)s.blocks.size()) s.blocks.push_back(pool->pop_front());
+      if (slots_out) slots_out[o] = (int64_t)s.blocks[t / bs] * bs + t % bs;
+      ++o;
+    }
+    s.len += n_new[i];
+  }
+  return ok();
+}
+
+pkv_status pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown parent %lld", (long long)parent);
+  if (pool->seqs.count(child)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld already exists", (long long)child);
+  Seq c = it->second;
+  for (int32_t b : c.blocks) pool->refcount[b] += 1;
+  pool->seqs.emplace(child, std::move(c));
+  return ok();
+}
+
+pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return ok();
+  for (int32_t b : it->second.blocks)
+    if (--pool->refcount[b] == 0) pool->push_back(b);
+  pool->seqs.erase(it);
+  return ok();
+}
+
+pkv_status pkv_seq_block_table(const pkv_pool* pool, const int64_t* seqs, int32_t n,
+                               int32_t max_blocks, int32_t* table_out, int32_t* lens_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !table_out || !lens_out)))
+    return fail(PKV_ERR_INVALID_ARG, "bad arguments");
+  std::vector<const Seq*> ss(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seqs[i]);
+    if ((int64_t)it->second.blocks.size() > max_blocks)
+      return fail(PKV_ERR_INVALID_ARG, "sequence %lld holds %zu blocks > max_blocks %d",
+                  (long long)seqs[i], it->second.blocks.size(), max_blocks);
+    ss[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t* row = table_out + (size_t)i * max_blocks;
+    const auto& b = ss[i]->blocks;
+    std::copy(b.begin(), b.end(), row);
+    std::fill(row + b.size(), row + max_blocks, -1);
+    lens_out[i] = (int32_t)ss[i]->len;
+  }
+  return ok();
+}
+
+pkv_status pkv_seq_length(const pkv_pool* pool, int64_t seq, int64_t* len_out) {
+  if (!pool || !len_out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq);
+  *len_out = it->second.len;
+  return ok();
+}
+
+pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
+  if (!pool || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  int64_t used = 0, shared = 0;
+  for (int32_t r : pool->refcount) { used += r > 0; shared += r > 1; }
+  out->free_blocks = pool->count;
+  out->used_blocks = used;
+  out->shared_blocks = shared;
+  out->cow_copies = pool->cow_total;
+  out->num_seqs = (int64_t)pool->seqs.size();
+  out->total_blocks = pool->cfg.num_blocks;
+  return ok();
+}
+
+pkv_status pkv_pool_free_queue(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!pool || !out || !n_out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (cap < pool->count) return fail(PKV_ERR_INVALID_ARG, "cap %d < %lld queued", cap, (long long)pool->count);
+  for (int64_t i = 0; i < pool->count; ++i) out[i] = pool->ring[(pool->head + i) % pool->cfg.num_blocks];
+  *n_out = (int32_t)pool->count;
+  return ok();
+}
+
+pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const void* v,
+                         pkv_dtype in_dtype, const int64_t* slot_mapping, int32_t n_tokens,
+                         void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  if (layer < 0 || layer >= pool->cfg.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, pool->cfg.num_layers);
+  if (in_dtype != PKV_F32 && in_dtype != PKV_F16 && in_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "input dtype must be F32, F16 or BF16");
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "NULL k, v or slot_mapping");
+  hipError_t e = pkv::launch_append(pool->layer_view(layer), k, v, in_dtype, slot_mapping,
+                                    n_tokens, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len) {
+  // Smallest power-of-two multiple of 16 tokens, between 128 and 512, that
+  // still gives about four workgroups per compute unit (256 CUs).
+  const int64_t pairs = (int64_t)num_seqs * pool->cfg.num_kv_heads;
+  int32_t T = 512;
+  while (T > 128 && pairs * ((max_context_len + T - 1) / T) < 1024) T /= 2;
+  if (T < pool->cfg.block_size) T = pool->cfg.block_size;
+  return T;
+}
+
+int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len) {
+  (void)num_q_heads;
+  if (!pool || num_seqs < 1 || max_context_len < 1) return 0;
+  return auto_partition(pool, num_seqs, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition_tokens) {
+  if (!pool || num_seqs < 1 || num_q_heads < 1 || max_context_len < 1) return 0;
+  const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
+  const int32_t P = (max_context_len + T - 1) / T;
+  return pkv::decode_workspace_bytes(num_seqs, num_q_heads, pool->cfg.head_dim, P);
+}
+
+pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, float softmax_scale,
+                                int32_t partition_tokens, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "q dtype must be F32, F16 or BF16");
+  if (num_q_heads < 1 || num_q_heads % c.num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, c.num_kv_heads);
+  const int32_t group = num_q_heads / c.num_kv_heads;
+  if (!pkv::decode_supported(c.head_dim, group))
+    return fail(PKV_ERR_UNSUPPORTED, "query heads per KV head %d: supported are 1, 2 and 4", group);
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (num_seqs == 0) return ok();
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.block_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [1, max_blocks_per_seq*bs = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * c.block_size);
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % c.block_size != 0))
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a positive multiple of block_size %d",
+                partition_tokens, c.block_size);
+  if (!q || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_INVALID_ARG, "NULL q, block_tables, context_lens or out");
+  const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
+  const int32_t P = (max_context_len + T - 1) / T;
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, c.head_dim, P);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (P > 65535) return fail(PKV_ERR_UNSUPPORTED, "%d partitions exceed the grid limit", P);
+
+  pkv::DecodeLaunch d{};
+  d.lv = pool->layer_view(layer);
+  d.q = q;
+  d.q_dtype = q_dtype;
+  d.num_q_heads = num_q_heads;
+  d.tables = block_tables;
+  d.max_blocks = max_blocks_per_seq;
+  d.lens = context_lens;
+  d.num_seqs = num_seqs;
+  d.partition_tokens = T;
+  d.max_partitions = P;
+  d.softmax_scale = softmax_scale;
+  d.out = out;
+  d.ws = (float*)workspace;
+  hipError_t e = pkv::launch_decode(d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
+                           void* codes_out, float* scales_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
+  if (n < 0 || (n > 0 && (!blocks || !codes_out))) return fail(PKV_ERR_INVALID_ARG, "bad arguments");
+  for (int32_t i = 0; i < n; ++i)
+    if (blocks[i] < 0 || blocks[i] >= c.num_blocks)
+      return fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", blocks[i], c.num_blocks);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronize before read-back");
+  const size_t tile_bytes = (size_t)c.num_kv_heads * pool->tile_elems * elem_bytes(c.kv_dtype);
+  const pkv::LayerView lv = pool->layer_view(layer);
+  for (int32_t i = 0; i < n; ++i) {
+    for (int kv = 0; kv < 2; ++kv) {
+      const char* src = (const char*)(kv ? lv.v_codes : lv.k_codes) + (size_t)blocks[i] * tile_bytes;
+      char* dst = (char*)codes_out + ((size_t)i * 2 + kv) * tile_bytes;
+      e = hipMemcpy(dst, src, tile_bytes, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "read-back of codes");
+      if (scales_out && pool->scales) {
+        const float* ssrc = (kv ? lv.v_scales : lv.k_scales) + (size_t)blocks[i] * c.num_kv_heads;
+        e = hipMemcpy(scales_out + ((size_t)i * 2 + kv) * c.num_kv_heads, ssrc,
+                      c.num_kv_heads * sizeof(float), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "read-back of scales");
+      }
+    }
+  }
+  return ok();
+}
+
+uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,
+                      uint64_t seqs, uint64_t bytes) {
+  return 2ull * layers * heads * head_dim * tokens * seqs * bytes;
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

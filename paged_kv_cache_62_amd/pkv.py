@@ -1,0 +1,331 @@
+"""Thin ctypes binding of libpkv (include/pkv.h).
+
+Argument marshalling only: every step of the decode path runs in libpkv's
+host code and HIP kernels. Module-level functions carry the C names; `Pool`
+bundles them for convenience. Device buffers are torch tensors on the pool's
+device (torch is used for device memory and streams only). There is no
+fallback: if libpkv.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_OOM = -2
+PKV_ERR_NO_FREE_BLOCK = -3
+PKV_ERR_UNKNOWN_SEQ = -4
+PKV_ERR_SEQ_EXISTS = -5
+PKV_ERR_DEVICE = -6
+PKV_ERR_UNSUPPORTED = -7
+STATUS_NAMES = {
+    0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_OOM", -3: "PKV_ERR_NO_FREE_BLOCK",
+    -4: "PKV_ERR_UNKNOWN_SEQ", -5: "PKV_ERR_SEQ_EXISTS", -6: "PKV_ERR_DEVICE",
+    -7: "PKV_ERR_UNSUPPORTED",
+}
+
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
+
+# Every symbol include/pkv.h declares, with its ctypes signature.
+_i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p
+
+
+class pkv_pool_config(C.Structure):
+    _fields_ = [
+        ("num_layers", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+        ("block_size", _i32), ("num_blocks", _i32), ("kv_dtype", C.c_int),
+        ("initial_free_order", _vp), ("device_arena", _vp), ("arena_bytes", _sz),
+        ("host_only", _i32),
+    ]
+
+
+class pkv_stats(C.Structure):
+    _fields_ = [("free_blocks", _i64), ("used_blocks", _i64), ("shared_blocks", _i64),
+                ("cow_copies", _i64), ("num_seqs", _i64), ("total_blocks", _i64)]
+
+
+SIGNATURES = {
+    "pkv_pool_required_bytes": (_sz, [_vp]),
+    "pkv_pool_create": (C.c_int, [_vp, _vp]),
+    "pkv_pool_destroy": (None, [_vp]),
+    "pkv_seq_allocate": (C.c_int, [_vp, _i64, _i32, _vp]),
+    "pkv_seq_append_slots": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _vp]),
+    "pkv_seq_fork": (C.c_int, [_vp, _i64, _i64]),
+    "pkv_seq_free": (C.c_int, [_vp, _i64]),
+    "pkv_seq_block_table": (C.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_seq_length": (C.c_int, [_vp, _i64, _vp]),
+    "pkv_pool_stats": (C.c_int, [_vp, _vp]),
+    "pkv_pool_free_queue": (C.c_int, [_vp, _vp, _i32, _vp]),
+    "pkv_append_kv": (C.c_int, [_vp, _i32, _vp, _vp, C.c_int, _vp, _i32, _vp]),
+    "pkv_decode_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
+    "pkv_decode_auto_partition": (_i32, [_vp, _i32, _i32, _i32]),
+    "pkv_decode_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
+                                       _f32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
+    "pkv_kv_bytes": (_u64, [_u64] * 6),
+    "pkv_last_error": (C.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libpkv.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run paged_kv_cache_62_amd.build.build() first")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(st: int) -> int:
+    if st != PKV_OK:
+        raise PkvError(st, lib().pkv_last_error().decode(errors="replace"))
+    return st
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+# ------------------------------------------------------- the C names ----
+def pkv_pool_required_bytes(cfg: pkv_pool_config) -> int:
+    return int(lib().pkv_pool_required_bytes(C.byref(cfg)))
+
+
+def pkv_pool_create(cfg: pkv_pool_config) -> C.c_void_p:
+    h = _vp()
+    _check(lib().pkv_pool_create(C.byref(cfg), C.byref(h)))
+    return h
+
+
+def pkv_pool_destroy(h) -> None:
+    lib().pkv_pool_destroy(h)
+
+
+def pkv_seq_allocate(h, seq: int, n_tokens: int, want_slots: bool = True) -> np.ndarray:
+    slots = np.zeros(max(n_tokens, 1), dtype=np.int64)
+    _check(lib().pkv_seq_allocate(h, seq, n_tokens, _np_ptr(slots) if want_slots else None))
+    return slots[:n_tokens]
+
+
+def pkv_seq_append_slots(h, seqs, n_new, stream=None) -> np.ndarray:
+    seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+    n_new = np.ascontiguousarray(n_new, dtype=np.int32)
+    total = int(n_new.sum()) if n_new.size else 0
+    slots = np.zeros(max(total, 1), dtype=np.int64)
+    _check(lib().pkv_seq_append_slots(h, _np_ptr(seqs), len(seqs), _np_ptr(n_new),
+                                      _np_ptr(slots), stream))
+    return slots[:total]
+
+
+def pkv_seq_fork(h, parent: int, child: int) -> None:
+    _check(lib().pkv_seq_fork(h, parent, child))
+
+
+def pkv_seq_free(h, seq: int) -> None:
+    _check(lib().pkv_seq_free(h, seq))
+
+
+def pkv_seq_block_table(h, seqs, max_blocks: int):
+    seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+    table = np.zeros((len(seqs), max_blocks), dtype=np.int32)
+    lens = np.zeros(len(seqs), dtype=np.int32)
+    _check(lib().pkv_seq_block_table(h, _np_ptr(seqs), len(seqs), max_blocks, _np_ptr(table),
+                                     _np_ptr(lens)))
+    return table, lens
+
+
+def pkv_seq_length(h, seq: int) -> int:
+    out = C.c_int64()
+    _check(lib().pkv_seq_length(h, seq, C.byref(out)))
+    return int(out.value)
+
+
+def pkv_pool_stats(h) -> dict:
+    s = pkv_stats()
+    _check(lib().pkv_pool_stats(h, C.byref(s)))
+    return {k: int(getattr(s, k)) for k, _ in pkv_stats._fields_}
+
+
+def pkv_pool_free_queue(h, cap: int) -> np.ndarray:
+    out = np.zeros(cap, dtype=np.int32)
+    n = C.c_int32()
+    _check(lib().pkv_pool_free_queue(h, _np_ptr(out), cap, C.byref(n)))
+    return out[: n.value]
+
+
+def pkv_append_kv(h, layer: int, k, v, slot_mapping, stream=None) -> None:
+    """k, v: device tensors [n][Hkv][d] (fp32/fp16/bf16); slot_mapping: int64 device tensor."""
+    assert k.is_contiguous() and v.is_contiguous() and slot_mapping.is_contiguous()
+    assert k.dtype == v.dtype and k.shape == v.shape and slot_mapping.dtype.itemsize == 8
+    n = int(slot_mapping.numel())
+    assert k.shape[0] == n
+    _check(lib().pkv_append_kv(h, layer, _vp(k.data_ptr()), _vp(v.data_ptr()), _torch_dtype_code(k),
+                               _vp(slot_mapping.data_ptr()), n, _stream_ptr(stream)))
+
+
+def pkv_decode_workspace_bytes(h, num_seqs, num_q_heads, max_context_len, partition_tokens=0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(h, num_seqs, num_q_heads, max_context_len,
+                                                partition_tokens))
+
+
+def pkv_decode_auto_partition(h, num_seqs, num_q_heads, max_context_len) -> int:
+    return int(lib().pkv_decode_auto_partition(h, num_seqs, num_q_heads, max_context_len))
+
+
+def pkv_decode_attention(h, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
+                         out, workspace=None, partition_tokens=0, stream=None) -> None:
+    """q: [B][Hq][d] device tensor; block_tables [B][max_blocks] int32; context_lens [B] int32;
+    out: [B][Hq][d] float32; workspace: uint8 device tensor or None."""
+    assert q.is_contiguous() and block_tables.is_contiguous() and context_lens.is_contiguous()
+    assert out.is_contiguous() and out.dtype.itemsize == 4
+    B, hq, _ = q.shape
+    ws_ptr = _vp(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib().pkv_decode_attention(
+        h, layer, _vp(q.data_ptr()), _torch_dtype_code(q), hq, _vp(block_tables.data_ptr()),
+        int(block_tables.shape[1]), _vp(context_lens.data_ptr()), B, int(max_context_len),
+        float(softmax_scale), int(partition_tokens), _vp(out.data_ptr()), ws_ptr, ws_bytes,
+        _stream_ptr(stream)))
+
+
+def pkv_read_blocks(h, layer: int, blocks, num_kv_heads: int, block_size: int, head_dim: int,
+                    kv_dtype: int):
+    """Host copy of blocks in canonical order: codes [n][2][Hkv][bs][d], scales [n][2][Hkv]."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.int32)
+    dt = np.int8 if kv_dtype == PKV_I8 else np.uint16
+    codes = np.zeros((len(blocks), 2, num_kv_heads, block_size, head_dim), dtype=dt)
+    scales = np.zeros((len(blocks), 2, num_kv_heads), dtype=np.float32)
+    _check(lib().pkv_read_blocks(h, layer, _np_ptr(blocks), len(blocks), _np_ptr(codes),
+                                 _np_ptr(scales)))
+    return codes, scales
+
+
+def pkv_kv_bytes(L, H, d, s, B, nbytes) -> int:
+    return int(lib().pkv_kv_bytes(L, H, d, s, B, nbytes))
+
+
+def pkv_last_error() -> str:
+    return lib().pkv_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------ Pool ----
+class Pool:
+    """A block pool: host allocator plus (unless host_only) the device cache,
+    whose arena is a torch uint8 tensor owned by this object."""
+
+    def __init__(self, num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
+                 initial_free_order=None, host_only=False, device="cuda"):
+        self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
+        self.block_size, self.num_blocks, self.kv_dtype = block_size, num_blocks, kv_dtype
+        self._order = (None if initial_free_order is None
+                       else np.ascontiguousarray(initial_free_order, dtype=np.int32))
+        cfg = pkv_pool_config(num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
+                              None if self._order is None else _np_ptr(self._order), None, 0,
+                              1 if host_only else 0)
+        self.arena = None
+        if not host_only:
+            import torch
+            nbytes = pkv_pool_required_bytes(cfg)
+            if nbytes == 0:
+                raise PkvError(PKV_ERR_INVALID_ARG, pkv_last_error())
+            self.arena = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            cfg.device_arena = _vp(self.arena.data_ptr())
+            cfg.arena_bytes = nbytes
+        self.h = pkv_pool_create(cfg)
+
+    def close(self):
+        if getattr(self, "h", None):
+            pkv_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
+
+    # allocator
+    def allocate(self, seq, n_tokens):
+        return pkv_seq_allocate(self.h, seq, n_tokens)
+
+    def append_slots(self, seqs, n_new, stream=None):
+        sp = None
+        if self.arena is not None:
+            sp = _stream_ptr(stream)
+        return pkv_seq_append_slots(self.h, seqs, n_new, sp)
+
+    def fork(self, parent, child):
+        pkv_seq_fork(self.h, parent, child)
+
+    def free(self, seq):
+        pkv_seq_free(self.h, seq)
+
+    def block_table(self, seqs, max_blocks):
+        return pkv_seq_block_table(self.h, seqs, max_blocks)
+
+    def length(self, seq):
+        return pkv_seq_length(self.h, seq)
+
+    def stats(self):
+        return pkv_pool_stats(self.h)
+
+    def free_queue(self):
+        return pkv_pool_free_queue(self.h, self.num_blocks)
+
+    # device
+    def append_kv(self, layer, k, v, slot_mapping, stream=None):
+        pkv_append_kv(self.h, layer, k, v, slot_mapping, stream)
+
+    def workspace_bytes(self, num_seqs, num_q_heads, max_context_len, partition_tokens=0):
+        return pkv_decode_workspace_bytes(self.h, num_seqs, num_q_heads, max_context_len,
+                                          partition_tokens)
+
+    def auto_partition(self, num_seqs, num_q_heads, max_context_len):
+        return pkv_decode_auto_partition(self.h, num_seqs, num_q_heads, max_context_len)
+
+    def decode(self, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
+               out=None, workspace=None, partition_tokens=0, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nb = self.workspace_bytes(q.shape[0], q.shape[1], max_context_len, partition_tokens)
+            workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+        pkv_decode_attention(self.h, layer, q, block_tables, context_lens, max_context_len,
+                             softmax_scale, out, workspace, partition_tokens, stream)
+        return out
+
+    def read_blocks(self, layer, blocks):
+        return pkv_read_blocks(self.h, layer, blocks, self.num_kv_heads, self.block_size,
+                               self.head_dim, self.kv_dtype)
