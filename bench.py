@@ -1,0 +1,332 @@
+"""Decode-attention benchmark on one MI355X.
+
+One step = one decode step of every sequence through all layers: the host
+allocator reserves one new slot per sequence and rebuilds the block tables,
+they are uploaded, then per layer the new token's K/V are appended (quantized
+for an INT8 cache) and the split-context decode runs. Inputs are seeded
+synthetic tensors already resident in HBM; the cache is filled before timing.
+
+Prints one JSON line: tokens/s (one new token per sequence per step), the
+decode kernel's KV-read bandwidth against the 8 TB/s HBM peak, and the FP64
+CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--config qwen|llama29|llama128|mix16|mix32|long_i8|long_f16]
+                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="merge partitions in a second launch instead of the last workgroup")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
+    return ap.parse_args()
+
+
+CONFIGS = {
+    # Qwen3-TTS talker: 28 layers, 8 KV / 16 query heads, d 128, bs 16, B=4 x 8000, INT8.
+    "qwen": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, nblocks=2048, B=4, ctx=8000, kv="i8",
+                 q="bf16", kvin="bf16", sigma="per_head", seed=62002, outlier=0.0),
+    # Llama-2-7B MHA, FP16 KV: 29 x 4096 (the A100 sizing case) and 128 x 1024.
+    "llama29": dict(layers=32, hq=32, hkv=32, dim=128, bs=16, nblocks=8192, B=29, ctx=4096, kv="f16",
+                    q="f16", kvin="f16", sigma="unit", seed=62003, outlier=0.0),
+    "llama128": dict(layers=32, hq=32, hkv=32, dim=128, bs=16, nblocks=8192, B=128, ctx=1024, kv="f16",
+                     q="f16", kvin="f16", sigma="unit", seed=62003, outlier=0.0),
+    # continuous-batching mix: shared 200-token prefix + lognormal suffixes, INT8, GQA 32/8.
+    "mix16": dict(layers=32, hq=32, hkv=8, dim=128, bs=16, nblocks=15000, B=128, ctx=None, kv="i8",
+                  q="bf16", kvin="bf16", sigma="unit", seed=62004, outlier=0.0),
+    "mix32": dict(layers=32, hq=32, hkv=8, dim=128, bs=32, nblocks=15000, B=128, ctx=None, kv="i8",
+                  q="bf16", kvin="bf16", sigma="unit", seed=62004, outlier=0.0),
+    # long context: 8 x 32768, bs 64, one layer timed over two rotating copies.
+    "long_i8": dict(layers=2, hq=32, hkv=8, dim=128, bs=64, nblocks=None, B=8, ctx=32768, kv="i8",
+                    q="bf16", kvin="bf16", sigma="unit", seed=62005, outlier=0.01, partition=512,
+                    rotate=True),
+    "long_f16": dict(layers=2, hq=32, hkv=8, dim=128, bs=64, nblocks=None, B=8, ctx=32768, kv="f16",
+                     q="bf16", kvin="bf16", sigma="unit", seed=62005, outlier=0.01, partition=512,
+                     rotate=True),
+}
+
+WORKLOAD_NAMES = {
+    "qwen": "qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, int8 kv",
+    "llama29": "llama-2-7b decode: 32 layers, B=29 x 4096 ctx, 32q/32kv, d128, bs16, fp16 kv",
+    "llama128": "llama-2-7b decode: 32 layers, B=128 x 1024 ctx, 32q/32kv, d128, bs16, fp16 kv",
+    "mix16": "continuous-batching mix: 32 layers, 128 seqs, shared 200-token prefix + lognormal suffix, 32q/8kv, bs16, int8 kv",
+    "mix32": "continuous-batching mix: 32 layers, 128 seqs, shared 200-token prefix + lognormal suffix, 32q/8kv, bs32, int8 kv",
+    "long_i8": "long-context: 1 layer (2 rotating copies), B=8 x 32768, 32q/8kv, d128, bs64, T=512, int8 kv",
+    "long_f16": "long-context: 1 layer (2 rotating copies), B=8 x 32768, 32q/8kv, d128, bs64, T=512, fp16 kv",
+}
+
+
+def mix_suffix_lengths(seed, n):
+    """round(X), X ~ lognormal(ln 300 - 0.32, 0.8) (mean 300), clamped to [1, 1024]."""
+    from paged_kv_cache_62_amd import synth
+    z = synth.normal(synth.stream_seed(seed, 4242), n)
+    x = np.exp(math.log(300.0) - 0.32 + 0.8 * z)
+    return np.clip(np.rint(x), 1, 1024).astype(np.int64)
+
+
+class Workload:
+    def __init__(self, name, steps_total, partition=0, flags=0):
+        import torch
+        from paged_kv_cache_62_amd import pkv, synth
+        self.torch, self.pkv = torch, pkv
+        c = dict(CONFIGS[name])
+        self.c, self.name = c, name
+        self.dev = torch.device("cuda")
+        self.B, self.L, self.hq, self.hkv, self.dim, self.bs = c["B"], c["layers"], c["hq"], c["hkv"], c["dim"], c["bs"]
+        self.kv_code = pkv.PKV_I8 if c["kv"] == "i8" else pkv.PKV_F16
+        self.rotate = c.get("rotate", False)
+        self.partition = partition or c.get("partition", 0)
+        self.flags = flags
+        self.scale = 1.0 / math.sqrt(self.dim)
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+        seed = c["seed"]
+        # sequence lengths before the timed steps
+        if c["ctx"] is None:  # mix: prefix 200 shared by all, then per-sequence suffixes
+            self.suffix = mix_suffix_lengths(seed, self.B)
+            lens0 = 200 + self.suffix
+        else:
+            lens0 = np.full(self.B, c["ctx"] - 1, dtype=np.int64)  # step 0 decodes at ctx
+        appends = steps_total if not self.rotate else (steps_total + 1) // 2 + 1
+        need = int(sum((int(n) + appends + self.bs - 1) // self.bs for n in lens0)) + 8
+        nblocks = c["nblocks"] if c["nblocks"] is not None else need
+        if need > nblocks:
+            nblocks = need  # headroom for the blocks the timed steps append
+        self.nblocks = nblocks
+        order = synth.permutation(synth.stream_seed(seed, 1), nblocks)
+        self.pool = pkv.Pool(self.L, self.hkv, self.dim, self.bs, nblocks, self.kv_code,
+                             initial_free_order=order)
+        self.seqs = np.arange(self.B, dtype=np.int64)
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(seed)
+        u = synth.uniform(synth.stream_seed(seed, 7777), self.L * 2 * self.hkv)
+        sig = (0.5 + 3.5 * u).reshape(self.L, 2, self.hkv) if c["sigma"] == "per_head" else np.ones((self.L, 2, self.hkv))
+        self.sig = torch.tensor(sig, dtype=torch.float32, device=self.dev)
+
+        def kv_fill(layer, n):
+            out = []
+            for kv in range(2):
+                x = torch.randn(n, self.hkv, self.dim, generator=gen, device=self.dev)
+                x *= self.sig[layer, kv][None, :, None]
+                if c["outlier"] > 0:
+                    m = torch.rand(x.shape, generator=gen, device=self.dev) < c["outlier"]
+                    sgn = torch.where(torch.rand(x.shape, generator=gen, device=self.dev) < 0.5, -20.0, 20.0)
+                    x = torch.where(m, sgn, x)
+                out.append(x.to(tdt[c["kvin"]]).contiguous())
+            return out
+
+        # fill the cache
+        if c["ctx"] is None:
+            slots = self.pool.allocate(0, 200)
+            self._append_all(kv_fill, slots)
+            for s in range(1, self.B):
+                self.pool.fork(0, s)
+            slots = self.pool.append_slots(self.seqs, self.suffix.astype(np.int32))
+            self._append_all(kv_fill, slots)
+        else:
+            for s in range(self.B):
+                slots = self.pool.allocate(s, int(lens0[s]))
+                self._append_all(kv_fill, slots)
+        torch.cuda.synchronize()
+        # per-step inputs: one query and one new K/V row per sequence and layer
+        self.q = [torch.randn(self.B, self.hq, self.dim, generator=gen, device=self.dev).to(tdt[c["q"]])
+                  for _ in range(self.L)]
+        self.knew, self.vnew = [], []
+        for layer in range(self.L):
+            k, v = kv_fill(layer, self.B)
+            self.knew.append(k)
+            self.vnew.append(v)
+        self.max_blocks = max((int(n) + appends + self.bs - 1) // self.bs for n in lens0) + 1
+        self.out = torch.empty(self.B, self.hq, self.dim, dtype=torch.float32, device=self.dev)
+        max_ctx = int(lens0.max()) + appends
+        ws = self.pool.workspace_bytes(self.B, self.hq, max_ctx, self.partition)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.dev)
+        # pinned staging ring for the per-step uploads
+        self.ring = []
+        for _ in range(4):
+            self.ring.append(dict(
+                slots=torch.empty(self.B, dtype=torch.int64, pin_memory=True),
+                table=torch.empty(self.B, self.max_blocks, dtype=torch.int32, pin_memory=True),
+                lens=torch.empty(self.B, dtype=torch.int32, pin_memory=True),
+                ev=torch.cuda.Event()))
+        self.d_slots = torch.empty(self.B, dtype=torch.int64, device=self.dev)
+        self.d_table = torch.empty(self.B, self.max_blocks, dtype=torch.int32, device=self.dev)
+        self.d_lens = torch.empty(self.B, dtype=torch.int32, device=self.dev)
+        self.step_i = 0
+        self.decode_events = []  # (start, end, kv_read_bytes) per decode launch
+        self.record = False
+
+    def _append_all(self, kv_fill, slots):
+        t = self.torch
+        d_slots = t.from_numpy(np.ascontiguousarray(slots)).to(self.dev)
+        chunk = 65536
+        for layer in range(self.L):
+            for i in range(0, len(slots), chunk):
+                k, v = kv_fill(layer, min(chunk, len(slots) - i))
+                self.pool.append_kv(layer, k, v, d_slots[i:i + chunk])
+
+    def kv_read_bytes(self, lens):
+        """Algorithmic bytes one decode launch reads: K and V payload of the
+        valid tokens plus one fp32 scale per (block, head, K|V) for INT8."""
+        elem = 1 if self.kv_code == self.pkv.PKV_I8 else 2
+        b = int(lens.sum()) * self.hkv * self.dim * 2 * elem
+        if elem == 1:
+            b += int(sum((int(n) + self.bs - 1) // self.bs for n in lens)) * self.hkv * 2 * 4
+        return b
+
+    def step(self):
+        t = self.torch
+        slot = self.ring[self.step_i % len(self.ring)]
+        slot["ev"].synchronize()  # the upload that last used this staging slot is done
+        slots = self.pool.append_slots(self.seqs, np.ones(self.B, dtype=np.int32))
+        table, lens = self.pool.block_table(self.seqs, self.max_blocks)
+        slot["slots"].numpy()[:] = slots
+        slot["table"].numpy()[:] = table
+        slot["lens"].numpy()[:] = lens
+        self.d_slots.copy_(slot["slots"], non_blocking=True)
+        self.d_table.copy_(slot["table"], non_blocking=True)
+        self.d_lens.copy_(slot["lens"], non_blocking=True)
+        slot["ev"].record()
+        max_ctx = int(lens.max())
+        layers = range(self.L) if not self.rotate else [self.step_i % self.L]
+        nbytes = self.kv_read_bytes(lens)
+        for layer in layers:
+            self.pool.append_kv(layer, self.knew[layer], self.vnew[layer], self.d_slots)
+            if self.record:
+                e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                e0.record()
+            self.pool.decode(layer, self.q[layer], self.d_table, self.d_lens, max_ctx, self.scale,
+                             out=self.out, workspace=self.ws, partition_tokens=self.partition,
+                             flags=self.flags)
+            if self.record:
+                e1.record()
+                self.decode_events.append((e0, e1, nbytes))
+        self.step_i += 1
+        return lens
+
+
+def cpu_baseline(w: Workload, target_s: float):
+    """The FP64 oracle on a bounded sample: layers in order until ~target_s of
+    CPU time, over the GPU's cache read back after the timed steps."""
+    from oracle import oracle as orc
+    from paged_kv_cache_62_amd import synth
+    table, lens = w.pool.block_table(w.seqs, w.max_blocks)
+    blocks = sorted({int(b) for i in range(w.B) for b in table[i, : (int(lens[i]) + w.bs - 1) // w.bs]})
+    threads = max(1, min(16, os.cpu_count() or 1))
+    kvd = orc.I8 if w.kv_code == w.pkv.PKV_I8 else orc.F16
+    dt = np.int8 if kvd == orc.I8 else np.uint16
+    done, elapsed = 0, 0.0
+    layers = range(w.L) if not w.rotate else [0]
+    for layer in layers:
+        codes, scales = w.pool.read_blocks(layer, blocks)
+        kc = np.zeros((w.nblocks, w.hkv, w.bs, w.dim), dtype=dt)
+        vc = np.zeros_like(kc)
+        ks = np.ones((w.nblocks, w.hkv), np.float32)
+        vs = np.ones_like(ks)
+        kc[blocks], vc[blocks] = codes[:, 0], codes[:, 1]
+        if kvd == orc.I8:
+            ks[blocks], vs[blocks] = scales[:, 0], scales[:, 1]
+        del codes
+        q = synth.as_f32(w.q[layer].cpu())
+        t0 = time.perf_counter()
+        orc.decode_attention(kvd, kc, vc, ks, vs, q, table, lens, w.scale, threads=threads)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= target_s:
+            break
+    t_layer = elapsed / done
+    layers_per_step = 1 if w.rotate else w.L
+    value = w.B / (t_layer * layers_per_step)
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"FP64 oracle decode of {done} of {layers_per_step} layer(s) per step "
+                       f"({t_layer * 1e3:.1f} ms per layer, {threads} threads) over the GPU cache "
+                       f"read back after the timed steps; tokens/s = B / (layers x time per layer), "
+                       f"extrapolated from the sampled layers")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if args.config not in CONFIGS:
+        sys.exit(f"unknown --config {args.config}; choose from {sorted(CONFIGS)}")
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    pkv.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"# building workload {args.config}", file=sys.stderr, flush=True)
+    w = Workload(args.config, args.warmup + args.steps, args.partition,
+                 flags=pkv.PKV_DECODE_SEPARATE_MERGE if args.separate_merge else 0)
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    print(f"# warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    w.record = True
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    tokens = 0
+    for _ in range(args.steps):
+        w.step()
+        tokens += w.B
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    durs = np.array([e0.elapsed_time(e1) for e0, e1, _ in w.decode_events])  # ms
+    nbytes = np.array([b for _, _, b in w.decode_events], dtype=np.float64)
+    avg_dur_s = durs.mean() / 1e3
+    achieved = nbytes.mean() / avg_dur_s / 1e9
+    kv_gbs_step = nbytes.sum() / (total_ms / 1e3) / 1e9
+    res = {
+        "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": tokens / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 kv / fp32 accumulate" if w.kv_code == pkv.PKV_I8 else "fp16 kv / fp32 accumulate",
+        "data": "synthetic (seeded), cache filled through pkv_append_kv before timing",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": w.B,
+                   "layers_per_step": 1 if w.rotate else w.L,
+                   "partition_tokens": w.pool.auto_partition(w.B, w.hq, int(w.d_lens.max().item()))
+                   if not w.partition else w.partition,
+                   "kv_read_GBps_whole_step": kv_gbs_step},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_split_kernel (+ merge when partitioned)",
+                     "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": nbytes.mean()},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

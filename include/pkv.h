@@ -26,7 +26,7 @@
  *    void*; NULL = the null stream). Their pointer arguments are device
  *    pointers on the pool's device unless marked "host".
  *  - A pool is not thread-safe: one host thread (or a lock) per pool.
- *  - Layout of the cache is private; pkv_read_block exports one block in a
+ *  - Layout of the cache is private; pkv_read_blocks exports blocks in a
  *    canonical order for checks.
  */
 #ifndef PKV_H_
@@ -162,8 +162,10 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const voi
                          pkv_dtype in_dtype, const int64_t* slot_mapping, int32_t n_tokens,
                          void* stream);
 
-/* Workspace bytes pkv_decode_attention needs for these sizes (partition
- * partials m, l and o/l in fp32). partition_tokens 0 = the automatic choice. */
+/* Workspace bytes pkv_decode_attention needs for these sizes: one int32
+ * arrival counter per (sequence, KV head), then the partition partials m, l
+ * and o/l in fp32. 0 when every sequence fits in one partition.
+ * partition_tokens 0 = the automatic choice. */
 size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_tokens);
 
@@ -171,6 +173,10 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
  * partition_tokens is 0. */
 int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len);
+
+/* flags for pkv_decode_attention */
+#define PKV_DECODE_SEPARATE_MERGE 1 /* merge partitions in a second launch instead of
+                                       in the last workgroup of each (seq, KV head) */
 
 /* Single-token decode attention over one layer ("vLLM核心概念" §3.1):
  *   out[s][h][:] = sum_t softmax_t(softmax_scale * q[s][h] . K[s,t]) V[s,t]
@@ -185,16 +191,20 @@ int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_
  *   out: [num_seqs][num_q_heads][head_dim] fp32.
  *   partition_tokens: context split (multiple of bs; 0 = automatic); each
  *     (sequence, KV head, partition) is one workgroup serving all query heads
- *     of the group; a sequence with more than one partition is finished by a
- *     log-sum-exp merge launch.
- *   workspace: at least pkv_decode_workspace_bytes(...) bytes (device).
- * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4,8}. */
+ *     of the group; the partitions of a sequence are combined by a
+ *     log-sum-exp merge, done by the last workgroup of each (sequence, KV
+ *     head) to finish, or by a second launch with PKV_DECODE_SEPARATE_MERGE.
+ *   workspace: at least pkv_decode_workspace_bytes(...) bytes (device). It
+ *     must be zero-filled before its first use; every call leaves its
+ *     counters at zero again, so one workspace serves any number of calls on
+ *     one stream (calls that overlap in time need separate workspaces).
+ * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4}. */
 pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
                                 int32_t num_q_heads, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
                                 int32_t num_seqs, int32_t max_context_len, float softmax_scale,
-                                int32_t partition_tokens, float* out, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                int32_t partition_tokens, int32_t flags, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as

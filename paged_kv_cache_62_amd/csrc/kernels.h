@@ -2,7 +2,7 @@
 // gfx950 kernels (kernels.hip). Internal to libpkv.
 #pragma once
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -11,7 +11,25 @@ namespace pkv {
 // Element type codes, same values as pkv_dtype in pkv.h.
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
 
-// One layer's view of the cache. Codes are [N][Hkv][bs][d] per K and V;
+// Tile layouts. A (block, KV head) tile holds bs tokens x d elements.
+//  K: row-major, element (t, dim) at t*d + dim, so a token row is contiguous
+//     and a 16-token slice is the A operand of the QK matrix-core product
+//     read straight from memory.
+//  V: split into 16-token sub-tiles; inside one, token t = 4*tg + ti and
+//     dim = 16*dt + dm sit at ((tg*16 + dm) * (d/16) + dt) * 4 + ti, so lane
+//     tg*16 + dm of a wavefront reads d/4 contiguous elements holding, for
+//     every 16-dim tile dt, the 4 tokens that make up its A operand of the
+//     PV product (16 dims x 16 tokens).
+__host__ __device__ inline int64_t k_tile_offset(int t, int dim, int d) {
+  return (int64_t)t * d + dim;
+}
+__host__ __device__ inline int64_t v_tile_offset(int t, int dim, int d) {
+  const int sub = t >> 4, tt = t & 15;
+  const int tg = tt >> 2, ti = tt & 3, dm = dim & 15, dt = dim >> 4;
+  return (int64_t)sub * 16 * d + ((int64_t)(tg * 16 + dm) * (d / 16) + dt) * 4 + ti;
+}
+
+// One layer's view of the cache. Codes are [N][Hkv][tile] per K and V;
 // scales [N][Hkv] per K and V (int8 only).
 struct LayerView {
   void* k_codes;
@@ -37,7 +55,9 @@ struct DecodeLaunch {
   int32_t max_partitions;    // ceil(max_context_len / partition_tokens)
   float softmax_scale;
   float* out;
-  float* ws;                 // partials; may be null when max_partitions == 1
+  int32_t* counters;         // [num_seqs][Hkv] arrival counters (zero between calls)
+  float* ws;                 // partials m, l [num_seqs][Hq][P], o [num_seqs][Hq][P][d]
+  int32_t fused_merge;       // 1: the last workgroup of a (seq, KV head) merges
 };
 
 // True if the kernels cover this head_dim / group size.
@@ -45,8 +65,9 @@ bool decode_supported(int head_dim, int group);
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 
-// Bytes of workspace for the partials (m, l, o/l).
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                              int32_t max_partitions);
+// Workspace: counters first (256-byte aligned), then the partials.
+size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_partitions);
 
 }  // namespace pkv

@@ -8,12 +8,26 @@
 //              block table[t / bs], row t % bs). One workgroup per (sequence,
 //              KV head, context partition) serves all G query heads of the
 //              group, so each K/V byte is read from HBM once per step.
-//  H3 merge:   log-sum-exp merge of the partition partials.
+//  H3 merge:   log-sum-exp merge of the partitions, done by the last
+//              workgroup of each (sequence, KV head) to arrive, or by a
+//              separate launch.
 //
-// Cache layout per layer and per K/V: codes [N][Hkv][bs][d] -- each
-// (block, head) tile is bs*d contiguous elements, so a 16-row slice of a tile
-// is one contiguous 2 KB (int8, d=128) or 4 KB (fp16) run that a wavefront
-// reads with 16-byte loads, 8 or 4 rows per load instruction.
+// Both contractions of H2 run on the matrix cores, 16 tokens at a time:
+//   S^T[token][col] = K[token][:] . Q^T[:][col]      (A = K rows from HBM)
+//   O^T[dim][col]  += V^T[dim][token] . P^T[token][col]
+// The output layout of the first product is exactly the B-operand layout of
+// the second, so the probabilities never leave their lanes. The 16 columns
+// carry the G <= 4 query heads of the group, each split into exact parts:
+//  * int8 K: q is rounded to a 22-bit integer (per-head power-of-two scale)
+//    and split into three signed 8-bit digits, one column each, so the int8
+//    product on the raw codes is exact and the three columns recombine to
+//    the fp32 score;
+//  * fp16 K: q is scaled by a power of two into fp16 (a second "lo" column
+//    carries the rest of an fp32 q);
+//  * P goes in as fp16 hi and lo parts in two columns, so the product keeps
+//    about 22 bits of each probability.
+// Scores are in base 2 (softmax_scale * log2 e folded in) so exp2 is one
+// instruction.
 
 #include <hip/hip_runtime.h>
 
@@ -22,9 +36,15 @@
 namespace pkv {
 namespace {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kWaves = 4;             // wavefronts per decode workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnit = 16;             // tokens per unit of work (16-row tile slice)
+constexpr int kUnit = 16;             // tokens per unit of work (one MFMA tile of tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -39,36 +59,31 @@ __device__ __forceinline__ float load_elem(const void* p, size_t i) {
   else return bf16_to_f32(((const uint16_t*)p)[i]);
 }
 
-// Cross-lane moves inside a row of 16 lanes (DPP). bound_ctrl: lanes that
-// would read outside the row read 0 (none of the patterns below do).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xF, 0xF, true));
-}
+// DPP moves inside a row of 16 lanes; lanes that would read outside the row
+// read 0 (bound_ctrl).
 constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kHalfMirror = 0x141; // lane i <- 7-i within 8
+constexpr int kMirror = 0x140;     // lane i <- 15-i within 16
+constexpr int kRowShl4 = 0x104;    // lane i <- i+4
+constexpr int kRowShl8 = 0x108;    // lane i <- i+8
+constexpr int kRowShr8 = 0x118;    // lane i <- i-8
 
-// Sum over the LPT consecutive lanes that hold one token row (LPT = 4, 8, 16):
-// after the quad steps every lane holds its quad's sum; the mirror steps pair
-// lanes from different quads / halves, so every lane ends with the group sum.
-template <int LPT>
-__device__ __forceinline__ float row_group_sum(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  if constexpr (LPT >= 8) x += dpp<kHalfMirror>(x);
-  if constexpr (LPT >= 16) x += dpp<kMirror>(x);
-  return x;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
 }
 
 // Maximum over all 64 lanes, returned wave-uniform.
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kQuadXor1>(x));
-  x = fmaxf(x, dpp<kQuadXor2>(x));
-  x = fmaxf(x, dpp<kHalfMirror>(x));
-  x = fmaxf(x, dpp<kMirror>(x));
+  x = fmaxf(x, dpp_f<kQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kMirror>(x));
   const int b = __builtin_bit_cast(int, x);
   const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
   const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
@@ -77,61 +92,70 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Combine the four 16-lane rows holding the same column: lane l with lanes
+// l^16, l^32, l^48 (the swaps exchange whole rows between two registers).
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
+  const int c = __builtin_bit_cast(int, x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
+}
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = __builtin_bit_cast(float, (int)r16[0]) + __builtin_bit_cast(float, (int)r16[1]);
+  const int c = __builtin_bit_cast(int, x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_bit_cast(float, (int)r32[0]) + __builtin_bit_cast(float, (int)r32[1]);
+}
+
 __device__ __forceinline__ int wave_max_int(int x) {
   for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
   return x;
 }
 
-// 16 int8 codes -> fp32 (sign-extending byte conversions).
-__device__ __forceinline__ void cvt_i8x16(const uint4 raw, float* f) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int8_t)(w[i] >> (8 * b));
-}
-
-// 8 binary16 values -> fp32.
-__device__ __forceinline__ void cvt_f16x8(const uint4 raw, float* f) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = f16_to_f32(w[i] & 0xffffu);
-    f[2 * i + 1] = f16_to_f32(w[i] >> 16);
-  }
+// Four int8 codes -> four fp16 values, exactly: each biased byte (code + 128)
+// becomes the low mantissa byte of 1024.0 (0x6400), then 1152 is subtracted.
+__device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  return f16x4{a[0], a[1], b[0], b[1]};
 }
 
 // ---------------------------------------------------------------------------
-// H2: split-context decode.
+// H2: split-context decode on the matrix cores.
 //
-// Lane layout inside a wavefront: a token row of d elements is read by LPT
-// lanes with one 16-byte load each (EPL elements per load); the wavefront
-// covers TPI = 64 / LPT rows per load instruction and NLD loads per 16-token
-// unit. Lane (r, c) = (lane / LPT, lane % LPT) owns dims [c*EPL, c*EPL+EPL)
-// of rows r, r+TPI, ... of each unit.
-//
-// Each wavefront runs an online softmax over the units it is dealt (units
-// u0+w, u0+w+4, ...): per unit it forms the G scores of every row (a dot
-// product of EPL terms per lane, summed over the row's LPT lanes with DPP),
-// takes the unit maximum across the wavefront, rescales its running (m, l, o)
-// only when that maximum grows, then accumulates p * v. Scores are kept in
-// base 2 (softmax_scale * log2 e folded into q) so exp2 is one instruction.
-// The four wavefronts' states are merged through LDS at the end; a sequence
-// that fits in one partition writes its output directly, otherwise the
-// partition's (m, l, o/l) goes to the workspace for the merge kernel.
+// Lane l of a wavefront: n16 = l % 16 (MFMA column / K row), gq = l / 16.
+// Per 16-token unit a lane loads NCH 16-byte chunks of K row n16 (bytes
+// 16*gq + 64*c) and NCH chunks of the V sub-tile (bytes l*16*NCH + 16*c).
+// Each wavefront runs an online softmax over the units dealt to it (units
+// u0+w, u0+w+4, ...): per-head running max m and sum l live in the lanes of
+// that head's column; the accumulators are rescaled only when some head's
+// maximum grows. The four wavefronts merge through LDS; a single-partition
+// sequence writes its output, otherwise the partition's (m, l, o/l) goes to
+// the workspace and the last workgroup of the (sequence, KV head) to finish
+// merges all partitions.
 // ---------------------------------------------------------------------------
 template <bool I8, int D, int G, int QT>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeLaunch a) {
+__device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   constexpr int ESZ = I8 ? 1 : 2;
-  constexpr int EPL = 16 / ESZ;
-  constexpr int LPT = D / EPL;
-  constexpr int TPI = 64 / LPT;
-  constexpr int NLD = kUnit / TPI;
+  constexpr int RB = D * ESZ;       // bytes per K row
+  constexpr int NCH = RB / 64;      // 16-byte chunks per lane per unit (K, and V)
+  constexpr int NDT = D / 16;       // 16-dim tiles of the PV product
+  constexpr int UB = kUnit * RB;    // bytes of one 16-token sub-tile
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane / LPT;
-  const int c = lane % LPT;
+  // wave-uniform: lets unit indices, table entries, scales and tile addresses
+  // live in scalar registers (scalar loads and ALU) instead of every lane
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int gq = lane >> 4;
   const int part = blockIdx.x;
   const int g = blockIdx.y;
   const int s = blockIdx.z;
@@ -151,140 +175,256 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeLaun
   const int upb = bs / kUnit;
   const int hq = a.num_q_heads;
   const int32_t* table = a.tables + (size_t)s * a.max_blocks;
-  const size_t tile_bytes = (size_t)bs * D * ESZ;
+  const size_t tile_bytes = (size_t)bs * RB;
   const char* kcodes = (const char*)a.lv.k_codes;
   const char* vcodes = (const char*)a.lv.v_codes;
 
-  // Query slice of every head of the group, pre-scaled into base 2.
-  float qr[G][EPL];
-  const float qscale = a.softmax_scale * kLog2e;
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      qr[j][e] = load_elem<QT>(a.q, ((size_t)s * hq + g * G + j) * D + c * EPL + e) * qscale;
-
-  float m[G], l[G], o[G][EPL];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
-  }
-
-  const size_t row_off = ((size_t)r * D + c * EPL) * ESZ;
-  uint4 kr[NLD], vr[NLD];
-  float ksc = 1.f, vsc = 1.f;
-  auto load_unit = [&](int u) {
-    const int blk = min(max(table[u / upb], 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
-    const size_t tile = ((size_t)blk * hkv + g) * tile_bytes + (size_t)(u % upb) * kUnit * D * ESZ;
-    const char* kp = kcodes + tile + row_off;
-    const char* vp = vcodes + tile + row_off;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kr[i] = *(const uint4*)(kp + (size_t)i * TPI * D * ESZ);
-      vr[i] = *(const uint4*)(vp + (size_t)i * TPI * D * ESZ);
-    }
+  // One K and one V buffer per lane, software-pipelined: the next unit's K
+  // is requested as soon as this unit's QK product has consumed K, its V as
+  // soon as the PV product has consumed V.
+  uint4 kr[NCH], vr[NCH];
+  size_t sub_next = 0;  // byte offset of the next unit's (block, head) sub-tile
+  float ksc = 1.f, vsc = 1.f, ksc_next = 1.f, vsc_next = 1.f;
+  auto locate = [&](int uu) {  // scalar: table entry, sub-tile offset, scales
+    const int blk = min(max(table[uu / upb], 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
+    sub_next = ((size_t)blk * hkv + g) * tile_bytes + (size_t)(uu % upb) * UB;
     if constexpr (I8) {
-      ksc = a.lv.k_scales[(size_t)blk * hkv + g];
-      vsc = a.lv.v_scales[(size_t)blk * hkv + g];
+      ksc_next = a.lv.k_scales[(size_t)blk * hkv + g];
+      vsc_next = a.lv.v_scales[(size_t)blk * hkv + g];
     }
   };
-
-  int u = u0 + wave;
-  if (u < u1) load_unit(u);
-  for (; u < u1; u += kWaves) {
-    uint4 kc[NLD], vc[NLD];
+  auto load_k = [&]() {
+    const char* kp = kcodes + sub_next + n16 * RB + 16 * gq;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) { kc[i] = kr[i]; vc[i] = vr[i]; }
+    for (int c = 0; c < NCH; ++c) kr[c] = *(const uint4*)(kp + 64 * c);
+  };
+  auto load_v = [&]() {
+    const char* vp = vcodes + sub_next + lane * (16 * NCH);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) vr[c] = *(const uint4*)(vp + 16 * c);
+  };
+  int u = u0 + wave;
+  if (u < u1) {  // first loads go out before the query is prepared
+    locate(u);
+    load_k();
+    load_v();
+  }
+
+  // ---- the query as the B operand of the QK product (Q^T: dims x columns),
+  // built once per workgroup in LDS. Column n16 carries head hc, part pc:
+  // int8 K: pc = digit 0..2 of q rounded to a 22-bit integer; fp16 K: pc = 0
+  // hi / 1 lo fp16 part of q scaled into [2^14, 2^15). The exponent is per
+  // head, from max |q| over its d dims.
+  const int hc = I8 ? (n16 & 3) : (n16 & 7);
+  const int pc = I8 ? (n16 >> 2) : (n16 >> 3);
+  const bool qcol = hc < G && (I8 ? pc < 3 : (pc == 0 || QT == kF32));
+  __shared__ __align__(16) uint32_t sm_qb[NCH * 64 * 4];  // [c][lane][16 bytes]
+  __shared__ int sm_hmax[G];
+  if (threadIdx.x < G) sm_hmax[threadIdx.x] = 0;
+  __syncthreads();
+  constexpr int QPT = (G * D + kThreads - 1) / kThreads;  // query elements per thread
+  float qe[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int e = threadIdx.x + k * kThreads;
+    qe[k] = e < G * D ? load_elem<QT>(a.q, ((size_t)s * hq + g * G) * D + e) : 0.f;
+    if (e < G * D) atomicMax(&sm_hmax[e / D], __float_as_int(fabsf(qe[k])));  // |q| >= 0: int order
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int e = threadIdx.x + k * kThreads;
+    if (e >= G * D) break;
+    const int h = e / D, dim = e % D;
+    int qexp;
+    frexpf(__int_as_float(sm_hmax[h]), &qexp);  // max = f * 2^qexp, f in [0.5, 1)
+    if constexpr (I8) {
+      // q * 2^(22 - qexp) rounded: |qi| < 2^22, so qi + 0x808080 holds the three
+      // balanced digits (each in [-128, 127]) as biased bytes, no carries.
+      const int qi = (int)rintf(ldexpf(qe[k], 22 - qexp));
+      const uint32_t z = (uint32_t)(qi + 0x808080);
+      const int c = dim >> 6, gql = (dim >> 4) & 3, j = dim & 15;
+      unsigned char* b = (unsigned char*)sm_qb;
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+        b[((c * 64 + gql * 16 + 4 * d + h) << 4) + j] = (unsigned char)(((z >> (8 * d)) & 255u) ^ 0x80u);
+    } else {
+      const float y = ldexpf(qe[k], 15 - qexp);
+      const _Float16 hi = (_Float16)y;
+      const int c = dim >> 5, gql = (dim >> 3) & 3, j = dim & 7;
+      _Float16* b = (_Float16*)sm_qb;
+      b[((c * 64 + gql * 16 + h) << 3) + j] = hi;
+      if constexpr (QT == kF32) b[((c * 64 + gql * 16 + 8 + h) << 3) + j] = (_Float16)(y - (float)hi);
+    }
+  }
+  __syncthreads();
+  int qexp;
+  frexpf(__int_as_float(sm_hmax[min(hc, G - 1)]), &qexp);
+  const float qconst = ldexpf(a.softmax_scale * kLog2e, (I8 ? qexp - 22 : qexp - 15));
+  i32x4 qb[I8 ? NCH : 1];
+  f16x8 qh[I8 ? 1 : NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    uint4 w = *(const uint4*)&sm_qb[(c * 64 + lane) * 4];
+    if (!qcol) w = make_uint4(0u, 0u, 0u, 0u);  // columns with no head part
+    if constexpr (I8) qb[c] = __builtin_bit_cast(i32x4, w);
+    else qh[c] = __builtin_bit_cast(f16x8, w);
+  }
+
+  const bool colv = n16 < G;  // this lane's column is a real head (hi / digit 0)
+  float m = -INFINITY, l = 0.f;
+  // P enters the PV product as p * vscale * 2^(14 - ev) with ev the largest
+  // binary exponent of any V scale seen so far (wave-uniform), which keeps
+  // the fp16 parts below 2^14 and their lo part clear of fp16 subnormals;
+  // the accumulators are rescaled exactly when ev grows and scaled back by
+  // 2^(ev - 14) at the end. An fp16 cache has no scale: ev stays 0.
+  int ev = I8 ? -1000 : 0;
+  f32x4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (; u < u1; u += kWaves) {
+    ksc = ksc_next;
+    vsc = vsc_next;
     const float kscale = ksc, vscale = vsc;
     const int tok0 = u * kUnit;
-    if (u + kWaves < u1) load_unit(u + kWaves);  // prefetch the next unit
-    const bool partial = tok0 + kUnit > t1;
+    const bool more = u + kWaves < u1;
+    if (more) locate(u + kWaves);
+    const int nvalid = t1 - tok0;  // rows of this unit inside the partition
 
-    float sc[NLD][G];
+    // S^T = K Q^T: lane holds tokens 4*gq + i of column n16
+    float sc[4];
+    if constexpr (I8) {
+      i32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      float kf[EPL];
-      if constexpr (I8) cvt_i8x16(kc[i], kf); else cvt_f16x8(kc[i], kf);
+      for (int c = 0; c < NCH; ++c)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kr[c]), qb[c], acc, 0, 0, 0);
+      if (more) load_k();
+      const float f = kscale * qconst;
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float acc = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int c1 = dpp_i<kRowShl4>(acc[i]);   // digit-1 column of this head
+        const int c2 = dpp_i<kRowShl8>(acc[i]);   // digit-2 column
+        const int t = acc[i] + (c1 << 8);         // exact, |t| < 2^30
+        sc[i] = fmaf((float)c2, 65536.f, (float)t) * f;
+      }
+    } else {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qr[j][e], kf[e], acc);
-        acc = row_group_sum<LPT>(acc);
-        sc[i][j] = I8 ? acc * kscale : acc;
+      for (int c = 0; c < NCH; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[c]), qh[c], acc, 0, 0, 0);
+      if (more) load_k();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[i];
+        if constexpr (QT == kF32) x += dpp_f<kRowShl8>(x);  // + the lo column
+        sc[i] = x * qconst;
       }
     }
-    if (partial) {
+
+    float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const bool valid = tok0 + i * TPI + r < t1;
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = colv ? (4 * gq + i < nvalid ? sc[i] : -INFINITY) : 0.f;
+      cm = fmaxf(cm, sc[i]);
+    }
+    cm = max_over_lane_groups(cm);  // unit maximum of this lane's column
+    const float mn = fmaxf(m, cm);
+    int evn = ev;
+    if constexpr (I8) {
+      int ve;
+      frexpf(vscale, &ve);  // vscale < 2^ve
+      evn = max(ev, __builtin_amdgcn_readfirstlane(ve));  // uniform: one scale per unit
+    }
+    if (__any(mn > m) || evn > ev) {  // a head's maximum or the V exponent grew (wave-uniform)
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      // lo columns follow their head: lane n16 >= 8 takes lane n16 - 8's alpha.
+      // The DPP result is consumed in every lane (lanes n16 < 8 read 0 from
+      // outside the row) so it cannot be moved under a lane mask, where a
+      // DPP read from a disabled lane would return 0.
+      const float ao = (dpp_f<kRowShr8>(alpha) + (n16 < 8 ? alpha : 0.f)) *
+                       ldexpf(1.0f, ev - evn);  // exact power of two
 #pragma unroll
-        for (int j = 0; j < G; ++j) sc[i][j] = valid ? sc[i][j] : -INFINITY;
-      }
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
+      m = mn;
+      ev = evn;
+    }
+
+    float p[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = colv ? __builtin_amdgcn_exp2f(sc[i] - m) : 0.f;
+      lsum += p[i];
+    }
+    l += lsum;
+    const float pscale = ldexpf(I8 ? vscale : 1.0f, 14 - ev);  // < 2^14
+    f16x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = p[i] * pscale;  // the V scale rides on P
+      const _Float16 hi = (_Float16)pv;
+      ph[i] = hi;
+      pl[i] = (_Float16)(pv - (float)hi);
+    }
+    // B operand of PV: column n16 < 8 is the hi part of head n16, column
+    // 8 + h the lo part of head h (moved over from lane n16 - 8). hi is zero
+    // in lanes 8..15 (no head) and the shifted lo is zero in lanes 0..7
+    // (outside the row), so OR-ing the bits merges them with no lane select.
+    const uint2 hb = __builtin_bit_cast(uint2, ph);
+    const uint2 lb = __builtin_bit_cast(uint2, pl);
+    const f16x4 pb = __builtin_bit_cast(
+        f16x4, make_uint2(hb.x | (uint32_t)dpp_i<kRowShr8>((int)lb.x), hb.y | (uint32_t)dpp_i<kRowShr8>((int)lb.y)));
+
+    uint32_t vw[4 * NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      vw[4 * c] = vr[c].x; vw[4 * c + 1] = vr[c].y; vw[4 * c + 2] = vr[c].z; vw[4 * c + 3] = vr[c].w;
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float cm = sc[0][j];
+    for (int dt = 0; dt < NDT; ++dt) {
+      f16x4 av;
+      if constexpr (I8) {
+        av = i8x4_to_f16x4(vw[dt]);
+      } else {
+        av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
+        if (nvalid < kUnit) {  // rows past the end may hold any bits (NaN included)
 #pragma unroll
-      for (int i = 1; i < NLD; ++i) cm = fmaxf(cm, sc[i][j]);
-      cm = wave_max(cm);
-      if (cm > m[j]) {  // wave-uniform
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - cm);
-        l[j] *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
-        m[j] = cm;
+          for (int j = 0; j < 4; ++j) av[j] = 4 * gq + j < nvalid ? av[j] : (_Float16)0.0f;
+        }
       }
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o[dt], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      float vf[EPL];
-      if constexpr (I8) cvt_i8x16(vc[i], vf); else cvt_f16x8(vc[i], vf);
-      if (partial && tok0 + i * TPI + r >= t1) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;  // rows past the end may hold any bits
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float pj = __builtin_amdgcn_exp2f(sc[i][j] - m[j]);
-        l[j] += pj;
-        const float pv = I8 ? pj * vscale : pj;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(pv, vf[e], o[j][e]);
-      }
-    }
+    if (more) load_v();
   }
 
-  // Sum l and o over the token slots (lanes with equal c).
+  // hi + lo columns, back to unit scale; l summed over the four lane groups
+  const float oscale = ldexpf(1.0f, ev - 14);
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      l[j] += __shfl_xor(l[j], off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[j][e] += __shfl_xor(o[j][e], off);
-    }
-  }
+    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i])) * oscale;
+  l = sum_over_lane_groups(l);
 
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
-  if (r == 0) {
+  __shared__ int sm_last;
+  if (colv) {
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][j][c * EPL + e] = o[j][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) { sm_m[wave][j] = m[j]; sm_l[wave][j] = l[j]; }
+      for (int i = 0; i < 4; ++i) sm_o[wave][n16][16 * dt + 4 * gq + i] = o[dt][i];
+    if (gq == 0) { sm_m[wave][n16] = m; sm_l[wave][n16] = l; }
   }
   __syncthreads();
 
   const size_t pmax = a.max_partitions;
+  const size_t nrow = (size_t)a.num_seqs * hq * pmax;
+  float* ws_m = a.ws;
+  float* ws_l = a.ws + nrow;
+  float* ws_o = a.ws + 2 * nrow;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int j = idx / D;
     const int dd = idx % D;
@@ -294,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeLaun
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(sm_m[w][j] - M);  // empty wave: exp2(-inf) = 0
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w][j] - M);  // idle wave: exp2(-inf) = 0
       L = fmaf(wt, sm_l[w][j], L);
       O = fmaf(wt, sm_o[w][j][dd], O);
     }
@@ -302,19 +442,85 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeLaun
     if (nparts == 1) {
       a.out[((size_t)s * hq + h) * D + dd] = O / L;
     } else {
+      // Partials are stored as device-scope atomics (written through to the
+      // point of coherence shared by all XCDs), so the workgroup that merges
+      // them needs no cache write-back or invalidate, which would cost every
+      // workgroup a pass over its XCD's L2.
       const size_t slot = ((size_t)s * hq + h) * pmax + part;
-      const size_t nrow = (size_t)a.num_seqs * hq * pmax;
-      float* ws_m = a.ws;
-      float* ws_l = a.ws + nrow;
-      float* ws_o = a.ws + 2 * nrow;
-      ws_o[slot * D + dd] = O / L;
-      if (dd == 0) { ws_m[slot] = M; ws_l[slot] = L; }
+      __hip_atomic_store(&ws_o[slot * D + dd], O / L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (dd == 0) {
+        __hip_atomic_store(&ws_m[slot], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws_l[slot], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
+  if (nparts == 1 || !a.fused_merge) return;
+
+  // ---- last arrival of this (sequence, KV head) merges every partition.
+  // Every thread waits until its partial stores have completed before the
+  // workgroup barrier; only then does one thread count the arrival.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm_last = __hip_atomic_fetch_add(&a.counters[(size_t)s * hkv + g], 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+  __syncthreads();
+  if (!sm_last) return;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int j = idx / D;
+    const int dd = idx % D;
+    const size_t base = ((size_t)s * hq + g * G + j) * pmax;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += 8) {  // 8 partitions' loads in flight at a time
+      float pm[8], pl[8], po[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = p0 + k < nparts;
+        const size_t r = base + (ok ? p0 + k : 0);
+        const float vm = __hip_atomic_load(&ws_m[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float vl = __hip_atomic_load(&ws_l[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float vo = __hip_atomic_load(&ws_o[r * D + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pm[k] = ok ? vm : -INFINITY;
+        pl[k] = ok ? vl : 0.f;
+        po[k] = ok ? vo : 0.f;
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, pm[k]);
+      const float r = __builtin_amdgcn_exp2f(M - Mn);  // M = -inf on the first chunk: 0
+      L *= r;
+      O *= r;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = __builtin_amdgcn_exp2f(pm[k] - Mn) * pl[k];
+        L += w;
+        O = fmaf(w, po[k], O);
+      }
+      M = Mn;
+    }
+    a.out[((size_t)s * hq + g * G + j) * D + dd] = O / L;
+  }
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(&a.counters[(size_t)s * hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Both variants fit in 128 registers: four wavefronts per SIMD, so the
+// automatic partition size can keep every workgroup of a launch resident.
+template <int D, int G, int QT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void decode_kernel_i8(const DecodeLaunch a) {
+  decode_body<true, D, G, QT>(a);
+}
+template <int D, int G, int QT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void decode_kernel_f16(const DecodeLaunch a) {
+  decode_body<false, D, G, QT>(a);
 }
 
 // ---------------------------------------------------------------------------
-// H3: merge the partitions of each (sequence, query head):
+// H3 as its own launch: merge the partitions of each (sequence, query head):
 //   M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p
 // where o_p is the partition's normalised output and m_p its base-2 maximum.
 // ---------------------------------------------------------------------------
@@ -336,6 +542,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const DecodeLaunch a) {
   float M = -INFINITY;
   for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_m[base + p]);
   float L = 0.f, O = 0.f;
+#pragma unroll 8
   for (int p = 0; p < nparts; ++p) {
     const float w = __builtin_amdgcn_exp2f(ws_m[base + p] - M) * ws_l[base + p];
     L += w;
@@ -365,21 +572,25 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
   const int64_t i = rest >> 1;
   const int64_t slot = slots[i];
   const int64_t blk = slot / lv.block_size;
-  const int64_t row = slot % lv.block_size;
+  const int row = (int)(slot % lv.block_size);
   if (slot < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
   const void* src = kv ? v : k;
   const size_t sbase = ((size_t)i * hkv + h) * D + ch * 8;
-  uint32_t packed[4];
+  uint16_t hv[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const _Float16 lo = (_Float16)load_elem<IN>(src, sbase + 2 * e);
-    const _Float16 hi = (_Float16)load_elem<IN>(src, sbase + 2 * e + 1);
-    packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  for (int e = 0; e < 8; ++e)
+    hv[e] = __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, sbase + e));
+  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
+                   ((size_t)blk * hkv + h) * lv.block_size * D;
+  if (kv == 0) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)hv[2 * e] | ((uint32_t)hv[2 * e + 1] << 16);
+    *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[v_tile_offset(row, ch * 8 + e, D)] = hv[e];
   }
-  uint16_t* dst = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
-                  (((size_t)blk * hkv + h) * lv.block_size + row) * D + ch * 8;
-  *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,12 +640,13 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
 
   int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
   float* sp = (kv ? lv.v_scales : lv.k_scales) + (size_t)blk * hkv + h;
+  auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
   float sc;
   if (row0 == 0) {
     sc = scale_of(mx);
   } else {
     int qm = 0;
-    for (int e = lane; e < row0 * D; e += 64) qm = max(qm, abs((int)tile[e]));
+    for (int e = lane; e < row0 * D; e += 64) qm = max(qm, abs((int)tile[off(e / D, e % D)]));
     qm = wave_max_int(qm);
     const float s_old = *sp;
     const float m_old = (float)qm * s_old;
@@ -442,23 +654,34 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
       sc = s_old;
     } else {
       sc = scale_of(mx);
-      for (int e = lane; e < row0 * D; e += 64) tile[e] = encode((float)tile[e] * s_old, sc);
+      for (int e = lane; e < row0 * D; e += 64) {
+        int8_t* c = tile + off(e / D, e % D);
+        *c = encode((float)*c * s_old, sc);
+      }
     }
   }
   for (int e = lane; e < nr * D; e += 64) {
     const int rr = e / D, dd = e % D;
-    tile[(size_t)row0 * D + e] = encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc);
+    tile[off(row0 + rr, dd)] = encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc);
   }
   if (lane == 0) *sp = sc;
 }
 
+template <bool I8, int D, int G, int QT>
+void launch_one(const DecodeLaunch& d, hipStream_t stream) {
+  const dim3 grid(d.max_partitions, d.lv.num_kv_heads, d.num_seqs);
+  if constexpr (I8)
+    hipLaunchKernelGGL((decode_kernel_i8<D, G, QT>), grid, dim3(kThreads), 0, stream, d);
+  else
+    hipLaunchKernelGGL((decode_kernel_f16<D, G, QT>), grid, dim3(kThreads), 0, stream, d);
+}
+
 template <bool I8, int D, int G>
 hipError_t launch_decode_q(const DecodeLaunch& d, hipStream_t stream) {
-  const dim3 grid(d.max_partitions, d.lv.num_kv_heads, d.num_seqs);
   switch (d.q_dtype) {
-    case kF32: hipLaunchKernelGGL((decode_split_kernel<I8, D, G, kF32>), grid, dim3(kThreads), 0, stream, d); break;
-    case kF16: hipLaunchKernelGGL((decode_split_kernel<I8, D, G, kF16>), grid, dim3(kThreads), 0, stream, d); break;
-    case kBF16: hipLaunchKernelGGL((decode_split_kernel<I8, D, G, kBF16>), grid, dim3(kThreads), 0, stream, d); break;
+    case kF32: launch_one<I8, D, G, kF32>(d, stream); break;
+    case kF16: launch_one<I8, D, G, kF16>(d, stream); break;
+    case kBF16: launch_one<I8, D, G, kBF16>(d, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -474,17 +697,23 @@ hipError_t launch_decode_g(const DecodeLaunch& d, int group, hipStream_t stream)
   }
 }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 bool decode_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
 }
 
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                              int32_t max_partitions) {
+size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+}
+
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_partitions) {
   if (max_partitions <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
-  return rows * (2 + (size_t)head_dim) * sizeof(float);
+  return decode_counter_bytes(num_seqs, num_kv_heads) + rows * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
@@ -495,7 +724,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     e = i8 ? launch_decode_g<true, 128>(d, group, stream) : launch_decode_g<false, 128>(d, group, stream);
   else
     e = i8 ? launch_decode_g<true, 64>(d, group, stream) : launch_decode_g<false, 64>(d, group, stream);
-  if (e != hipSuccess || d.max_partitions <= 1) return e;
+  if (e != hipSuccess || d.max_partitions <= 1 || d.fused_merge) return e;
   const dim3 grid((unsigned)(d.num_seqs * d.num_q_heads));
   if (d.lv.head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, d);

@@ -405,16 +405,17 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
   if (!pool || num_seqs < 1 || num_q_heads < 1 || max_context_len < 1) return 0;
   const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
   const int32_t P = (max_context_len + T - 1) / T;
-  return pkv::decode_workspace_bytes(num_seqs, num_q_heads, pool->cfg.head_dim, P);
+  return pkv::decode_workspace_bytes(num_seqs, num_q_heads, pool->cfg.num_kv_heads, pool->cfg.head_dim, P);
 }
 
 pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
                                 int32_t num_q_heads, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
                                 int32_t num_seqs, int32_t max_context_len, float softmax_scale,
-                                int32_t partition_tokens, float* out, void* workspace,
+                                int32_t partition_tokens, int32_t flags, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (flags & ~PKV_DECODE_SEPARATE_MERGE) return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
   const pkv_pool_config& c = pool->cfg;
   if (layer < 0 || layer >= c.num_layers)
@@ -440,7 +441,7 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
     return fail(PKV_ERR_INVALID_ARG, "NULL q, block_tables, context_lens or out");
   const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
   const int32_t P = (max_context_len + T - 1) / T;
-  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, c.head_dim, P);
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, c.num_kv_heads, c.head_dim, P);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (P > 65535) return fail(PKV_ERR_UNSUPPORTED, "%d partitions exceed the grid limit", P);
@@ -458,7 +459,9 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
   d.max_partitions = P;
   d.softmax_scale = softmax_scale;
   d.out = out;
-  d.ws = (float*)workspace;
+  d.counters = (int32_t*)workspace;
+  d.ws = need > 0 ? (float*)((char*)workspace + pkv::decode_counter_bytes(num_seqs, c.num_kv_heads)) : nullptr;
+  d.fused_merge = (flags & PKV_DECODE_SEPARATE_MERGE) ? 0 : 1;
   hipError_t e = pkv::launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -477,14 +480,24 @@ pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* b
       return fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", blocks[i], c.num_blocks);
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "synchronize before read-back");
-  const size_t tile_bytes = (size_t)c.num_kv_heads * pool->tile_elems * elem_bytes(c.kv_dtype);
+  const size_t esz = elem_bytes(c.kv_dtype);
+  const size_t tile_bytes = (size_t)c.num_kv_heads * pool->tile_elems * esz;
   const pkv::LayerView lv = pool->layer_view(layer);
+  std::vector<char> raw(tile_bytes);
   for (int32_t i = 0; i < n; ++i) {
     for (int kv = 0; kv < 2; ++kv) {
       const char* src = (const char*)(kv ? lv.v_codes : lv.k_codes) + (size_t)blocks[i] * tile_bytes;
       char* dst = (char*)codes_out + ((size_t)i * 2 + kv) * tile_bytes;
-      e = hipMemcpy(dst, src, tile_bytes, hipMemcpyDeviceToHost);
+      e = hipMemcpy(kv ? raw.data() : dst, src, tile_bytes, hipMemcpyDeviceToHost);
       if (e != hipSuccess) return hip_fail(e, "read-back of codes");
+      if (kv) {  // V tiles are stored in matrix-core order: put them back in [token][dim]
+        const size_t te = pool->tile_elems;
+        for (int32_t hd = 0; hd < c.num_kv_heads; ++hd)
+          for (int32_t t = 0; t < c.block_size; ++t)
+            for (int32_t d = 0; d < c.head_dim; ++d)
+              std::memcpy(dst + (hd * te + (size_t)t * c.head_dim + d) * esz,
+                          raw.data() + (hd * te + pkv::v_tile_offset(t, d, c.head_dim)) * esz, esz);
+      }
       if (scales_out && pool->scales) {
         const float* ssrc = (kv ? lv.v_scales : lv.k_scales) + (size_t)blocks[i] * c.num_kv_heads;
         e = hipMemcpy(scales_out + ((size_t)i * 2 + kv) * c.num_kv_heads, ssrc,

@@ -31,6 +31,7 @@ STATUS_NAMES = {
 }
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
+PKV_DECODE_SEPARATE_MERGE = 1
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p
@@ -66,7 +67,7 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
     "pkv_decode_auto_partition": (_i32, [_vp, _i32, _i32, _i32]),
     "pkv_decode_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
-                                       _f32, _i32, _vp, _vp, _sz, _vp]),
+                                       _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
@@ -207,9 +208,9 @@ def pkv_decode_auto_partition(h, num_seqs, num_q_heads, max_context_len) -> int:
 
 
 def pkv_decode_attention(h, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
-                         out, workspace=None, partition_tokens=0, stream=None) -> None:
+                         out, workspace=None, partition_tokens=0, stream=None, flags=0) -> None:
     """q: [B][Hq][d] device tensor; block_tables [B][max_blocks] int32; context_lens [B] int32;
-    out: [B][Hq][d] float32; workspace: uint8 device tensor or None."""
+    out: [B][Hq][d] float32; workspace: zero-initialised uint8 device tensor or None."""
     assert q.is_contiguous() and block_tables.is_contiguous() and context_lens.is_contiguous()
     assert out.is_contiguous() and out.dtype.itemsize == 4
     B, hq, _ = q.shape
@@ -218,7 +219,7 @@ def pkv_decode_attention(h, layer, q, block_tables, context_lens, max_context_le
     _check(lib().pkv_decode_attention(
         h, layer, _vp(q.data_ptr()), _torch_dtype_code(q), hq, _vp(block_tables.data_ptr()),
         int(block_tables.shape[1]), _vp(context_lens.data_ptr()), B, int(max_context_len),
-        float(softmax_scale), int(partition_tokens), _vp(out.data_ptr()), ws_ptr, ws_bytes,
+        float(softmax_scale), int(partition_tokens), int(flags), _vp(out.data_ptr()), ws_ptr, ws_bytes,
         _stream_ptr(stream)))
 
 
@@ -315,15 +316,16 @@ class Pool:
         return pkv_decode_auto_partition(self.h, num_seqs, num_q_heads, max_context_len)
 
     def decode(self, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
-               out=None, workspace=None, partition_tokens=0, stream=None):
+               out=None, workspace=None, partition_tokens=0, stream=None, flags=0):
+        """workspace, if given, must have been zero-filled before its first use."""
         import torch
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if workspace is None:
             nb = self.workspace_bytes(q.shape[0], q.shape[1], max_context_len, partition_tokens)
-            workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
         pkv_decode_attention(self.h, layer, q, block_tables, context_lens, max_context_len,
-                             softmax_scale, out, workspace, partition_tokens, stream)
+                             softmax_scale, out, workspace, partition_tokens, stream, flags)
         return out
 
     def read_blocks(self, layer, blocks):

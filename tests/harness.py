@@ -226,7 +226,7 @@ def make_gpu_pool(case: Case, device="cuda"):
                     initial_free_order=free_order(sh, case.seed), device=device)
 
 
-def run_decode_case(case: Case, partition_tokens=0, layers=None, compare_cache=True):
+def run_decode_case(case: Case, partition_tokens=0, layers=None, compare_cache=True, flags=0):
     """Replay the script on both sides, compare caches bit for bit, decode on
     the GPU and compare with the FP64 oracle over the GPU's read-back cache."""
     import torch
@@ -251,7 +251,7 @@ def run_decode_case(case: Case, partition_tokens=0, layers=None, compare_cache=T
     res = {"gpu": [], "ref": []}
     for layer in (range(sh.layers) if layers is None else layers):
         out = pool.decode(layer, q.to(dev), t_table, t_lens, int(lens.max()), sh.scale,
-                          partition_tokens=partition_tokens)
+                          partition_tokens=partition_tokens, flags=flags)
         torch.cuda.synchronize()
         kc, vc, ks, vs = gpu_layer_arrays(pool, layer, rows.keys(), sh)
         ref = orc.decode_attention(sh.kv_dtype, kc, vc, ks, vs, synth.as_f32(q), table, lens, sh.scale)
