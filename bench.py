@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
     ap.add_argument("--separate-merge", action="store_true",
                     help="merge partitions in a second launch instead of the last workgroup")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     return ap.parse_args()
@@ -159,7 +161,7 @@ class Workload:
             self.vnew.append(v)
         self.max_blocks = max((int(n) + appends + self.bs - 1) // self.bs for n in lens0) + 1
         self.out = torch.empty(self.B, self.hq, self.dim, dtype=torch.float32, device=self.dev)
-        max_ctx = int(lens0.max()) + appends
+        self.max_ctx = max_ctx = int(lens0.max()) + appends
         ws = self.pool.workspace_bytes(self.B, self.hq, max_ctx, self.partition)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.dev)
         # pinned staging ring for the per-step uploads
@@ -174,8 +176,6 @@ class Workload:
         self.d_table = torch.empty(self.B, self.max_blocks, dtype=torch.int32, device=self.dev)
         self.d_lens = torch.empty(self.B, dtype=torch.int32, device=self.dev)
         self.step_i = 0
-        self.decode_events = []  # (start, end, kv_read_bytes) per decode launch
-        self.record = False
 
     def _append_all(self, kv_fill, slots):
         t = self.torch
@@ -195,8 +195,9 @@ class Workload:
             b += int(sum((int(n) + self.bs - 1) // self.bs for n in lens)) * self.hkv * 2 * 4
         return b
 
-    def step(self):
-        t = self.torch
+    def host_prep(self):
+        """Host side of a step: one new slot per sequence from the allocator,
+        the block tables rebuilt, both staged in pinned memory and uploaded."""
         slot = self.ring[self.step_i % len(self.ring)]
         slot["ev"].synchronize()  # the upload that last used this staging slot is done
         slots = self.pool.append_slots(self.seqs, np.ones(self.B, dtype=np.int32))
@@ -208,22 +209,25 @@ class Workload:
         self.d_table.copy_(slot["table"], non_blocking=True)
         self.d_lens.copy_(slot["lens"], non_blocking=True)
         slot["ev"].record()
-        max_ctx = int(lens.max())
-        layers = range(self.L) if not self.rotate else [self.step_i % self.L]
-        nbytes = self.kv_read_bytes(lens)
-        for layer in layers:
-            self.pool.append_kv(layer, self.knew[layer], self.vnew[layer], self.d_slots)
-            if self.record:
-                e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-                e0.record()
-            self.pool.decode(layer, self.q[layer], self.d_table, self.d_lens, max_ctx, self.scale,
-                             out=self.out, workspace=self.ws, partition_tokens=self.partition,
-                             flags=self.flags)
-            if self.record:
-                e1.record()
-                self.decode_events.append((e0, e1, nbytes))
         self.step_i += 1
         return lens
+
+    def device_step(self, layers=None, decode_only=False):
+        """Device side of a step: per layer, append the new tokens' K/V, then
+        decode. max_context_len is the capacity for the whole run, so the
+        launch shapes never change (the kernels read the true lengths)."""
+        dec = set(range(self.L) if layers is None else layers)
+        for layer in range(self.L):  # every layer receives the new token
+            if not decode_only:
+                self.pool.append_kv(layer, self.knew[layer], self.vnew[layer], self.d_slots)
+            if layer in dec:
+                self.pool.decode(layer, self.q[layer], self.d_table, self.d_lens, self.max_ctx,
+                                 self.scale, out=self.out, workspace=self.ws,
+                                 partition_tokens=self.partition, flags=self.flags)
+
+    def decode_layers(self, step_i):
+        """Layers decoded in a step (one rotating copy for the long-context runs)."""
+        return range(self.L) if not self.rotate else [step_i % self.L]
 
 
 def cpu_baseline(w: Workload, target_s: float):
@@ -276,29 +280,84 @@ def main():
     from paged_kv_cache_62_amd import pkv
     pkv.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
+    with torch.cuda.stream(stream):
+        res = run(args, stream)
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(res.pop("_workload"), args.cpu_seconds)
+    else:
+        res.pop("_workload")
+    print(json.dumps(res), flush=True)
+
+
+def run(args, stream):
+    import torch
+    from paged_kv_cache_62_amd import pkv
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
     w = Workload(args.config, args.warmup + args.steps, args.partition,
                  flags=pkv.PKV_DECODE_SEPARATE_MERGE if args.separate_merge else 0)
+    graphs = {}
+    if not args.no_graph:
+        # The device work of a step, captured once as a HIP graph per layer
+        # set (all layers, or each rotating copy) and replayed every step.
+        w.host_prep()
+        for key in sorted({tuple(w.decode_layers(i)) for i in range(max(2, w.L))}):
+            w.device_step(key)  # eager once before capture
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                w.device_step(key)
+            graphs[key] = g
+        torch.cuda.synchronize()
+
+    def run_step():
+        i = w.step_i
+        lens = w.host_prep()
+        key = tuple(w.decode_layers(i))
+        if graphs:
+            graphs[key].replay()
+        else:
+            w.device_step(key)
+        return lens
+
     for _ in range(args.warmup):
-        w.step()
+        run_step()
     torch.cuda.synchronize()
     print(f"# warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
-    w.record = True
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_bytes = []
     start.record()
     tokens = 0
     for _ in range(args.steps):
-        w.step()
+        lens = run_step()
+        step_bytes.append(w.kv_read_bytes(lens) * len(w.decode_layers(0)))
         tokens += w.B
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    durs = np.array([e0.elapsed_time(e1) for e0, e1, _ in w.decode_events])  # ms
-    nbytes = np.array([b for _, _, b in w.decode_events], dtype=np.float64)
-    avg_dur_s = durs.mean() / 1e3
-    achieved = nbytes.mean() / avg_dur_s / 1e9
-    kv_gbs_step = nbytes.sum() / (total_ms / 1e3) / 1e9
+
+    # The decode kernel alone: a graph of the step's decode launches on the
+    # same stream, replayed back to back between two events; the cache is in
+    # its final state, so each launch reads the current lengths.
+    layers = list(w.decode_layers(0))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        w.device_step(layers, decode_only=True)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(5, int(args.kernel_reps))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    avg_dur_s = e0.elapsed_time(e1) / 1e3 / (reps * len(layers))
+    _, lens_now = w.pool.block_table(w.seqs, w.max_blocks)
+    bytes_launch = float(w.kv_read_bytes(lens_now))
+    achieved = bytes_launch / avg_dur_s / 1e9
+    kv_gbs_step = float(np.sum(step_bytes)) / (total_ms / 1e3) / 1e9
     res = {
         "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
         "value": tokens / (total_ms / 1e3),
@@ -313,20 +372,19 @@ def main():
         "dtype": "int8 kv / fp32 accumulate" if w.kv_code == pkv.PKV_I8 else "fp16 kv / fp32 accumulate",
         "data": "synthetic (seeded), cache filled through pkv_append_kv before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": w.B,
-                   "layers_per_step": 1 if w.rotate else w.L,
-                   "partition_tokens": w.pool.auto_partition(w.B, w.hq, int(w.d_lens.max().item()))
-                   if not w.partition else w.partition,
+                   "layers_per_step": len(layers),
+                   "partition_tokens": w.partition or w.pool.auto_partition(w.B, w.hq, w.max_ctx),
+                   "merge": "separate launch" if args.separate_merge else "last workgroup",
+                   "hip_graph": not args.no_graph,
                    "kv_read_GBps_whole_step": kv_gbs_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_split_kernel (+ merge when partitioned)",
-                     "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": nbytes.mean()},
+                     "kernel": "decode_kernel (split-context decode incl. partition merge)",
+                     "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
+                     "timing": f"HIP events around {reps} replays of a graph of the {len(layers)} decode launches"},
     }
-    if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
-
+    res["_workload"] = w
+    return res
 
 if __name__ == "__main__":
     main()

@@ -149,6 +149,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   constexpr int NCH = RB / 64;      // 16-byte chunks per lane per unit (K, and V)
   constexpr int NDT = D / 16;       // 16-dim tiles of the PV product
   constexpr int UB = kUnit * RB;    // bytes of one 16-token sub-tile
+  constexpr int NB = I8 ? 3 : 2;    // units in flight per wavefront
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: lets unit indices, table entries, scales and tile addresses
@@ -179,36 +180,56 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const char* kcodes = (const char*)a.lv.k_codes;
   const char* vcodes = (const char*)a.lv.v_codes;
 
-  // One K and one V buffer per lane, software-pipelined: the next unit's K
-  // is requested as soon as this unit's QK product has consumed K, its V as
-  // soon as the PV product has consumed V.
-  uint4 kr[NCH], vr[NCH];
-  size_t sub_next = 0;  // byte offset of the next unit's (block, head) sub-tile
-  float ksc = 1.f, vsc = 1.f, ksc_next = 1.f, vsc_next = 1.f;
-  auto locate = [&](int uu) {  // scalar: table entry, sub-tile offset, scales
-    const int blk = min(max(table[uu / upb], 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
-    sub_next = ((size_t)blk * hkv + g) * tile_bytes + (size_t)(uu % upb) * UB;
+  // ---- this wavefront's units are u0 + wave + kWaves*i, i < nu. Lane i
+  // gathers unit i's block id and scales with vector loads (64 units at a
+  // time); the loop reads them back with readlane. Scalar loads would put
+  // their latency on the loop's path: they can only be awaited all at once.
+  const int ufirst = u0 + wave;
+  const int nu = ufirst < u1 ? (u1 - ufirst + kWaves - 1) / kWaves : 0;
+  int ublk = 0;
+  float uks = 1.f, uvs = 1.f;
+  auto gather_blocks = [&](int base) {
+    const int i = base + lane;
+    if (i < nu) ublk = min(max(table[(ufirst + kWaves * i) / upb], 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
+  };
+  auto gather_scales = [&](int base) {
     if constexpr (I8) {
-      ksc_next = a.lv.k_scales[(size_t)blk * hkv + g];
-      vsc_next = a.lv.v_scales[(size_t)blk * hkv + g];
+      if (base + lane < nu) {
+        uks = a.lv.k_scales[(size_t)ublk * hkv + g];
+        uvs = a.lv.v_scales[(size_t)ublk * hkv + g];
+      }
     }
   };
-  auto load_k = [&]() {
-    const char* kp = kcodes + sub_next + n16 * RB + 16 * gq;
+  // NB-deep ring of K/V buffers: unit i is requested NB units before use.
+  uint4 kb[NB][NCH], vb[NB][NCH];
+  auto issue = [&](int i, int base, uint4 (&kd)[NCH], uint4 (&vd)[NCH]) {
+    const int blk = __builtin_amdgcn_readlane(ublk, i - base);
+    const int uu = ufirst + kWaves * i;
+    const size_t sub = ((size_t)blk * hkv + g) * tile_bytes + (size_t)(uu % upb) * UB;
+    const char* kp = kcodes + sub + n16 * RB + 16 * gq;
+    const char* vp = vcodes + sub + lane * (16 * NCH);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kr[c] = *(const uint4*)(kp + 64 * c);
-  };
-  auto load_v = [&]() {
-    const char* vp = vcodes + sub_next + lane * (16 * NCH);
+    for (int c = 0; c < NCH; ++c) kd[c] = *(const uint4*)(kp + 64 * c);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) vr[c] = *(const uint4*)(vp + 16 * c);
+    for (int c = 0; c < NCH; ++c) vd[c] = *(const uint4*)(vp + 16 * c);
   };
-  int u = u0 + wave;
-  if (u < u1) {  // first loads go out before the query is prepared
-    locate(u);
-    load_k();
-    load_v();
+  // Start-up order: block ids (the K/V loads depend on them), then the
+  // query, then scales and the first NB units. Vector loads complete in
+  // order, so each wait below covers only what was issued before it.
+  gather_blocks(0);
+  // the query's elements for this workgroup
+  constexpr int QPT = (G * D + kThreads - 1) / kThreads;  // query elements per thread
+  float qe[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int e = threadIdx.x + k * kThreads;
+    qe[k] = e < G * D ? load_elem<QT>(a.q, ((size_t)s * hq + g * G) * D + min(e, G * D - 1)) : 0.f;
   }
+
+  gather_scales(0);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (b < nu) issue(b, 0, kb[b], vb[b]);
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -222,12 +243,9 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   __shared__ int sm_hmax[G];
   if (threadIdx.x < G) sm_hmax[threadIdx.x] = 0;
   __syncthreads();
-  constexpr int QPT = (G * D + kThreads - 1) / kThreads;  // query elements per thread
-  float qe[QPT];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int e = threadIdx.x + k * kThreads;
-    qe[k] = e < G * D ? load_elem<QT>(a.q, ((size_t)s * hq + g * G) * D + e) : 0.f;
     if (e < G * D) atomicMax(&sm_hmax[e / D], __float_as_int(fabsf(qe[k])));  // |q| >= 0: int order
   }
   __syncthreads();
@@ -283,13 +301,8 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (; u < u1; u += kWaves) {
-    ksc = ksc_next;
-    vsc = vsc_next;
-    const float kscale = ksc, vscale = vsc;
-    const int tok0 = u * kUnit;
-    const bool more = u + kWaves < u1;
-    if (more) locate(u + kWaves);
+  auto process = [&](const uint4 (&kr)[NCH], const uint4 (&vr)[NCH], float kscale, float vscale,
+                     int tok0) {
     const int nvalid = t1 - tok0;  // rows of this unit inside the partition
 
     // S^T = K Q^T: lane holds tokens 4*gq + i of column n16
@@ -299,7 +312,6 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kr[c]), qb[c], acc, 0, 0, 0);
-      if (more) load_k();
       const float f = kscale * qconst;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -313,7 +325,6 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[c]), qh[c], acc, 0, 0, 0);
-      if (more) load_k();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = acc[i];
@@ -396,7 +407,29 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       }
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o[dt], 0, 0, 0);
     }
-    if (more) load_v();
+  };
+
+  for (int cb = 0; cb < nu; cb += 64) {
+    const int cn = min(64, nu - cb);
+    if (cb > 0) {  // next 64 units: their bookkeeping, then the ring
+      gather_blocks(cb);
+      gather_scales(cb);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < cn) issue(cb + b, cb, kb[b], vb[b]);
+    }
+    for (int i0 = 0; i0 < cn; i0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + b;
+        if (i < cn) {
+          const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
+          const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
+          process(kb[b], vb[b], ks, vs, (ufirst + kWaves * (cb + i)) * kUnit);
+          if (i + NB < cn) issue(cb + i + NB, cb, kb[b], vb[b]);
+        }
+      }
+    }
   }
 
   // hi + lo columns, back to unit scale; l summed over the four lane groups
@@ -473,10 +506,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     const int dd = idx % D;
     const size_t base = ((size_t)s * hq + g * G + j) * pmax;
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += 8) {  // 8 partitions' loads in flight at a time
-      float pm[8], pl[8], po[8];
+    for (int p0 = 0; p0 < nparts; p0 += 16) {  // 16 partitions' loads in flight at a time
+      float pm[16], pl[16], po[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 16; ++k) {
         const bool ok = p0 + k < nparts;
         const size_t r = base + (ok ? p0 + k : 0);
         const float vm = __hip_atomic_load(&ws_m[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -488,12 +521,12 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       }
       float Mn = M;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, pm[k]);
+      for (int k = 0; k < 16; ++k) Mn = fmaxf(Mn, pm[k]);
       const float r = __builtin_amdgcn_exp2f(M - Mn);  // M = -inf on the first chunk: 0
       L *= r;
       O *= r;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 16; ++k) {
         const float w = __builtin_amdgcn_exp2f(pm[k] - Mn) * pl[k];
         L += w;
         O = fmaf(w, po[k], O);
@@ -506,15 +539,16 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     __hip_atomic_store(&a.counters[(size_t)s * hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Both variants fit in 128 registers: four wavefronts per SIMD, so the
-// automatic partition size can keep every workgroup of a launch resident.
+// Both variants fit in 168 registers with their K/V rings: three wavefronts
+// (three workgroups) per SIMD pair of registers budget, i.e. 768 resident
+// workgroups on 256 CUs.
 template <int D, int G, int QT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_i8(const DecodeLaunch a) {
   decode_body<true, D, G, QT>(a);
 }
 template <int D, int G, int QT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_f16(const DecodeLaunch a) {
   decode_body<false, D, G, QT>(a);
 }
@@ -613,55 +647,106 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
                                                         const void* v, const int64_t* slots,
                                                         int32_t n) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = lv.num_kv_heads;
   if (wid >= (int64_t)n * hkv * 2) return;
   const int h = (int)(wid % hkv);
   const int kv = (int)((wid / hkv) & 1);
   const int64_t i = wid / hkv / 2;
   const int bs = lv.block_size;
+  const int lbs = __builtin_ctz(bs);  // block sizes are powers of two
   const int D = lv.head_dim;
-  const int64_t slot0 = slots[i];
-  const int64_t blk = slot0 / bs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && slots[i - 1] / bs == blk) return;  // not the first token of its run
-  int nr = 1;
-  while (i + nr < n && slots[i + nr] / bs == blk) ++nr;
-  const int row0 = (int)(slot0 % bs);
-  nr = min(nr, bs - row0);  // rows stay inside the tile even for malformed slots
+  const int ld = __builtin_ctz(D);  // head_dim is 64 or 128: shifts instead of divisions
 
-  const void* src = kv ? v : k;
-  float mx = 0.f;
-  for (int e = lane; e < nr * D; e += 64) {
-    const int rr = e / D, dd = e % D;
-    mx = fmaxf(mx, fabsf(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd)));
-  }
-  mx = wave_max(mx);
+  // The slots of tokens i .. i+63, one per lane, and of token i-1: the run
+  // starting at i is the leading lanes whose slot lies in the same block.
+  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
+  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
+  const int64_t blk = slot0 >> lbs;
+  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
+  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
+  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
+  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
+  const int row0 = (int)(slot0 & (bs - 1));
+  const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
 
   int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
   float* sp = (kv ? lv.v_scales : lv.k_scales) + (size_t)blk * hkv + h;
   auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
+  const void* src = kv ? v : k;
+
+  // Everything this wave reads goes out before the first wait: the block's
+  // old codes (rows < row0, 16 bytes per load), its scale, the new values.
+  // Old rows of a K tile are its first row0*D bytes; those of a V tile lie
+  // in its first ceil(row0/16) 16-token sub-tiles, where each byte's token
+  // is decoded from its offset.
+  const int old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
+  constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
+  uint4 oc[kMaxChunks];
+  uint32_t valid_mask[kMaxChunks];  // bit b: byte b of chunk belongs to a row < row0
+  int qm = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxChunks; ++k) {
+    const int c = lane + 64 * k;
+    valid_mask[k] = 0;
+    if (c * 16 < old_bytes) {
+      oc[k] = *(const uint4*)(tile + (size_t)c * 16);
+      const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        bool valid = true;
+        if (kv) {
+          const int byte = c * 16 + b;
+          const int sub = byte >> (ld + 4);                     // 16-token sub-tile
+          const int L = (byte & ((16 << ld) - 1)) >> (ld - 2);  // lane chunk tg*16 + dm
+          valid = sub * 16 + (L >> 4) * 4 + (byte & 3) < row0;
+        }
+        if (valid) {
+          valid_mask[k] |= 1u << b;
+          qm = max(qm, abs((int)(int8_t)(ws[b >> 2] >> (8 * (b & 3)))));
+        }
+      }
+    }
+  }
+  const float s_old = row0 > 0 ? *sp : 1.f;
+  float mx = 0.f;
+  for (int e = lane; e < nr * D; e += 64)
+    mx = fmaxf(mx, fabsf(load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1)))));
+  mx = wave_max(mx);
+
   float sc;
   if (row0 == 0) {
     sc = scale_of(mx);
   } else {
-    int qm = 0;
-    for (int e = lane; e < row0 * D; e += 64) qm = max(qm, abs((int)tile[off(e / D, e % D)]));
     qm = wave_max_int(qm);
-    const float s_old = *sp;
     const float m_old = (float)qm * s_old;
     if (mx <= m_old) {
       sc = s_old;
     } else {
+      // the max grew: re-encode the old codes from their dequantised values,
+      // in the registers they were read into, and store whole chunks back
+      // (bytes of rows >= row0 are written back unchanged)
       sc = scale_of(mx);
-      for (int e = lane; e < row0 * D; e += 64) {
-        int8_t* c = tile + off(e / D, e % D);
-        *c = encode((float)*c * s_old, sc);
+#pragma unroll
+      for (int k = 0; k < kMaxChunks; ++k) {
+        const int c = lane + 64 * k;
+        if (c * 16 < old_bytes) {
+          uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
+#pragma unroll
+          for (int b = 0; b < 16; ++b) {
+            if (valid_mask[k] & (1u << b)) {
+              const int code = (int)(int8_t)(ws[b >> 2] >> (8 * (b & 3)));
+              const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, sc);
+              ws[b >> 2] = (ws[b >> 2] & ~(0xFFu << (8 * (b & 3)))) | (q << (8 * (b & 3)));
+            }
+          }
+          *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+        }
       }
     }
   }
   for (int e = lane; e < nr * D; e += 64) {
-    const int rr = e / D, dd = e % D;
+    const int rr = e >> ld, dd = e & (D - 1);
     tile[off(row0 + rr, dd)] = encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc);
   }
   if (lane == 0) *sp = sc;

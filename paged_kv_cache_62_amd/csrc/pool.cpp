@@ -384,11 +384,12 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const voi
 }
 
 static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len) {
-  // Smallest power-of-two multiple of 16 tokens, between 128 and 512, that
-  // still gives about four workgroups per compute unit (256 CUs).
+  // 512 tokens (32 units: 8 per wavefront, enough to amortise a workgroup's
+  // start-up and merge), halved down to 128 while the launch would have
+  // fewer than two workgroups per compute unit (256 CUs).
   const int64_t pairs = (int64_t)num_seqs * pool->cfg.num_kv_heads;
   int32_t T = 512;
-  while (T > 128 && pairs * ((max_context_len + T - 1) / T) < 1024) T /= 2;
+  while (T > 128 && pairs * ((max_context_len + T - 1) / T) < 512) T /= 2;
   if (T < pool->cfg.block_size) T = pool->cfg.block_size;
   return T;
 }
