@@ -29,6 +29,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 
+# rocprofv3 FETCH_SIZE + WRITE_SIZE summaries (scaled by a plain-copy reference)
+# per workload; used only while the kernel source still has the hash they record.
+TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md"}
+
+
+def measured_traffic(config):
+    """HBM bytes per decode launch from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    import hashlib
+    import re
+    path = TRAFFIC_PROFILES.get(config)
+    if path is None or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    text = open(os.path.join(ROOT, path), encoding="utf-8").read()
+    t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"kernels_hip_sha256: ([0-9a-f]{64})", text)
+    src = os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip")
+    if not t or not h or hashlib.sha256(open(src, "rb").read()).hexdigest() != h.group(1):
+        return None
+    return int(t.group(1))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -41,6 +62,8 @@ def parse():
                     help="merge partitions in a second launch instead of the last workgroup")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer 3 times (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     return ap.parse_args()
@@ -280,6 +303,17 @@ def main():
     from paged_kv_cache_62_amd import pkv
     pkv.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        # A plain device copy of known size: reads and writes exactly
+        # calibrate_copy MiB per launch, for scaling FETCH_SIZE / WRITE_SIZE.
+        n = args.calibrate_copy << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
     stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
     with torch.cuda.stream(stream):
         res = run(args, stream)
@@ -378,7 +412,7 @@ def run(args, stream):
                    "hip_graph": not args.no_graph,
                    "kv_read_GBps_whole_step": kv_gbs_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
                      "kernel": "decode_kernel (split-context decode incl. partition merge)",
                      "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
                      "timing": f"HIP events around {reps} replays of a graph of the {len(layers)} decode launches"},
