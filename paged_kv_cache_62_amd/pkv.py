@@ -274,7 +274,10 @@ class Pool:
             self.h = None
 
     def __del__(self):
-        self.close()
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: module globals may already be gone
+            pass
 
     # allocator
     def allocate(self, seq, n_tokens):

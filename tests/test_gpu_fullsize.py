@@ -1,0 +1,110 @@
+"""Parity at the benchmark's full sizes and launch configuration.
+
+For every bench workload: build it exactly as bench.py does (seeded fill
+through pkv_append_kv), run one step (host slot/table update, then per layer
+append + decode with the bench's partition size, merge mode and capacity
+max_context_len), and check
+  * the step's append bit for bit: the touched blocks read back before the
+    step, pushed through the oracle's quantizer / binary16 rounding with the
+    step's K/V, must equal the blocks read back after it;
+  * decode outputs of sampled sequences (all their query heads) against the
+    FP64 oracle over the GPU's read-back cache, in the first and last layer.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from paged_kv_cache_62_amd import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["qwen", "llama29", "llama128", "mix16", "mix32", "long_i8", "long_f16"]
+
+
+def _kv_code(w):
+    from paged_kv_cache_62_amd import pkv
+    return orc.I8 if w.kv_code == pkv.PKV_I8 else orc.F16
+
+
+def _expected_after_append(w, layer, before_codes, before_scales, blocks, slots, knew, vnew):
+    """Oracle: apply this step's tokens to the pre-step blocks."""
+    bs, kvd = w.bs, _kv_code(w)
+    exp_codes, exp_scales = before_codes.copy(), before_scales.copy()
+    bidx = {b: i for i, b in enumerate(blocks)}
+    for t, slot in enumerate(slots):  # one token per sequence: each is its own run
+        b, row = int(slot) // bs, int(slot) % bs
+        i = bidx[b]
+        for kv, x in ((0, knew), (1, vnew)):
+            for h in range(w.hkv):
+                if kvd == orc.I8:
+                    codes, sc = orc.quant_append(exp_codes[i, kv, h], float(exp_scales[i, kv, h]), row,
+                                                 x[t:t + 1, h, :])
+                    exp_codes[i, kv, h] = codes
+                    exp_scales[i, kv, h] = sc
+                else:
+                    exp_codes[i, kv, h, row] = orc.f32_to_f16_bits(x[t, h, :])
+    return exp_codes, exp_scales
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_full_size_step(gpu, cfg):
+    import torch
+    import bench
+    print(f"[fullsize] building {cfg}", flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        w = bench.Workload(cfg, steps_total=4)
+        torch.cuda.synchronize()
+        bs = w.bs
+        w.host_prep()  # this step's slots and tables, uploaded
+        slots = w.d_slots.cpu().numpy()
+        blocks = sorted({int(s) // bs for s in slots})
+        layers_checked = [0, w.L - 1]
+        before = {l: w.pool.read_blocks(l, blocks) for l in layers_checked}
+        w.device_step(list(w.decode_layers(0)))
+        torch.cuda.synchronize()
+        for l in layers_checked:
+            knew = synth.as_f32(w.knew[l].cpu())
+            vnew = synth.as_f32(w.vnew[l].cpu())
+            exp_c, exp_s = _expected_after_append(w, l, before[l][0], before[l][1], blocks, slots, knew, vnew)
+            got_c, got_s = w.pool.read_blocks(l, blocks)
+            for i, b in enumerate(blocks):
+                rows = max(int(s) % bs for s in slots if int(s) // bs == b) + 1
+                np.testing.assert_array_equal(got_c[i][:, :, :rows], exp_c[i][:, :, :rows],
+                                              err_msg=f"{cfg} layer {l} block {b} codes")
+                if _kv_code(w) == orc.I8:
+                    np.testing.assert_array_equal(got_s[i].view(np.uint32), exp_s[i].view(np.uint32),
+                                                  err_msg=f"{cfg} layer {l} block {b} scales")
+        print(f"[fullsize] {cfg}: append bit-exact on {len(blocks)} blocks x {len(layers_checked)} layers",
+              flush=True)
+
+        # decode parity on sampled sequences, same launch configuration as bench.py
+        rng = np.random.default_rng(7)
+        sample = sorted(rng.choice(w.B, size=min(3, w.B), replace=False).tolist())
+        table, lens = w.pool.block_table(w.seqs, w.max_blocks)
+        d_table = torch.from_numpy(table).cuda()
+        d_lens = torch.from_numpy(lens).cuda()
+        dlayers = [l for l in layers_checked if l in set(w.decode_layers(0)) | set(w.decode_layers(1))]
+        for l in dlayers:
+            out = torch.empty(w.B, w.hq, w.dim, dtype=torch.float32, device="cuda")
+            w.pool.decode(l, w.q[l], d_table, d_lens, w.max_ctx, w.scale, out=out, workspace=w.ws,
+                          partition_tokens=w.partition, flags=w.flags)
+            torch.cuda.synchronize()
+            sub_blocks = sorted({int(b) for s in sample for b in table[s, :(int(lens[s]) + bs - 1) // bs]})
+            shape = H.Shape(layers=w.L, hq=w.hq, hkv=w.hkv, dim=w.dim, bs=bs, nblocks=w.nblocks,
+                            kv_dtype=_kv_code(w))
+            kc, vc, ks, vs = H.gpu_layer_arrays(w.pool, l, sub_blocks, shape)
+            q = synth.as_f32(w.q[l].cpu())[sample]
+            ref = orc.decode_attention(_kv_code(w), kc, vc, ks, vs, q, table[sample], lens[sample], w.scale)
+            got = out.cpu().numpy()[sample]
+            max_abs, max_rel = H.attention_errors(got, ref)
+            print(f"[fullsize] {cfg} layer {l} seqs {sample}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
+                  flush=True)
+            H.assert_attention_close(got, ref)
+        w.pool.close()
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
