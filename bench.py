@@ -58,8 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
-    ap.add_argument("--separate-merge", action="store_true",
-                    help="merge partitions in a second launch instead of the last workgroup")
+    ap.add_argument("--merge", choices=["auto", "fused", "separate"], default="auto",
+                    help="where partitions are merged: automatic, last workgroup, or a second launch")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -329,8 +329,8 @@ def run(args, stream):
     import torch
     from paged_kv_cache_62_amd import pkv
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
-    w = Workload(args.config, args.warmup + args.steps, args.partition,
-                 flags=pkv.PKV_DECODE_SEPARATE_MERGE if args.separate_merge else 0)
+    merge_flags = {"auto": 0, "fused": pkv.PKV_DECODE_FUSED_MERGE, "separate": pkv.PKV_DECODE_SEPARATE_MERGE}
+    w = Workload(args.config, args.warmup + args.steps, args.partition, flags=merge_flags[args.merge])
     graphs = {}
     if not args.no_graph:
         # The device work of a step, captured once as a HIP graph per layer
@@ -392,6 +392,7 @@ def run(args, stream):
     bytes_launch = float(w.kv_read_bytes(lens_now))
     achieved = bytes_launch / avg_dur_s / 1e9
     kv_gbs_step = float(np.sum(step_bytes)) / (total_ms / 1e3) / 1e9
+    plan = w.pool.decode_plan(w.B, w.max_ctx, w.partition, w.flags)
     res = {
         "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
         "value": tokens / (total_ms / 1e3),
@@ -407,8 +408,9 @@ def run(args, stream):
         "data": "synthetic (seeded), cache filled through pkv_append_kv before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": w.B,
                    "layers_per_step": len(layers),
-                   "partition_tokens": w.partition or w.pool.auto_partition(w.B, w.hq, w.max_ctx),
-                   "merge": "separate launch" if args.separate_merge else "last workgroup",
+                   "partition_tokens": plan[0], "partitions": plan[1],
+                   "merge": "none (one partition)" if plan[1] == 1 else
+                            "last workgroup" if plan[2] else "separate launch",
                    "hip_graph": not args.no_graph,
                    "kv_read_GBps_whole_step": kv_gbs_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -174,9 +174,18 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
 int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len);
 
-/* flags for pkv_decode_attention */
-#define PKV_DECODE_SEPARATE_MERGE 1 /* merge partitions in a second launch instead of
-                                       in the last workgroup of each (seq, KV head) */
+/* flags for pkv_decode_attention (0: automatic merge placement) */
+#define PKV_DECODE_SEPARATE_MERGE 1 /* merge partitions in a second launch */
+#define PKV_DECODE_FUSED_MERGE 2    /* merge partitions in the last workgroup of
+                                       each (seq, KV head) to finish */
+
+/* The launch plan pkv_decode_attention follows for these sizes and flags:
+ * partition tokens, partitions per sequence, and 1 when partitions are
+ * merged in the last workgroup of each (sequence, KV head), 0 when in a
+ * second launch. Output pointers may be NULL. Host only, synchronous. */
+pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len,
+                           int32_t partition_tokens, int32_t flags, int32_t* partition_out,
+                           int32_t* partitions_out, int32_t* fused_merge_out);
 
 /* Single-token decode attention over one layer ("vLLM核心概念" §3.1):
  *   out[s][h][:] = sum_t softmax_t(softmax_scale * q[s][h] . K[s,t]) V[s,t]
@@ -193,7 +202,10 @@ int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_
  *     (sequence, KV head, partition) is one workgroup serving all query heads
  *     of the group; the partitions of a sequence are combined by a
  *     log-sum-exp merge, done by the last workgroup of each (sequence, KV
- *     head) to finish, or by a second launch with PKV_DECODE_SEPARATE_MERGE.
+ *     head) to finish (PKV_DECODE_FUSED_MERGE) or by a second launch
+ *     (PKV_DECODE_SEPARATE_MERGE). flags 0 picks the first when the whole
+ *     grid fits on the device at once, the second otherwise; both flags set
+ *     is an error.
  *   workspace: at least pkv_decode_workspace_bytes(...) bytes (device). It
  *     must be zero-filled before its first use; every call leaves its
  *     counters at zero again, so one workspace serves any number of calls on

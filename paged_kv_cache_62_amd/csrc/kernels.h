@@ -19,7 +19,9 @@ enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
 //     dim = 16*dt + dm sit at ((tg*16 + dm) * (d/16) + dt) * 4 + ti, so lane
 //     tg*16 + dm of a wavefront reads d/4 contiguous elements holding, for
 //     every 16-dim tile dt, the 4 tokens that make up its A operand of the
-//     PV product (16 dims x 16 tokens).
+//     PV product (16 dims x 16 tokens). INT8 V codes are stored biased by
+//     128 (code ^ 0x80), which the decode kernel turns into fp16 with byte
+//     permutes alone.
 __host__ __device__ inline int64_t k_tile_offset(int t, int dim, int d) {
   return (int64_t)t * d + dim;
 }

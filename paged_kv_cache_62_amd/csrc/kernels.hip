@@ -45,6 +45,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;             // wavefronts per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kUnit = 16;             // tokens per unit of work (one MFMA tile of tokens)
+constexpr int kRsrcWord3 = 0x00020000; // buffer descriptor word 3 for untyped dword loads (gfx9 family)
+constexpr int kSlack = 4;              // the running max may trail the true maximum by this much (log2)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -116,16 +118,25 @@ __device__ __forceinline__ int wave_max_int(int x) {
   return x;
 }
 
-// Four int8 codes -> four fp16 values, exactly: each biased byte (code + 128)
-// becomes the low mantissa byte of 1024.0 (0x6400), then 1152 is subtracted.
-__device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
+// A pointer the compiler can treat as wave-uniform (it is, by construction,
+// wherever this is used): buffer descriptors must live in scalar registers,
+// and a value it cannot prove uniform costs a loop over the lanes per load.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
+// INT8 V codes are stored biased (code + 128, i.e. code ^ 0x80). Four of them
+// -> four fp16 values 1152 + code, exactly: each byte becomes the low mantissa
+// byte of 1024.0 (0x6400). The 1152 * sum(P) this adds to P V is subtracted
+// once, after the last unit.
+constexpr float kVBias = 1152.0f;
+__device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
-  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
-  return f16x4{a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(f16x4, make_uint2(lo, hi));
 }
 
 // ---------------------------------------------------------------------------
@@ -136,8 +147,10 @@ __device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
 // 16*gq + 64*c) and NCH chunks of the V sub-tile (bytes l*16*NCH + 16*c).
 // Each wavefront runs an online softmax over the units dealt to it (units
 // u0+w, u0+w+4, ...): per-head running max m and sum l live in the lanes of
-// that head's column; the accumulators are rescaled only when some head's
-// maximum grows. The four wavefronts merge through LDS; a single-partition
+// that head's column. The running max is a reference that may trail the true
+// maximum by up to kSlack (log2 units): it is raised, and the accumulators
+// rescaled, only when some head's score exceeds it by more, so P stays below
+// 2^kSlack. The four wavefronts merge through LDS; a single-partition
 // sequence writes its output, otherwise the partition's (m, l, o/l) goes to
 // the workspace and the last workgroup of the (sequence, KV head) to finish
 // merges all partitions.
@@ -162,74 +175,95 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int s = blockIdx.z;
 
   const int T = a.partition_tokens;
-  // Lengths beyond what the table or the grid covers are clamped, so a bad
-  // length cannot send a load outside the cache or the workspace.
-  const int len = min(a.lens[s], min(a.max_blocks * a.lv.block_size, a.max_partitions * T));
   const int t0 = part * T;
-  if (t0 >= len) return;
-  const int t1 = min(len, t0 + T);
-  const int nparts = (len + T - 1) / T;
   const int u0 = t0 / kUnit;
-  const int u1 = (t1 + kUnit - 1) / kUnit;
-  const int hkv = a.lv.num_kv_heads;
-  const int bs = a.lv.block_size;
-  const int upb = bs / kUnit;
+  const int maxb = a.max_blocks;
+  const int hkv = __builtin_amdgcn_readfirstlane(a.lv.num_kv_heads);
+  const int bs = __builtin_amdgcn_readfirstlane(a.lv.block_size);
+  const int lupb = __builtin_ctz(bs / kUnit);  // log2 units per block (block sizes are powers of two)
   const int hq = a.num_q_heads;
-  const int32_t* table = a.tables + (size_t)s * a.max_blocks;
-  const size_t tile_bytes = (size_t)bs * RB;
+  const int32_t* table = a.tables + (size_t)s * maxb;
+  const uint64_t tile_bytes = (uint64_t)bs * RB;
   const char* kcodes = (const char*)a.lv.k_codes;
   const char* vcodes = (const char*)a.lv.v_codes;
-
-  // ---- this wavefront's units are u0 + wave + kWaves*i, i < nu. Lane i
-  // gathers unit i's block id and scales with vector loads (64 units at a
-  // time); the loop reads them back with readlane. Scalar loads would put
-  // their latency on the loop's path: they can only be awaited all at once.
   const int ufirst = u0 + wave;
-  const int nu = ufirst < u1 ? (u1 - ufirst + kWaves - 1) / kWaves : 0;
-  int ublk = 0;
-  float uks = 1.f, uvs = 1.f;
-  auto gather_blocks = [&](int base) {
-    const int i = base + lane;
-    if (i < nu) ublk = min(max(table[(ufirst + kWaves * i) / upb], 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
+
+  // ---- start-up: the sequence length, this wavefront's first 64 block-table
+  // entries and the query all go out before the first wait, none of their
+  // addresses depending on another load. Lane i of a wavefront handles its
+  // unit i (units u0 + wave + kWaves*i, i < nu). Table reads are clamped to
+  // the row, so a lane past the sequence's end reads a valid (unused) entry.
+  auto table_entry = [&](int base) {
+    return table[min((ufirst + kWaves * (base + lane)) >> lupb, maxb - 1)];
   };
-  auto gather_scales = [&](int base) {
-    if constexpr (I8) {
-      if (base + lane < nu) {
-        uks = a.lv.k_scales[(size_t)ublk * hkv + g];
-        uvs = a.lv.v_scales[(size_t)ublk * hkv + g];
-      }
-    }
-  };
-  // NB-deep ring of K/V buffers: unit i is requested NB units before use.
-  uint4 kb[NB][NCH], vb[NB][NCH];
-  auto issue = [&](int i, int base, uint4 (&kd)[NCH], uint4 (&vd)[NCH]) {
-    const int blk = __builtin_amdgcn_readlane(ublk, i - base);
-    const int uu = ufirst + kWaves * i;
-    const size_t sub = ((size_t)blk * hkv + g) * tile_bytes + (size_t)(uu % upb) * UB;
-    const char* kp = kcodes + sub + n16 * RB + 16 * gq;
-    const char* vp = vcodes + sub + lane * (16 * NCH);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kd[c] = *(const uint4*)(kp + 64 * c);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) vd[c] = *(const uint4*)(vp + 16 * c);
-  };
-  // Start-up order: block ids (the K/V loads depend on them), then the
-  // query, then scales and the first NB units. Vector loads complete in
-  // order, so each wait below covers only what was issued before it.
-  gather_blocks(0);
-  // the query's elements for this workgroup
+  const int raw_len = a.lens[s];
+  int tentry = table_entry(0);
   constexpr int QPT = (G * D + kThreads - 1) / kThreads;  // query elements per thread
   float qe[QPT];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int e = threadIdx.x + k * kThreads;
-    qe[k] = e < G * D ? load_elem<QT>(a.q, ((size_t)s * hq + g * G) * D + min(e, G * D - 1)) : 0.f;
+    const float v = load_elem<QT>(a.q, ((size_t)s * hq + g * G) * D + min(e, G * D - 1));
+    qe[k] = e < G * D ? v : 0.f;
   }
 
-  gather_scales(0);
+  // Lengths beyond what the table or the grid covers are clamped, so a bad
+  // length cannot send a load outside the cache or the workspace.
+  const int len = min(raw_len, min(maxb * bs, a.max_partitions * T));
+  const int t1 = min(len, t0 + T);  // t0 >= len (nothing to do): nu = 0 below
+  const int nparts = (len + T - 1) / T;
+  const int u1 = (t1 + kUnit - 1) / kUnit;
+  const int nu = ufirst < u1 ? (u1 - ufirst + kWaves - 1) / kWaves : 0;
+
+  // Lane i keeps unit i's block id, its byte offset in the K (and V) codes
+  // of the layer and (int8) its scales; the loop reads them with readlane.
+  // Scalar loads would put their latency on the loop's path: they can only
+  // be awaited all at once. Lanes past nu hold in-bounds values never used.
+  int ublk = 0;
+  uint32_t usub_lo = 0, usub_hi = 0;
+  float uks = 1.f, uvs = 1.f;
+  auto set_blocks = [&](int base, int entry) {
+    const int u = ufirst + kWaves * (base + lane);
+    ublk = min(max(entry, 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
+    const uint64_t sub = ((uint64_t)ublk * hkv + g) * tile_bytes + (uint64_t)(u & ((1 << lupb) - 1)) * UB;
+    usub_lo = (uint32_t)sub;
+    usub_hi = (uint32_t)(sub >> 32);
+  };
+  auto gather_scales = [&]() {
+    if constexpr (I8) {
+      uks = a.lv.k_scales[(size_t)ublk * hkv + g];
+      uvs = a.lv.v_scales[(size_t)ublk * hkv + g];
+    }
+  };
+  // NB-deep ring of K/V buffers: unit i is requested NB units before use.
+  // Every slot of the loop issues its loads, also past the last unit: there
+  // the buffer descriptor's size is 0, so the loads return zeros without
+  // touching memory. With the same number of loads on every path the
+  // compiler's wait counts stay exact; a skipped issue on any path would
+  // make each wait drain the whole ring.
+  uint4 kb[NB][NCH], vb[NB][NCH];
+  auto issue = [&](int i, int base, int n, uint4 (&kd)[NCH], uint4 (&vd)[NCH]) {
+    const bool live = i < n;
+    const int j = min(i - base, 63);
+    const uint64_t sub = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(usub_hi, j) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane(usub_lo, j);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kcodes + sub), (short)0, live ? UB : 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcodes + sub), (short)0, live ? UB : 0, kRsrcWord3);
+    const int ko = n16 * RB + 16 * gq;
+    const int vo = lane * (16 * NCH);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    if (b < nu) issue(b, 0, kb[b], vb[b]);
+    for (int c = 0; c < NCH; ++c)
+      kd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, ko + 64 * c, 0, 0));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      vd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, vo + 16 * c, 0, 0));
+  };
+  set_blocks(0, tentry);
+  gather_scales();
+#pragma unroll
+  for (int b = 0; b < NB; ++b) issue(b, 0, min(nu, 64), kb[b], vb[b]);
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -276,6 +310,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   }
   __syncthreads();
+  // A partition past the sequence's end leaves only here (its K/V requests
+  // had size 0). Any earlier exit would let the compiler move the start-up
+  // loads behind the branch, each then waited for before the next.
+  if (t0 >= len) return;
   int qexp;
   frexpf(__int_as_float(sm_hmax[min(hc, G - 1)]), &qexp);
   const float qconst = ldexpf(a.softmax_scale * kLog2e, (I8 ? qexp - 22 : qexp - 15));
@@ -290,12 +328,20 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   }
 
   const bool colv = n16 < G;  // this lane's column is a real head (hi / digit 0)
+  // Only the real head columns decide when the running max is raised; the
+  // other columns of the S^T tile carry partial digits or nothing and are
+  // never read. They may hold any value (even inf or NaN): an MFMA output
+  // column depends on its own B column only, and P enters the PV product
+  // with its hi part cleared in lanes n16 >= 8.
+  const uint64_t colmask = __ballot(colv);
   float m = -INFINITY, l = 0.f;
-  // P enters the PV product as p * vscale * 2^(14 - ev) with ev the largest
-  // binary exponent of any V scale seen so far (wave-uniform), which keeps
-  // the fp16 parts below 2^14 and their lo part clear of fp16 subnormals;
-  // the accumulators are rescaled exactly when ev grows and scaled back by
-  // 2^(ev - 14) at the end. An fp16 cache has no scale: ev stays 0.
+  float corr = 0.f;  // sum of the P fed to PV: what the int8 V code bias adds, over kVBias
+  // P enters the PV product as p * vscale * 2^(14 - kSlack - ev) with ev the
+  // largest binary exponent of any V scale seen so far (wave-uniform), which
+  // keeps the fp16 parts below 2^14 and their lo part clear of fp16
+  // subnormals; the accumulators are rescaled exactly when ev grows and
+  // scaled back by 2^(ev + kSlack - 14) at the end. An fp16 cache has no
+  // scale: ev stays 0.
   int ev = I8 ? -1000 : 0;
   f32x4 o[NDT];
 #pragma unroll
@@ -333,21 +379,20 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       }
     }
 
-    float cm = -INFINITY;
+    if (nvalid < kUnit) {  // the partition's last unit: rows past its end (wave-uniform branch)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = colv ? (4 * gq + i < nvalid ? sc[i] : -INFINITY) : 0.f;
-      cm = fmaxf(cm, sc[i]);
+      for (int i = 0; i < 4; ++i) sc[i] = 4 * gq + i < nvalid ? sc[i] : -INFINITY;
     }
-    cm = max_over_lane_groups(cm);  // unit maximum of this lane's column
-    const float mn = fmaxf(m, cm);
+    const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     int evn = ev;
     if constexpr (I8) {
       int ve;
       frexpf(vscale, &ve);  // vscale < 2^ve
       evn = max(ev, __builtin_amdgcn_readfirstlane(ve));  // uniform: one scale per unit
     }
-    if (__any(mn > m) || evn > ev) {  // a head's maximum or the V exponent grew (wave-uniform)
+    // m = -inf before the first unit: every finite score raises it
+    if ((__ballot(lm > m + kSlack) & colmask) != 0 || evn > ev) {  // wave-uniform
+      const float mn = fmaxf(m, max_over_lane_groups(lm));  // + the column's maximum
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
       // lo columns follow their head: lane n16 >= 8 takes lane n16 - 8's alpha.
@@ -358,19 +403,18 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
                        ldexpf(1.0f, ev - evn);  // exact power of two
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
+      if constexpr (I8) corr *= ao;
       m = mn;
       ev = evn;
     }
 
     float p[4];
-    float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = colv ? __builtin_amdgcn_exp2f(sc[i] - m) : 0.f;
-      lsum += p[i];
-    }
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m);  // < 2^kSlack in head columns
+    const float lsum = (p[0] + p[1]) + (p[2] + p[3]);
     l += lsum;
-    const float pscale = ldexpf(I8 ? vscale : 1.0f, 14 - ev);  // < 2^14
+    const float pscale = ldexpf(I8 ? vscale : 1.0f, 14 - kSlack - ev);  // p * pscale < 2^14
+    if constexpr (I8) corr = fmaf(lsum, pscale, corr);
     f16x4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -380,10 +424,12 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       pl[i] = (_Float16)(pv - (float)hi);
     }
     // B operand of PV: column n16 < 8 is the hi part of head n16, column
-    // 8 + h the lo part of head h (moved over from lane n16 - 8). hi is zero
-    // in lanes 8..15 (no head) and the shifted lo is zero in lanes 0..7
-    // (outside the row), so OR-ing the bits merges them with no lane select.
-    const uint2 hb = __builtin_bit_cast(uint2, ph);
+    // 8 + h the lo part of head h (moved over from lane n16 - 8). hi is
+    // cleared in lanes 8..15 and the shifted lo is zero in lanes 0..7
+    // (outside the row), so OR-ing the bits merges them.
+    uint2 hb = __builtin_bit_cast(uint2, ph);
+    hb.x = n16 < 8 ? hb.x : 0u;
+    hb.y = n16 < 8 ? hb.y : 0u;
     const uint2 lb = __builtin_bit_cast(uint2, pl);
     const f16x4 pb = __builtin_bit_cast(
         f16x4, make_uint2(hb.x | (uint32_t)dpp_i<kRowShr8>((int)lb.x), hb.y | (uint32_t)dpp_i<kRowShr8>((int)lb.y)));
@@ -397,7 +443,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     for (int dt = 0; dt < NDT; ++dt) {
       f16x4 av;
       if constexpr (I8) {
-        av = i8x4_to_f16x4(vw[dt]);
+        av = biased_i8x4_to_f16x4(vw[dt]);
       } else {
         av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
         if (nvalid < kUnit) {  // rows past the end may hold any bits (NaN included)
@@ -412,11 +458,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   for (int cb = 0; cb < nu; cb += 64) {
     const int cn = min(64, nu - cb);
     if (cb > 0) {  // next 64 units: their bookkeeping, then the ring
-      gather_blocks(cb);
-      gather_scales(cb);
+      set_blocks(cb, table_entry(cb));
+      gather_scales();
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (b < cn) issue(cb + b, cb, kb[b], vb[b]);
+      for (int b = 0; b < NB; ++b) issue(cb + b, cb, cb + cn, kb[b], vb[b]);
     }
     for (int i0 = 0; i0 < cn; i0 += NB) {
 #pragma unroll
@@ -426,19 +471,21 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
           const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
           const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
           process(kb[b], vb[b], ks, vs, (ufirst + kWaves * (cb + i)) * kUnit);
-          if (i + NB < cn) issue(cb + i + NB, cb, kb[b], vb[b]);
         }
+        issue(cb + i + NB, cb, cb + cn, kb[b], vb[b]);
       }
     }
   }
 
-  // hi + lo columns, back to unit scale; l summed over the four lane groups
-  const float oscale = ldexpf(1.0f, ev - 14);
+  // hi + lo columns less the code bias, back to unit scale; l (and the P sum)
+  // summed over the four lane groups
+  const float oscale = ldexpf(1.0f, ev + kSlack - 14);
+  l = sum_over_lane_groups(l);
+  const float bias = I8 ? kVBias * sum_over_lane_groups(corr) : 0.f;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i])) * oscale;
-  l = sum_over_lane_groups(l);
+    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i]) - bias) * oscale;
 
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
@@ -671,6 +718,7 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
   const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
 
   int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
+  const uint32_t bias4 = kv ? 0x80808080u : 0u;  // V codes are stored biased by 128 (code ^ 0x80)
   float* sp = (kv ? lv.v_scales : lv.k_scales) + (size_t)blk * hkv + h;
   auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
   const void* src = kv ? v : k;
@@ -691,6 +739,7 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
     valid_mask[k] = 0;
     if (c * 16 < old_bytes) {
       oc[k] = *(const uint4*)(tile + (size_t)c * 16);
+      oc[k].x ^= bias4; oc[k].y ^= bias4; oc[k].z ^= bias4; oc[k].w ^= bias4;  // stored -> signed codes
       const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
@@ -740,14 +789,14 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
               ws[b >> 2] = (ws[b >> 2] & ~(0xFFu << (8 * (b & 3)))) | (q << (8 * (b & 3)));
             }
           }
-          *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+          *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
         }
       }
     }
   }
   for (int e = lane; e < nr * D; e += 64) {
     const int rr = e >> ld, dd = e & (D - 1);
-    tile[off(row0 + rr, dd)] = encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc);
+    tile[off(row0 + rr, dd)] = (int8_t)(encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc) ^ (int8_t)bias4);
   }
   if (lane == 0) *sp = sc;
 }

@@ -383,15 +383,70 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const voi
   return ok();
 }
 
+// Compute units of the device the kernels are built for, and how many decode
+// workgroups fit on the device at once (three per compute unit).
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kResidentWorkgroups = 3 * kComputeUnits;
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len) {
-  // 512 tokens (32 units: 8 per wavefront, enough to amortise a workgroup's
-  // start-up and merge), halved down to 128 while the launch would have
-  // fewer than two workgroups per compute unit (256 CUs).
-  const int64_t pairs = (int64_t)num_seqs * pool->cfg.num_kv_heads;
-  int32_t T = 512;
-  while (T > 128 && pairs * ((max_context_len + T - 1) / T) < 512) T /= 2;
-  if (T < pool->cfg.block_size) T = pool->cfg.block_size;
+  const pkv_pool_config& c = pool->cfg;
+  const int64_t pairs = (int64_t)num_seqs * c.num_kv_heads;
+  // Many workgroups in flight already and short contexts: one partition per
+  // sequence, no merge.
+  if (pairs >= 4 * kResidentWorkgroups && max_context_len <= 2048) {
+    int32_t T = c.block_size;
+    while (T < max_context_len) T *= 2;
+    return T;
+  }
+  // About 256 KiB of K and V per workgroup amortises its start-up and its
+  // share of the merge: 1024 tokens of INT8 or 512 of FP16 at head_dim 128.
+  const int64_t token_bytes = 2LL * c.head_dim * (c.kv_dtype == PKV_I8 ? 1 : 2);
+  int32_t T = 128;
+  while (T < 2048 && (int64_t)T * 2 * token_bytes <= 262144) T *= 2;
+  // With several rounds of workgroups the longest one sets the tail: longer
+  // partitions than 512 tokens only for long contexts.
+  if (T > 512 && pairs * ceil_div(max_context_len, T) > kResidentWorkgroups &&
+      max_context_len < 8 * T)
+    T = 512;
+  // At least one workgroup per compute unit.
+  while (T > 128 && pairs * ceil_div(max_context_len, T) < kComputeUnits) T /= 2;
+  if (T < c.block_size) T = c.block_size;
   return T;
+}
+
+// Automatic merge: in the last workgroup of each (sequence, KV head) when the
+// whole grid is resident at once; otherwise workgroups waiting on the arrival
+// count would hold slots the next ones need, and a second launch is cheaper.
+static int32_t plan_fused_merge(const pkv_pool* pool, int32_t num_seqs, int32_t P, int32_t flags) {
+  if (flags & PKV_DECODE_FUSED_MERGE) return 1;
+  if (flags & PKV_DECODE_SEPARATE_MERGE) return 0;
+  return (int64_t)num_seqs * pool->cfg.num_kv_heads * P <= kResidentWorkgroups ? 1 : 0;
+}
+
+static bool valid_flags(int32_t flags) {
+  return !(flags & ~(PKV_DECODE_SEPARATE_MERGE | PKV_DECODE_FUSED_MERGE)) &&
+         !((flags & PKV_DECODE_SEPARATE_MERGE) && (flags & PKV_DECODE_FUSED_MERGE));
+}
+
+pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len,
+                           int32_t partition_tokens, int32_t flags, int32_t* partition_out,
+                           int32_t* partitions_out, int32_t* fused_merge_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (num_seqs < 1 || max_context_len < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d and max_context_len %d must be >= 1", num_seqs,
+                max_context_len);
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % pool->cfg.block_size != 0))
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a positive multiple of block_size %d",
+                partition_tokens, pool->cfg.block_size);
+  if (!valid_flags(flags)) return fail(PKV_ERR_INVALID_ARG, "invalid flags 0x%x", flags);
+  const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
+  const int32_t P = (max_context_len + T - 1) / T;
+  if (partition_out) *partition_out = T;
+  if (partitions_out) *partitions_out = P;
+  if (fused_merge_out) *fused_merge_out = plan_fused_merge(pool, num_seqs, P, flags);
+  return ok();
 }
 
 int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
@@ -416,7 +471,7 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
                                 int32_t partition_tokens, int32_t flags, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
-  if (flags & ~PKV_DECODE_SEPARATE_MERGE) return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!valid_flags(flags)) return fail(PKV_ERR_INVALID_ARG, "invalid flags 0x%x", flags);
   if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
   const pkv_pool_config& c = pool->cfg;
   if (layer < 0 || layer >= c.num_layers)
@@ -462,7 +517,7 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
   d.out = out;
   d.counters = (int32_t*)workspace;
   d.ws = need > 0 ? (float*)((char*)workspace + pkv::decode_counter_bytes(num_seqs, c.num_kv_heads)) : nullptr;
-  d.fused_merge = (flags & PKV_DECODE_SEPARATE_MERGE) ? 0 : 1;
+  d.fused_merge = plan_fused_merge(pool, num_seqs, P, flags);
   hipError_t e = pkv::launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -498,6 +553,8 @@ pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* b
             for (int32_t d = 0; d < c.head_dim; ++d)
               std::memcpy(dst + (hd * te + (size_t)t * c.head_dim + d) * esz,
                           raw.data() + (hd * te + pkv::v_tile_offset(t, d, c.head_dim)) * esz, esz);
+        if (c.kv_dtype == PKV_I8)  // int8 V codes are stored biased by 128
+          for (size_t b = 0; b < tile_bytes; ++b) dst[b] = (char)(dst[b] ^ 0x80);
       }
       if (scales_out && pool->scales) {
         const float* ssrc = (kv ? lv.v_scales : lv.k_scales) + (size_t)blocks[i] * c.num_kv_heads;

@@ -32,6 +32,7 @@ STATUS_NAMES = {
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
 PKV_DECODE_SEPARATE_MERGE = 1
+PKV_DECODE_FUSED_MERGE = 2
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p
@@ -66,6 +67,7 @@ SIGNATURES = {
     "pkv_append_kv": (C.c_int, [_vp, _i32, _vp, _vp, C.c_int, _vp, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
     "pkv_decode_auto_partition": (_i32, [_vp, _i32, _i32, _i32]),
+    "pkv_decode_plan": (C.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_decode_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
                                        _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
@@ -207,6 +209,14 @@ def pkv_decode_auto_partition(h, num_seqs, num_q_heads, max_context_len) -> int:
     return int(lib().pkv_decode_auto_partition(h, num_seqs, num_q_heads, max_context_len))
 
 
+def pkv_decode_plan(h, num_seqs, max_context_len, partition_tokens=0, flags=0):
+    """(partition tokens, partitions per sequence, fused merge 0/1) of a decode call."""
+    T, P, fused = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib().pkv_decode_plan(h, num_seqs, max_context_len, partition_tokens, flags, C.byref(T),
+                                 C.byref(P), C.byref(fused)))
+    return T.value, P.value, fused.value
+
+
 def pkv_decode_attention(h, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
                          out, workspace=None, partition_tokens=0, stream=None, flags=0) -> None:
     """q: [B][Hq][d] device tensor; block_tables [B][max_blocks] int32; context_lens [B] int32;
@@ -317,6 +327,9 @@ class Pool:
 
     def auto_partition(self, num_seqs, num_q_heads, max_context_len):
         return pkv_decode_auto_partition(self.h, num_seqs, num_q_heads, max_context_len)
+
+    def decode_plan(self, num_seqs, max_context_len, partition_tokens=0, flags=0):
+        return pkv_decode_plan(self.h, num_seqs, max_context_len, partition_tokens, flags)
 
     def decode(self, layer, q, block_tables, context_lens, max_context_len, softmax_scale,
                out=None, workspace=None, partition_tokens=0, stream=None, flags=0):

@@ -16,10 +16,11 @@ def _report(tag, res):
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("T", [16, 64, 512, 0])
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_tiny_config(gpu, kv, T, flags):
     """Lengths 1, 15, 16, 600; 4q/2kv; d64; bs16; 64 blocks, seeded free order;
-    partitions merged in the last workgroup (flags 0) or a second launch (1)."""
+    partitions merged automatically (flags 0), in a second launch (1) or in the
+    last workgroup (2)."""
     res = H.run_decode_case(H.tiny_case(kv), partition_tokens=T, flags=flags)
     _report(f"tiny kv={kv} T={T} flags={flags}", res)
     H.assert_attention_close(res["gpu"], res["ref"])
