@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
     ap.add_argument("--merge", choices=["auto", "fused", "separate"], default="auto",
                     help="where partitions are merged: automatic, last workgroup, or a second launch")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append and decode as two launches per layer instead of one pkv_decode_step")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -112,7 +114,7 @@ def mix_suffix_lengths(seed, n):
 
 
 class Workload:
-    def __init__(self, name, steps_total, partition=0, flags=0):
+    def __init__(self, name, steps_total, partition=0, flags=0, fused=True):
         import torch
         from paged_kv_cache_62_amd import pkv, synth
         self.torch, self.pkv = torch, pkv
@@ -124,6 +126,7 @@ class Workload:
         self.rotate = c.get("rotate", False)
         self.partition = partition or c.get("partition", 0)
         self.flags = flags
+        self.fused = fused  # one pkv_decode_step launch per decoded layer instead of append + decode
         self.scale = 1.0 / math.sqrt(self.dim)
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
         seed = c["seed"]
@@ -236,11 +239,19 @@ class Workload:
         return lens
 
     def device_step(self, layers=None, decode_only=False):
-        """Device side of a step: per layer, append the new tokens' K/V, then
-        decode. max_context_len is the capacity for the whole run, so the
-        launch shapes never change (the kernels read the true lengths)."""
+        """Device side of a step: per layer, the new tokens' K/V are appended
+        and the layer decoded, in one pkv_decode_step launch (fused) or as
+        pkv_append_kv + pkv_decode_attention. decode_only keeps just the
+        launches that decode (the fused ones include their append).
+        max_context_len is the capacity for the whole run, so the launch
+        shapes never change (the kernels read the true lengths)."""
         dec = set(range(self.L) if layers is None else layers)
         for layer in range(self.L):  # every layer receives the new token
+            if layer in dec and self.fused:
+                self.pool.decode_step(layer, self.q[layer], self.knew[layer], self.vnew[layer], self.d_table,
+                                      self.d_lens, self.max_ctx, self.scale, out=self.out, workspace=self.ws,
+                                      partition_tokens=self.partition, flags=self.flags)
+                continue
             if not decode_only:
                 self.pool.append_kv(layer, self.knew[layer], self.vnew[layer], self.d_slots)
             if layer in dec:
@@ -330,7 +341,8 @@ def run(args, stream):
     from paged_kv_cache_62_amd import pkv
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
     merge_flags = {"auto": 0, "fused": pkv.PKV_DECODE_FUSED_MERGE, "separate": pkv.PKV_DECODE_SEPARATE_MERGE}
-    w = Workload(args.config, args.warmup + args.steps, args.partition, flags=merge_flags[args.merge])
+    w = Workload(args.config, args.warmup + args.steps, args.partition, flags=merge_flags[args.merge],
+                 fused=not args.unfused)
     graphs = {}
     if not args.no_graph:
         # The device work of a step, captured once as a HIP graph per layer
@@ -373,7 +385,9 @@ def run(args, stream):
 
     # The decode kernel alone: a graph of the step's decode launches on the
     # same stream, replayed back to back between two events; the cache is in
-    # its final state, so each launch reads the current lengths.
+    # its final state, so each launch reads the current lengths. A fused
+    # launch also re-stores the last token, which leaves the cache unchanged
+    # (the same rows at the same slots give the same codes and scales).
     layers = list(w.decode_layers(0))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -412,10 +426,12 @@ def run(args, stream):
                    "merge": "none (one partition)" if plan[1] == 1 else
                             "last workgroup" if plan[2] else "separate launch",
                    "hip_graph": not args.no_graph,
+                   "launches_per_layer": 1 if w.fused else 2,
                    "kv_read_GBps_whole_step": kv_gbs_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
-                     "kernel": "decode_kernel (split-context decode incl. partition merge)",
+                     "kernel": ("decode_kernel, decode step (new token's append + split-context decode + merge)"
+                                if w.fused else "decode_kernel (split-context decode incl. partition merge)"),
                      "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
                      "timing": f"HIP events around {reps} replays of a graph of the {len(layers)} decode launches"},
     }

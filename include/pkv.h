@@ -198,7 +198,8 @@ pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_c
  *     1 <= len <= max_blocks_per_seq*bs and len <= max_context_len (not
  *     checked on the device: the caller uploads what pkv_seq_block_table gave).
  *   out: [num_seqs][num_q_heads][head_dim] fp32.
- *   partition_tokens: context split (multiple of bs; 0 = automatic); each
+ *   partition_tokens: context split (multiple of bs, at most 4096; 0 =
+ *     automatic, which stays within 2048); each
  *     (sequence, KV head, partition) is one workgroup serving all query heads
  *     of the group; the partitions of a sequence are combined by a
  *     log-sum-exp merge, done by the last workgroup of each (sequence, KV
@@ -217,6 +218,28 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
                                 int32_t num_seqs, int32_t max_context_len, float softmax_scale,
                                 int32_t partition_tokens, int32_t flags, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step of one layer in a single launch: pkv_append_kv of each
+ * sequence's new token, then pkv_decode_attention, with the same results
+ * (cache codes and scales bit for bit, attention outputs as from
+ * pkv_decode_attention over the updated cache). The new token of sequence s
+ * is its last position, context_lens[s] - 1 (the context counts it, as in
+ * "vLLM核心概念" §3.1: the new token's query is scored against the cache that
+ * holds its own key); it is stored at block_tables[s][(len-1)/bs], row
+ * (len-1) % bs.
+ *   k_new, v_new: [num_seqs][num_kv_heads][head_dim] device rows in the same
+ *     dtype as q (F32, F16 or BF16).
+ *   Precondition: that block is not shared (pkv_seq_append_slots gave the
+ *     position, copying a shared block first). A table entry outside the
+ *     pool is not written.
+ * All other arguments, the workspace and the flags are as for
+ * pkv_decode_attention. */
+pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, pkv_dtype dtype, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                           float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as

@@ -60,7 +60,15 @@ struct DecodeLaunch {
   int32_t* counters;         // [num_seqs][Hkv] arrival counters (zero between calls)
   float* ws;                 // partials m, l [num_seqs][Hq][P], o [num_seqs][Hq][P][d]
   int32_t fused_merge;       // 1: the last workgroup of a (seq, KV head) merges
+  // Decode step: the new token of each sequence (position len-1), rows of
+  // [num_seqs][Hkv][d] in q's dtype, written into the cache before it is
+  // read. Null for plain decode.
+  const void* k_new;
+  const void* v_new;
 };
+
+// Longest decode partition (tokens) the kernels take.
+constexpr int32_t kMaxPartitionTokens = 4096;
 
 // True if the kernels cover this head_dim / group size.
 bool decode_supported(int head_dim, int group);

@@ -46,7 +46,13 @@ constexpr int kWaves = 4;             // wavefronts per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kUnit = 16;             // tokens per unit of work (one MFMA tile of tokens)
 constexpr int kRsrcWord3 = 0x00020000; // buffer descriptor word 3 for untyped dword loads (gfx9 family)
+// sched_barrier mask: ALU, VALU, SALU and MFMA instructions may be scheduled
+// across the barrier; memory instructions may not.
+constexpr int kSchedAluOnly = 0x000F;
 constexpr int kSlack = 4;              // the running max may trail the true maximum by this much (log2)
+// The longest partition is 4 wavefronts x 64 units of 16 tokens, so one lane
+// per unit holds a wavefront's bookkeeping.
+static_assert(kMaxPartitionTokens == kWaves * 64 * kUnit, "partition bound");
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -129,14 +135,255 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
 }
 
 // INT8 V codes are stored biased (code + 128, i.e. code ^ 0x80). Four of them
-// -> four fp16 values 1152 + code, exactly: each byte becomes the low mantissa
-// byte of 1024.0 (0x6400). The 1152 * sum(P) this adds to P V is subtracted
-// once, after the last unit.
-constexpr float kVBias = 1152.0f;
+// -> four fp16 codes, exactly: each byte becomes the low mantissa byte of
+// 1024.0 (0x6400), giving 1152 + code, and 1152 is subtracted. (Leaving the
+// 1152 in and removing 1152 * sum(P) after the product would save the two
+// subtractions, but the fp32 accumulators would then carry ~1152/|code|
+// times the signal and its rounding error.)
 __device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  return __builtin_bit_cast(f16x4, make_uint2(lo, hi));
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+// ---------------------------------------------------------------------------
+// H1 (binary16 cache): one thread per (token, head, K|V, 8-element chunk);
+// each value rounded to binary16, ties to even.
+// ---------------------------------------------------------------------------
+// Chunk ch (8 elements) of token i's row of head h, K (kv 0) or V (kv 1),
+// into row `row` of block blk.
+template <int IN>
+__device__ __forceinline__ void append_f16_chunk(const LayerView& lv, int kv, int h, int64_t blk, int row,
+                                                 const void* src, int64_t i, int ch) {
+  const int D = lv.head_dim;
+  const int hkv = lv.num_kv_heads;
+  const size_t sbase = ((size_t)i * hkv + h) * D + ch * 8;
+  uint16_t hv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    hv[e] = __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, sbase + e));
+  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
+                   ((size_t)blk * hkv + h) * lv.block_size * D;
+  if (kv == 0) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)hv[2 * e] | ((uint32_t)hv[2 * e + 1] << 16);
+    *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[v_tile_offset(row, ch * 8 + e, D)] = hv[e];
+  }
+}
+
+template <int IN>
+__global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, const void* k,
+                                                         const void* v, const int64_t* slots,
+                                                         int32_t n) {
+  const int hkv = lv.num_kv_heads;
+  const int chunks = lv.head_dim / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n * hkv * 2 * chunks) return;
+  const int ch = (int)(idx % chunks);
+  int64_t rest = idx / chunks;
+  const int h = (int)(rest % hkv);
+  rest /= hkv;
+  const int kv = (int)(rest & 1);
+  const int64_t i = rest >> 1;
+  const int64_t slot = slots[i];
+  const int64_t blk = slot / lv.block_size;
+  const int row = (int)(slot % lv.block_size);
+  if (slot < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
+  append_f16_chunk<IN>(lv, kv, h, blk, row, kv ? v : k, i, ch);
+}
+
+// ---------------------------------------------------------------------------
+// H1 (int8 cache): one wavefront per (run, head, K|V), where a run is the
+// maximal group of consecutive tokens that land in one block. Only the
+// wavefront of a run's first token works, so every (block, head, K|V) tile
+// has a single writer and no atomics are needed.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float scale_of(float max_abs) {
+  return max_abs > 1e-6f ? max_abs / 127.0f : 1.0f;
+}
+__device__ __forceinline__ int8_t encode(float x, float scale) {
+  const float y = x / scale;  // IEEE binary32 division (correctly rounded)
+  const float rr = fminf(fmaxf(rintf(y), -127.0f), 127.0f);  // rintf: ties to even
+  return (int8_t)(int)rr;
+}
+
+// One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
+// head h, K (kv 0) or V (kv 1), at rows row0 .. row0+nr-1 of block blk:
+// grow-only scale, old rows re-encoded when it grows (P5 section 3 plus the
+// rule for partly filled blocks). issue() sends every load without waiting
+// (the block's old codes, rows < row0, 16 bytes per load; its scale; up to
+// kPre new values per lane), so a wavefront can have the K and the V append
+// in flight together; finish() does the rest and returns the new scale.
+// Old rows of a K tile are its first row0*D bytes; those of a V tile lie in
+// its first ceil(row0/16) 16-token sub-tiles, where each byte's token is
+// decoded from its offset.
+template <int IN>
+struct I8Append {
+  static constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
+  static constexpr int kPre = 2;        // new values held per lane (one row of d <= 128)
+  const LayerView* lv;
+  int kv, h, row0, nr;
+  int64_t i;
+  const void* src;
+  int8_t* tile;
+  float* sp;
+  int old_bytes;
+  uint4 oc[kMaxChunks];
+  float s_old;
+  float pre[kPre];
+
+  __device__ __forceinline__ void issue(const LayerView& lv_, int kv_, int h_, int64_t blk, int row0_, int nr_,
+                                        const void* src_, int64_t i_) {
+    lv = &lv_; kv = kv_; h = h_; row0 = row0_; nr = nr_; src = src_; i = i_;
+    const int lane = threadIdx.x & 63;
+    const int hkv = lv_.num_kv_heads, D = lv_.head_dim, ld = __builtin_ctz(D);
+    tile = (int8_t*)(kv ? lv_.v_codes : lv_.k_codes) + ((size_t)blk * hkv + h) * lv_.block_size * D;
+    sp = (kv ? lv_.v_scales : lv_.k_scales) + (size_t)blk * hkv + h;
+    old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
+#pragma unroll
+    for (int k = 0; k < kMaxChunks; ++k) {
+      const int c = lane + 64 * k;
+      oc[k] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    s_old = row0 > 0 ? *sp : 1.f;
+    if (nr * D <= 64 * kPre) {
+#pragma unroll
+      for (int k = 0; k < kPre; ++k) {
+        const int e = lane + 64 * k;
+        pre[k] = e < nr * D ? load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))) : 0.f;
+      }
+    }
+  }
+
+  __device__ __forceinline__ float finish() {
+    const int lane = threadIdx.x & 63;
+    const int hkv = lv->num_kv_heads, D = lv->head_dim, ld = __builtin_ctz(D);
+    const uint32_t bias4 = kv ? 0x80808080u : 0u;  // V codes are stored biased by 128 (code ^ 0x80)
+    auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
+    // Bytes of chunk k that hold rows < row0, as a mask over each of its four
+    // words (the same for all four). A K chunk lies in one row. A V chunk
+    // lies in one lane's slice of a 16-token sub-tile (d/4 >= 16 bytes):
+    // tokens base + byte % 4 with base = 16*sub + 4*tg.
+    auto word_mask = [&](int k) -> uint32_t {
+      const int c = lane + 64 * k;
+      if (c * 16 >= old_bytes) return 0u;
+      if (!kv) return ~0u;
+      const int byte = c * 16;
+      const int sub = byte >> (ld + 4);                     // 16-token sub-tile
+      const int L = (byte & ((16 << ld) - 1)) >> (ld - 2);  // lane slice tg*16 + dm
+      const int n = min(max(row0 - (sub * 16 + (L >> 4) * 4), 0), 4);  // valid tokens of the word
+      return n == 4 ? ~0u : (1u << (8 * n)) - 1u;
+    };
+    auto new_value = [&](int e) {
+      return load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1)));
+    };
+    const bool held = nr * D <= 64 * kPre;
+    int qm = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxChunks; ++k) {
+      const uint32_t wm = word_mask(k);
+      const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = (ws[w] ^ bias4) & wm;  // signed codes; other rows read as 0
+#pragma unroll
+        for (int b = 0; b < 4; ++b) qm = max(qm, abs((int)(int8_t)(x >> (8 * b))));
+      }
+    }
+    float mx = 0.f;
+    if (held) {
+#pragma unroll
+      for (int k = 0; k < kPre; ++k) mx = fmaxf(mx, fabsf(pre[k]));
+    } else {
+      for (int e = lane; e < nr * D; e += 64) mx = fmaxf(mx, fabsf(new_value(e)));
+    }
+    mx = wave_max(mx);
+
+    float sc;
+    if (row0 == 0) {
+      sc = scale_of(mx);
+    } else {
+      qm = wave_max_int(qm);
+      const float m_old = (float)qm * s_old;
+      if (mx <= m_old) {
+        sc = s_old;
+      } else {
+        // the max grew: re-encode the old codes from their dequantised values,
+        // in the registers they were read into, and store whole chunks back
+        // (bytes of rows >= row0 are written back unchanged)
+        sc = scale_of(mx);
+#pragma unroll
+        for (int k = 0; k < kMaxChunks; ++k) {
+          const int c = lane + 64 * k;
+          if (c * 16 < old_bytes) {
+            const uint32_t wm = word_mask(k);
+            uint32_t ws[4] = {oc[k].x ^ bias4, oc[k].y ^ bias4, oc[k].z ^ bias4, oc[k].w ^ bias4};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                if (wm & (0xFFu << (8 * b))) {
+                  const int code = (int)(int8_t)(ws[w] >> (8 * b));
+                  const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, sc);
+                  ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | (q << (8 * b));
+                }
+              }
+            }
+            *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
+          }
+        }
+      }
+    }
+    if (held) {
+#pragma unroll
+      for (int k = 0; k < kPre; ++k) {
+        const int e = lane + 64 * k;
+        if (e < nr * D) tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(encode(pre[k], sc) ^ (int8_t)bias4);
+      }
+    } else {
+      for (int e = lane; e < nr * D; e += 64)
+        tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(encode(new_value(e), sc) ^ (int8_t)bias4);
+    }
+    if (lane == 0) *sp = sc;
+    return sc;  // the same in every lane
+  }
+};
+
+template <int IN>
+__global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, const void* k,
+                                                        const void* v, const int64_t* slots,
+                                                        int32_t n) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hkv = lv.num_kv_heads;
+  if (wid >= (int64_t)n * hkv * 2) return;
+  const int h = (int)(wid % hkv);
+  const int kv = (int)((wid / hkv) & 1);
+  const int64_t i = wid / hkv / 2;
+  const int bs = lv.block_size;
+  const int lbs = __builtin_ctz(bs);  // block sizes are powers of two
+
+  // The slots of tokens i .. i+63, one per lane, and of token i-1: the run
+  // starting at i is the leading lanes whose slot lies in the same block.
+  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
+  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
+  const int64_t blk = slot0 >> lbs;
+  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
+  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
+  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
+  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
+  const int row0 = (int)(slot0 & (bs - 1));
+  const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
+  I8Append<IN> ap;
+  ap.issue(lv, kv, h, blk, row0, nr, kv ? v : k, i);
+  (void)ap.finish();
 }
 
 // ---------------------------------------------------------------------------
@@ -155,7 +402,7 @@ __device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
 // the workspace and the last workgroup of the (sequence, KV head) to finish
 // merges all partitions.
 // ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT>
+template <bool I8, int D, int G, int QT, bool APPEND>
 __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int RB = D * ESZ;       // bytes per K row
@@ -186,16 +433,18 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const uint64_t tile_bytes = (uint64_t)bs * RB;
   const char* kcodes = (const char*)a.lv.k_codes;
   const char* vcodes = (const char*)a.lv.v_codes;
-  const int ufirst = u0 + wave;
+  const int upb = 1 << lupb;
+  // Wavefront w takes whole blocks: the partition's blocks w, w+4, w+8, ...
+  // (partitions start on a block). Its unit i is unit i % upb of its block
+  // i / upb, so every unit of a block is read by one wavefront.
+  auto unit_of = [&](int i) { return u0 + ((((i >> lupb) * kWaves + wave) << lupb) | (i & (upb - 1))); };
 
-  // ---- start-up: the sequence length, this wavefront's first 64 block-table
-  // entries and the query all go out before the first wait, none of their
+  // ---- start-up: the sequence length, this wavefront's block-table entries
+  // (at most 64) and the query all go out before the first wait, none of their
   // addresses depending on another load. Lane i of a wavefront handles its
-  // unit i (units u0 + wave + kWaves*i, i < nu). Table reads are clamped to
-  // the row, so a lane past the sequence's end reads a valid (unused) entry.
-  auto table_entry = [&](int base) {
-    return table[min((ufirst + kWaves * (base + lane)) >> lupb, maxb - 1)];
-  };
+  // unit i (i < nu). Table reads are clamped to the row, so a lane past the
+  // sequence's end reads a valid (unused) entry.
+  auto table_entry = [&](int base) { return table[min(unit_of(base + lane) >> lupb, maxb - 1)]; };
   const int raw_len = a.lens[s];
   int tentry = table_entry(0);
   constexpr int QPT = (G * D + kThreads - 1) / kThreads;  // query elements per thread
@@ -213,7 +462,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int t1 = min(len, t0 + T);  // t0 >= len (nothing to do): nu = 0 below
   const int nparts = (len + T - 1) / T;
   const int u1 = (t1 + kUnit - 1) / kUnit;
-  const int nu = ufirst < u1 ? (u1 - ufirst + kWaves - 1) / kWaves : 0;
+  const int nblk_full = max(u1 - u0, 0) >> lupb;  // whole blocks of the partition, and units left over
+  const int nrem = max(u1 - u0, 0) & (upb - 1);
+  const int nu = (nblk_full > wave ? ((nblk_full - wave + kWaves - 1) / kWaves) << lupb : 0) +
+                 (nrem > 0 && (nblk_full & (kWaves - 1)) == wave ? nrem : 0);
 
   // Lane i keeps unit i's block id, its byte offset in the K (and V) codes
   // of the layer and (int8) its scales; the loop reads them with readlane.
@@ -223,7 +475,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   uint32_t usub_lo = 0, usub_hi = 0;
   float uks = 1.f, uvs = 1.f;
   auto set_blocks = [&](int base, int entry) {
-    const int u = ufirst + kWaves * (base + lane);
+    const int u = unit_of(base + lane);
     ublk = min(max(entry, 0), a.lv.num_blocks - 1);  // in-bounds even for a bad entry
     const uint64_t sub = ((uint64_t)ublk * hkv + g) * tile_bytes + (uint64_t)(u & ((1 << lupb) - 1)) * UB;
     usub_lo = (uint32_t)sub;
@@ -242,9 +494,9 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // compiler's wait counts stay exact; a skipped issue on any path would
   // make each wait drain the whole ring.
   uint4 kb[NB][NCH], vb[NB][NCH];
-  auto issue = [&](int i, int base, int n, uint4 (&kd)[NCH], uint4 (&vd)[NCH]) {
+  auto issue = [&](int i, int n, uint4 (&kd)[NCH], uint4 (&vd)[NCH]) {
     const bool live = i < n;
-    const int j = min(i - base, 63);
+    const int j = min(i, 63);
     const uint64_t sub = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(usub_hi, j) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane(usub_lo, j);
     const __amdgpu_buffer_rsrc_t kr =
@@ -253,17 +505,40 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
         __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcodes + sub), (short)0, live ? UB : 0, kRsrcWord3);
     const int ko = n16 * RB + 16 * gq;
     const int vo = lane * (16 * NCH);
+    // The loads of a ring slot always leave in the same order (its K, then
+    // its V, then the next slot), in the start-up as in the loop: the wait
+    // counts the compiler derives on the paths into the loop then agree. The
+    // scheduling barriers let ALU and matrix work move across, not memory
+    // operations.
+    __builtin_amdgcn_sched_barrier(kSchedAluOnly);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       kd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, ko + 64 * c, 0, 0));
+    __builtin_amdgcn_sched_barrier(kSchedAluOnly);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       vd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, vo + 16 * c, 0, 0));
+    __builtin_amdgcn_sched_barrier(kSchedAluOnly);
   };
+  // Decode step: the sequence's last position is the token this step adds.
+  // The one wavefront that reads its block (the owner) stores the token's K
+  // and V rows first, exactly as the append kernels store a one-token run,
+  // and waits until the stores are complete; no other wavefront or
+  // workgroup reads that block. It does so after the query preparation
+  // below, so the other wavefronts never wait for it, and it issues its own
+  // first ring requests only then: its vector memory queue is then the same
+  // (ring requests last) on every path into the loop.
+  const int pos = len - 1;
+  const int nb_rel = (pos >> (lupb + 4)) - (u0 >> lupb);  // the new token's block within the partition
+  const bool owner = APPEND && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
+  const int i_new = (nb_rel >> 2) << lupb;  // owner: its unit index of that block's first unit
+
   set_blocks(0, tentry);
   gather_scales();
+  if (!owner) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) issue(b, 0, min(nu, 64), kb[b], vb[b]);
+    for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
+  }
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -314,6 +589,36 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // had size 0). Any earlier exit would let the compiler move the start-up
   // loads behind the branch, each then waited for before the next.
   if (t0 >= len) return;
+
+  if constexpr (APPEND) {
+    if (owner) {
+      const int entry = __builtin_amdgcn_readlane(tentry, i_new);  // i_new < nu <= 64
+      if (entry >= 0 && entry < a.lv.num_blocks) {  // a bad entry is not written
+        const int row = pos & (bs - 1);
+        if constexpr (I8) {
+          I8Append<QT> ak, av;
+          ak.issue(a.lv, 0, g, entry, row, 1, a.k_new, s);
+          av.issue(a.lv, 1, g, entry, row, 1, a.v_new, s);
+          const float sk = ak.finish();
+          const float sv = av.finish();
+          if (lane >= i_new && lane < i_new + upb) {  // this block's units: the new scales
+            uks = sk;
+            uvs = sv;
+          }
+        } else {
+          constexpr int CH = D / 8;  // 8-element chunks per row
+          if (lane < 2 * CH)
+            append_f16_chunk<QT>(a.lv, lane / CH, g, entry, row, lane < CH ? a.k_new : a.v_new, s, lane % CH);
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // the stores have completed
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
+    }
+  }
+
   int qexp;
   frexpf(__int_as_float(sm_hmax[min(hc, G - 1)]), &qexp);
   const float qconst = ldexpf(a.softmax_scale * kLog2e, (I8 ? qexp - 22 : qexp - 15));
@@ -335,7 +640,6 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // with its hi part cleared in lanes n16 >= 8.
   const uint64_t colmask = __ballot(colv);
   float m = -INFINITY, l = 0.f;
-  float corr = 0.f;  // sum of the P fed to PV: what the int8 V code bias adds, over kVBias
   // P enters the PV product as p * vscale * 2^(14 - kSlack - ev) with ev the
   // largest binary exponent of any V scale seen so far (wave-uniform), which
   // keeps the fp16 parts below 2^14 and their lo part clear of fp16
@@ -403,7 +707,6 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
                        ldexpf(1.0f, ev - evn);  // exact power of two
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
-      if constexpr (I8) corr *= ao;
       m = mn;
       ev = evn;
     }
@@ -414,7 +717,6 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     const float lsum = (p[0] + p[1]) + (p[2] + p[3]);
     l += lsum;
     const float pscale = ldexpf(I8 ? vscale : 1.0f, 14 - kSlack - ev);  // p * pscale < 2^14
-    if constexpr (I8) corr = fmaf(lsum, pscale, corr);
     f16x4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -455,37 +757,46 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   };
 
-  for (int cb = 0; cb < nu; cb += 64) {
-    const int cn = min(64, nu - cb);
-    if (cb > 0) {  // next 64 units: their bookkeeping, then the ring
-      set_blocks(cb, table_entry(cb));
-      gather_scales();
+  // The scales reach the loop through a register move the compiler cannot
+  // see into: it waits once for their loads here, and the loop's readlanes
+  // then carry no wait. (Otherwise, where the scales' registers were
+  // written along several paths, it kept them pending and drained the ring
+  // at every unit.)
+  if constexpr (I8) {
+    asm volatile("v_mov_b32 %0, %1" : "=v"(uks) : "v"(uks));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(uvs) : "v"(uvs));
+  }
+  // At most 64 units per wavefront (partitions of at most kMaxPartition
+  // tokens): lane i's bookkeeping covers every unit. A slot past the last
+  // unit still consumes its (zero-size) loads, so that every path through
+  // the loop leaves the same loads outstanding and the compiler's wait
+  // counts stay exact.
+  for (int i0 = 0; i0 < nu; i0 += NB) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) issue(cb + b, cb, cb + cn, kb[b], vb[b]);
-    }
-    for (int i0 = 0; i0 < cn; i0 += NB) {
+    for (int b = 0; b < NB; ++b) {
+      const int i = i0 + b;
+      if (i < nu) {
+        const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
+        const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
+        process(kb[b], vb[b], ks, vs, unit_of(i) * kUnit);
+      } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int i = i0 + b;
-        if (i < cn) {
-          const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
-          const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
-          process(kb[b], vb[b], ks, vs, (ufirst + kWaves * (cb + i)) * kUnit);
+        for (int c = 0; c < NCH; ++c) {
+          asm volatile("" ::"v"(kb[b][c].x), "v"(kb[b][c].y), "v"(kb[b][c].z), "v"(kb[b][c].w));
+          asm volatile("" ::"v"(vb[b][c].x), "v"(vb[b][c].y), "v"(vb[b][c].z), "v"(vb[b][c].w));
         }
-        issue(cb + i + NB, cb, cb + cn, kb[b], vb[b]);
       }
+      issue(i + NB, nu, kb[b], vb[b]);
     }
   }
 
-  // hi + lo columns less the code bias, back to unit scale; l (and the P sum)
-  // summed over the four lane groups
+  // hi + lo columns, back to unit scale; l summed over the four lane groups
   const float oscale = ldexpf(1.0f, ev + kSlack - 14);
   l = sum_over_lane_groups(l);
-  const float bias = I8 ? kVBias * sum_over_lane_groups(corr) : 0.f;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i]) - bias) * oscale;
+    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i])) * oscale;
 
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
@@ -589,15 +900,15 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 // Both variants fit in 168 registers with their K/V rings: three wavefronts
 // (three workgroups) per SIMD pair of registers budget, i.e. 768 resident
 // workgroups on 256 CUs.
-template <int D, int G, int QT>
+template <int D, int G, int QT, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_i8(const DecodeLaunch a) {
-  decode_body<true, D, G, QT>(a);
+  decode_body<true, D, G, QT, APPEND>(a);
 }
-template <int D, int G, int QT>
+template <int D, int G, int QT, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_f16(const DecodeLaunch a) {
-  decode_body<false, D, G, QT>(a);
+  decode_body<false, D, G, QT, APPEND>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,182 +943,22 @@ __global__ __launch_bounds__(D) void merge_kernel(const DecodeLaunch a) {
   a.out[((size_t)s * hq + h) * D + threadIdx.x] = O / L;
 }
 
-// ---------------------------------------------------------------------------
-// H1 (binary16 cache): one thread per (token, head, K|V, 8-element chunk);
-// each value rounded to binary16, ties to even.
-// ---------------------------------------------------------------------------
-template <int IN>
-__global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, const void* k,
-                                                         const void* v, const int64_t* slots,
-                                                         int32_t n) {
-  const int D = lv.head_dim;
-  const int hkv = lv.num_kv_heads;
-  const int chunks = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n * hkv * 2 * chunks) return;
-  const int ch = (int)(idx % chunks);
-  int64_t rest = idx / chunks;
-  const int h = (int)(rest % hkv);
-  rest /= hkv;
-  const int kv = (int)(rest & 1);
-  const int64_t i = rest >> 1;
-  const int64_t slot = slots[i];
-  const int64_t blk = slot / lv.block_size;
-  const int row = (int)(slot % lv.block_size);
-  if (slot < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  const void* src = kv ? v : k;
-  const size_t sbase = ((size_t)i * hkv + h) * D + ch * 8;
-  uint16_t hv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    hv[e] = __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, sbase + e));
-  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
-                   ((size_t)blk * hkv + h) * lv.block_size * D;
-  if (kv == 0) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)hv[2 * e] | ((uint32_t)hv[2 * e + 1] << 16);
-    *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[v_tile_offset(row, ch * 8 + e, D)] = hv[e];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// H1 (int8 cache): one wavefront per (run, head, K|V), where a run is the
-// maximal group of consecutive tokens that land in one block. Only the
-// wavefront of a run's first token works, so every (block, head, K|V) tile
-// has a single writer and no atomics are needed.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float scale_of(float max_abs) {
-  return max_abs > 1e-6f ? max_abs / 127.0f : 1.0f;
-}
-__device__ __forceinline__ int8_t encode(float x, float scale) {
-  const float y = x / scale;  // IEEE binary32 division (correctly rounded)
-  const float rr = fminf(fmaxf(rintf(y), -127.0f), 127.0f);  // rintf: ties to even
-  return (int8_t)(int)rr;
-}
-
-template <int IN>
-__global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, const void* k,
-                                                        const void* v, const int64_t* slots,
-                                                        int32_t n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hkv = lv.num_kv_heads;
-  if (wid >= (int64_t)n * hkv * 2) return;
-  const int h = (int)(wid % hkv);
-  const int kv = (int)((wid / hkv) & 1);
-  const int64_t i = wid / hkv / 2;
-  const int bs = lv.block_size;
-  const int lbs = __builtin_ctz(bs);  // block sizes are powers of two
-  const int D = lv.head_dim;
-  const int ld = __builtin_ctz(D);  // head_dim is 64 or 128: shifts instead of divisions
-
-  // The slots of tokens i .. i+63, one per lane, and of token i-1: the run
-  // starting at i is the leading lanes whose slot lies in the same block.
-  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
-  const int64_t blk = slot0 >> lbs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
-  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
-  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
-  const int row0 = (int)(slot0 & (bs - 1));
-  const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
-
-  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
-  const uint32_t bias4 = kv ? 0x80808080u : 0u;  // V codes are stored biased by 128 (code ^ 0x80)
-  float* sp = (kv ? lv.v_scales : lv.k_scales) + (size_t)blk * hkv + h;
-  auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
-  const void* src = kv ? v : k;
-
-  // Everything this wave reads goes out before the first wait: the block's
-  // old codes (rows < row0, 16 bytes per load), its scale, the new values.
-  // Old rows of a K tile are its first row0*D bytes; those of a V tile lie
-  // in its first ceil(row0/16) 16-token sub-tiles, where each byte's token
-  // is decoded from its offset.
-  const int old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
-  constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
-  uint4 oc[kMaxChunks];
-  uint32_t valid_mask[kMaxChunks];  // bit b: byte b of chunk belongs to a row < row0
-  int qm = 0;
-#pragma unroll
-  for (int k = 0; k < kMaxChunks; ++k) {
-    const int c = lane + 64 * k;
-    valid_mask[k] = 0;
-    if (c * 16 < old_bytes) {
-      oc[k] = *(const uint4*)(tile + (size_t)c * 16);
-      oc[k].x ^= bias4; oc[k].y ^= bias4; oc[k].z ^= bias4; oc[k].w ^= bias4;  // stored -> signed codes
-      const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        bool valid = true;
-        if (kv) {
-          const int byte = c * 16 + b;
-          const int sub = byte >> (ld + 4);                     // 16-token sub-tile
-          const int L = (byte & ((16 << ld) - 1)) >> (ld - 2);  // lane chunk tg*16 + dm
-          valid = sub * 16 + (L >> 4) * 4 + (byte & 3) < row0;
-        }
-        if (valid) {
-          valid_mask[k] |= 1u << b;
-          qm = max(qm, abs((int)(int8_t)(ws[b >> 2] >> (8 * (b & 3)))));
-        }
-      }
-    }
-  }
-  const float s_old = row0 > 0 ? *sp : 1.f;
-  float mx = 0.f;
-  for (int e = lane; e < nr * D; e += 64)
-    mx = fmaxf(mx, fabsf(load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1)))));
-  mx = wave_max(mx);
-
-  float sc;
-  if (row0 == 0) {
-    sc = scale_of(mx);
-  } else {
-    qm = wave_max_int(qm);
-    const float m_old = (float)qm * s_old;
-    if (mx <= m_old) {
-      sc = s_old;
-    } else {
-      // the max grew: re-encode the old codes from their dequantised values,
-      // in the registers they were read into, and store whole chunks back
-      // (bytes of rows >= row0 are written back unchanged)
-      sc = scale_of(mx);
-#pragma unroll
-      for (int k = 0; k < kMaxChunks; ++k) {
-        const int c = lane + 64 * k;
-        if (c * 16 < old_bytes) {
-          uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
-#pragma unroll
-          for (int b = 0; b < 16; ++b) {
-            if (valid_mask[k] & (1u << b)) {
-              const int code = (int)(int8_t)(ws[b >> 2] >> (8 * (b & 3)));
-              const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, sc);
-              ws[b >> 2] = (ws[b >> 2] & ~(0xFFu << (8 * (b & 3)))) | (q << (8 * (b & 3)));
-            }
-          }
-          *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
-        }
-      }
-    }
-  }
-  for (int e = lane; e < nr * D; e += 64) {
-    const int rr = e >> ld, dd = e & (D - 1);
-    tile[off(row0 + rr, dd)] = (int8_t)(encode(load_elem<IN>(src, ((size_t)(i + rr) * hkv + h) * D + dd), sc) ^ (int8_t)bias4);
-  }
-  if (lane == 0) *sp = sc;
-}
 
 template <bool I8, int D, int G, int QT>
 void launch_one(const DecodeLaunch& d, hipStream_t stream) {
   const dim3 grid(d.max_partitions, d.lv.num_kv_heads, d.num_seqs);
-  if constexpr (I8)
-    hipLaunchKernelGGL((decode_kernel_i8<D, G, QT>), grid, dim3(kThreads), 0, stream, d);
-  else
-    hipLaunchKernelGGL((decode_kernel_f16<D, G, QT>), grid, dim3(kThreads), 0, stream, d);
+  const bool step = d.k_new != nullptr;
+  if constexpr (I8) {
+    if (step)
+      hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true>), grid, dim3(kThreads), 0, stream, d);
+    else
+      hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, false>), grid, dim3(kThreads), 0, stream, d);
+  } else {
+    if (step)
+      hipLaunchKernelGGL((decode_kernel_f16<D, G, QT, true>), grid, dim3(kThreads), 0, stream, d);
+    else
+      hipLaunchKernelGGL((decode_kernel_f16<D, G, QT, false>), grid, dim3(kThreads), 0, stream, d);
+  }
 }
 
 template <bool I8, int D, int G>

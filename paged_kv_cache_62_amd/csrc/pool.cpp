@@ -437,9 +437,10 @@ pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_c
   if (num_seqs < 1 || max_context_len < 1)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs %d and max_context_len %d must be >= 1", num_seqs,
                 max_context_len);
-  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % pool->cfg.block_size != 0))
-    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a positive multiple of block_size %d",
-                partition_tokens, pool->cfg.block_size);
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % pool->cfg.block_size != 0) ||
+      partition_tokens > pkv::kMaxPartitionTokens)
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a multiple of block_size %d in [0, %d]",
+                partition_tokens, pool->cfg.block_size, pkv::kMaxPartitionTokens);
   if (!valid_flags(flags)) return fail(PKV_ERR_INVALID_ARG, "invalid flags 0x%x", flags);
   const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
   const int32_t P = (max_context_len + T - 1) / T;
@@ -464,12 +465,13 @@ size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
   return pkv::decode_workspace_bytes(num_seqs, num_q_heads, pool->cfg.num_kv_heads, pool->cfg.head_dim, P);
 }
 
-pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
-                                int32_t num_q_heads, const int32_t* block_tables,
-                                int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                int32_t num_seqs, int32_t max_context_len, float softmax_scale,
-                                int32_t partition_tokens, int32_t flags, float* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+// Shared by pkv_decode_attention and pkv_decode_step (k_new, v_new non-null).
+static pkv_status decode_launch(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                int32_t num_q_heads, const void* k_new, const void* v_new,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   if (!valid_flags(flags)) return fail(PKV_ERR_INVALID_ARG, "invalid flags 0x%x", flags);
   if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
@@ -490,9 +492,10 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
   if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.block_size)
     return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [1, max_blocks_per_seq*bs = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * c.block_size);
-  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % c.block_size != 0))
-    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a positive multiple of block_size %d",
-                partition_tokens, c.block_size);
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % c.block_size != 0) ||
+      partition_tokens > pkv::kMaxPartitionTokens)
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a multiple of block_size %d in [0, %d]",
+                partition_tokens, c.block_size, pkv::kMaxPartitionTokens);
   if (!q || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID_ARG, "NULL q, block_tables, context_lens or out");
   const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
@@ -518,9 +521,34 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
   d.counters = (int32_t*)workspace;
   d.ws = need > 0 ? (float*)((char*)workspace + pkv::decode_counter_bytes(num_seqs, c.num_kv_heads)) : nullptr;
   d.fused_merge = plan_fused_merge(pool, num_seqs, P, flags);
+  d.k_new = k_new;
+  d.v_new = v_new;
   hipError_t e = pkv::launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, float softmax_scale,
+                                int32_t partition_tokens, int32_t flags, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_launch(pool, layer, q, q_dtype, num_q_heads, nullptr, nullptr, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, softmax_scale,
+                       partition_tokens, flags, out, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, pkv_dtype dtype, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                           float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL k_new or v_new");
+  return decode_launch(pool, layer, q, dtype, num_q_heads, k_new, v_new, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, softmax_scale,
+                       partition_tokens, flags, out, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,

@@ -70,6 +70,8 @@ SIGNATURES = {
     "pkv_decode_plan": (C.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_decode_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
                                        _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_decode_step": (C.c_int, [_vp, _i32, _vp, _vp, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
+                                  _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
@@ -233,6 +235,24 @@ def pkv_decode_attention(h, layer, q, block_tables, context_lens, max_context_le
         _stream_ptr(stream)))
 
 
+def pkv_decode_step(h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                    softmax_scale, out, workspace=None, partition_tokens=0, stream=None, flags=0) -> None:
+    """q: [B][Hq][d]; k_new, v_new: [B][Hkv][d] in q's dtype (the token at position
+    context_lens[s]-1 of each sequence); other arguments as pkv_decode_attention."""
+    for t in (q, k_new, v_new, block_tables, context_lens, out):
+        assert t.is_contiguous()
+    assert k_new.dtype == q.dtype and v_new.dtype == q.dtype and out.dtype.itemsize == 4
+    B, hq, _ = q.shape
+    assert k_new.shape[0] == B and v_new.shape == k_new.shape
+    ws_ptr = _vp(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib().pkv_decode_step(
+        h, layer, _vp(q.data_ptr()), _vp(k_new.data_ptr()), _vp(v_new.data_ptr()), _torch_dtype_code(q), hq,
+        _vp(block_tables.data_ptr()), int(block_tables.shape[1]), _vp(context_lens.data_ptr()), B,
+        int(max_context_len), float(softmax_scale), int(partition_tokens), int(flags), _vp(out.data_ptr()),
+        ws_ptr, ws_bytes, _stream_ptr(stream)))
+
+
 def pkv_read_blocks(h, layer: int, blocks, num_kv_heads: int, block_size: int, head_dim: int,
                     kv_dtype: int):
     """Host copy of blocks in canonical order: codes [n][2][Hkv][bs][d], scales [n][2][Hkv]."""
@@ -342,6 +362,19 @@ class Pool:
             workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
         pkv_decode_attention(self.h, layer, q, block_tables, context_lens, max_context_len,
                              softmax_scale, out, workspace, partition_tokens, stream, flags)
+        return out
+
+    def decode_step(self, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                    softmax_scale, out=None, workspace=None, partition_tokens=0, stream=None, flags=0):
+        """Append each sequence's new token (rows k_new, v_new) and decode, in one launch."""
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nb = self.workspace_bytes(q.shape[0], q.shape[1], max_context_len, partition_tokens)
+            workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
+        pkv_decode_step(self.h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                        softmax_scale, out, workspace, partition_tokens, stream, flags)
         return out
 
     def read_blocks(self, layer, blocks):

@@ -262,3 +262,64 @@ def run_decode_case(case: Case, partition_tokens=0, layers=None, compare_cache=T
     res["max_abs"], res["max_rel"] = attention_errors(res["gpu"], res["ref"])
     res["pool"], res["oracle"], res["table"], res["lens"], res["q"] = pool, o, table, lens, q
     return res
+
+
+def run_step_case(case: Case, partition_tokens=0, flags=0):
+    """One decode step (one new token for every decode sequence), done two ways
+    on two pools built from the same script: pkv_append_kv then
+    pkv_decode_attention, and the single-launch pkv_decode_step. Both caches
+    must equal the oracle's bit for bit, the two outputs must be identical
+    bits, and the step's output must match the FP64 oracle over its cache."""
+    import torch
+    sh = case.shape
+    assert sh.in_dtype == sh.q_dtype, "the fused step takes K/V rows in q's dtype"
+    pools = [make_gpu_pool(case), make_gpu_pool(case)]
+    o = replay(case, pools[0])
+    replay(case, pools[1])
+    seqs = case.decode_seqs
+    ones = [1] * len(seqs)
+    st, slots = o.alloc.append(seqs, ones)
+    assert st == orc.OK
+    for src, dst, rows in o.alloc.take_cows():
+        o.cache.copy_block(int(src), int(dst), int(rows))
+    for p in pools:
+        np.testing.assert_array_equal(p.append_slots(seqs, ones), slots)
+    maxb = max((int(pools[0].length(s)) + sh.bs - 1) // sh.bs for s in seqs)
+    st, table, lens = o.alloc.table(seqs, maxb)
+    assert st == orc.OK
+    for p in pools:
+        g_table, g_lens = p.block_table(seqs, maxb)
+        np.testing.assert_array_equal(g_table, table)
+        np.testing.assert_array_equal(g_lens, lens)
+    dev = pools[0].arena.device
+    t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    t_slots = torch.from_numpy(np.ascontiguousarray(slots)).to(dev)
+    q = q_values(sh, case.seed, len(seqs)).to(dev)
+    sig = sigmas(sh, case.seed)
+    op = len(case.script)
+    outs = [[], []]
+    for layer in range(sh.layers):
+        k, v = kv_values(sh, case.seed, op, layer, len(seqs), sig)
+        assert o.cache.append(layer, synth.as_f32(k), synth.as_f32(v), slots) == orc.OK
+        k, v = k.to(dev), v.to(dev)
+        pools[0].append_kv(layer, k, v, t_slots)
+        outs[0].append(pools[0].decode(layer, q, t_table, t_lens, int(lens.max()), sh.scale,
+                                       partition_tokens=partition_tokens, flags=flags))
+        outs[1].append(pools[1].decode_step(layer, q, k, v, t_table, t_lens, int(lens.max()), sh.scale,
+                                            partition_tokens=partition_tokens, flags=flags))
+    torch.cuda.synchronize()
+    for p in pools:
+        compare_caches(case, o, p, seqs, maxb)
+    a = np.stack([x.cpu().numpy() for x in outs[0]])
+    b = np.stack([x.cpu().numpy() for x in outs[1]])
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32),
+                                  err_msg="decode step differs from append + decode")
+    rows = used_blocks_with_rows(o, seqs, maxb)
+    refs = []
+    for layer in range(sh.layers):
+        kc, vc, ks, vs = gpu_layer_arrays(pools[1], layer, rows.keys(), sh)
+        refs.append(orc.decode_attention(sh.kv_dtype, kc, vc, ks, vs, synth.as_f32(q.cpu()), table, lens,
+                                         sh.scale))
+    res = {"gpu": b, "ref": np.stack(refs), "pool": pools[1], "oracle": o, "table": table, "lens": lens}
+    res["max_abs"], res["max_rel"] = attention_errors(res["gpu"], res["ref"])
+    return res

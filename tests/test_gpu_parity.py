@@ -110,6 +110,46 @@ def test_partition_size_invariance(gpu, kv):
         np.testing.assert_allclose(o, outs[0], atol=1e-5, rtol=1e-5)
 
 
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("T", [16, 64, 0])
+@pytest.mark.parametrize("flags", [1, 2])
+def test_decode_step_tiny(gpu, kv, T, flags):
+    """pkv_decode_step on the tiny config (lengths 1, 15, 16, 600 -> 2, 16, 17,
+    601: the new token opens a block, fills one, continues one): identical to
+    append + decode, cache bit-exact with the oracle."""
+    res = H.run_step_case(H.tiny_case(kv), partition_tokens=T, flags=flags)
+    _report(f"step tiny kv={kv} T={T} flags={flags}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("shape_i", [0, 1, 2, 4])
+def test_decode_step_shapes(gpu, kv, shape_i):
+    hq, hkv, dim, bs, lens = SHAPES[shape_i]
+    nblocks = sum((n + bs) // bs + 1 for n in lens) + 5
+    sh = H.Shape(layers=2, hq=hq, hkv=hkv, dim=dim, bs=bs, nblocks=nblocks, kv_dtype=kv,
+                 in_dtype="bf16", q_dtype="bf16", free_order_seed=3, sigma_kv="per_head",
+                 outlier_p=0.01)
+    case = H.Case(sh, 62300 + shape_i, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=list(range(len(lens))))
+    res = H.run_step_case(case)
+    _report(f"step shape {SHAPES[shape_i][:4]} kv={kv}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+def test_decode_step_after_copy_on_write(gpu, kv):
+    """The step writes into blocks that the preceding append_slots copied from a
+    shared prefix (and into a freshly opened block after a freed sequence)."""
+    c = _growing_case(kv, 16, 62400)
+    c.script = c.script[:2] + [("fork", 0, k) for k in range(2, 6)]  # 200-token prefix shared 5x
+    c.decode_seqs = [0, 1, 2, 3, 4, 5]
+    res = H.run_step_case(c)
+    _report(f"step cow kv={kv}", res)
+    assert res["pool"].stats()["cow_copies"] == 5
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
 def test_f16_cache_special_values(gpu):
     """binary16 rounding of edge values (ties, subnormals, overflow)."""
     import torch
