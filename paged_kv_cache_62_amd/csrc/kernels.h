@@ -32,12 +32,17 @@ __host__ __device__ inline int64_t v_tile_offset(int t, int dim, int d) {
 }
 
 // One layer's view of the cache. Codes are [N][Hkv][tile] per K and V;
-// scales [N][Hkv] per K and V (int8 only).
+// scales [N][Hkv] per K and V (int8 only), and beside each scale the largest
+// |code| among the rows written so far (0 for a block of zero codes). The
+// append kernels keep it up to date; the decode step uses it to decide, with
+// no pass over the old codes, whether a new row grows the block's scale.
 struct LayerView {
   void* k_codes;
   void* v_codes;
   float* k_scales;
   float* v_scales;
+  int32_t* k_qmax;
+  int32_t* v_qmax;
   int32_t num_blocks, num_kv_heads, head_dim, block_size, kv_dtype;
 };
 

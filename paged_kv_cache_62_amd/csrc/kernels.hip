@@ -213,6 +213,21 @@ __device__ __forceinline__ int8_t encode(float x, float scale) {
   const float rr = fminf(fmaxf(rintf(y), -127.0f), 127.0f);  // rintf: ties to even
   return (int8_t)(int)rr;
 }
+// Re-encode the bytes of a word of codes selected by `mask` from scale s_old
+// to s_new (the bytes are stored XOR bias4).
+__device__ __forceinline__ uint32_t requant_word(uint32_t w, uint32_t mask, float s_old, float s_new,
+                                                 uint32_t bias4) {
+  uint32_t x = w ^ bias4;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (mask & (0xFFu << (8 * b))) {
+      const int code = (int)(int8_t)(x >> (8 * b));
+      const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, s_new);
+      x = (x & ~(0xFFu << (8 * b))) | (q << (8 * b));
+    }
+  }
+  return x ^ bias4;
+}
 
 // One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
 // head h, K (kv 0) or V (kv 1), at rows row0 .. row0+nr-1 of block blk:
@@ -234,6 +249,7 @@ struct I8Append {
   const void* src;
   int8_t* tile;
   float* sp;
+  int32_t* qp;
   int old_bytes;
   uint4 oc[kMaxChunks];
   float s_old;
@@ -246,6 +262,7 @@ struct I8Append {
     const int hkv = lv_.num_kv_heads, D = lv_.head_dim, ld = __builtin_ctz(D);
     tile = (int8_t*)(kv ? lv_.v_codes : lv_.k_codes) + ((size_t)blk * hkv + h) * lv_.block_size * D;
     sp = (kv ? lv_.v_scales : lv_.k_scales) + (size_t)blk * hkv + h;
+    qp = (kv ? lv_.v_qmax : lv_.k_qmax) + (size_t)blk * hkv + h;
     old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
 #pragma unroll
     for (int k = 0; k < kMaxChunks; ++k) {
@@ -307,6 +324,7 @@ struct I8Append {
     mx = wave_max(mx);
 
     float sc;
+    int qold = 0;  // largest |code| of the old rows once this append is done
     if (row0 == 0) {
       sc = scale_of(mx);
     } else {
@@ -314,6 +332,7 @@ struct I8Append {
       const float m_old = (float)qm * s_old;
       if (mx <= m_old) {
         sc = s_old;
+        qold = qm;
       } else {
         // the max grew: re-encode the old codes from their dequantised values,
         // in the registers they were read into, and store whole chunks back
@@ -331,27 +350,41 @@ struct I8Append {
               for (int b = 0; b < 4; ++b) {
                 if (wm & (0xFFu << (8 * b))) {
                   const int code = (int)(int8_t)(ws[w] >> (8 * b));
-                  const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, sc);
-                  ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | (q << (8 * b));
+                  const int8_t qn = encode((float)code * s_old, sc);
+                  qold = max(qold, abs((int)qn));
+                  ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | ((uint32_t)(uint8_t)qn << (8 * b));
                 }
               }
             }
             *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
           }
         }
+        qold = wave_max_int(qold);
       }
     }
+    int qnew = 0;  // largest |code| of the new rows
     if (held) {
 #pragma unroll
       for (int k = 0; k < kPre; ++k) {
         const int e = lane + 64 * k;
-        if (e < nr * D) tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(encode(pre[k], sc) ^ (int8_t)bias4);
+        if (e < nr * D) {
+          const int8_t q = encode(pre[k], sc);
+          qnew = max(qnew, abs((int)q));
+          tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(q ^ (int8_t)bias4);
+        }
       }
     } else {
-      for (int e = lane; e < nr * D; e += 64)
-        tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(encode(new_value(e), sc) ^ (int8_t)bias4);
+      for (int e = lane; e < nr * D; e += 64) {
+        const int8_t q = encode(new_value(e), sc);
+        qnew = max(qnew, abs((int)q));
+        tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(q ^ (int8_t)bias4);
+      }
     }
-    if (lane == 0) *sp = sc;
+    qnew = wave_max_int(qnew);
+    if (lane == 0) {
+      *sp = sc;
+      *qp = max(qold, qnew);
+    }
     return sc;  // the same in every lane
   }
 };
@@ -520,25 +553,50 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       vd[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, vo + 16 * c, 0, 0));
     __builtin_amdgcn_sched_barrier(kSchedAluOnly);
   };
-  // Decode step: the sequence's last position is the token this step adds.
-  // The one wavefront that reads its block (the owner) stores the token's K
-  // and V rows first, exactly as the append kernels store a one-token run,
-  // and waits until the stores are complete; no other wavefront or
-  // workgroup reads that block. It does so after the query preparation
-  // below, so the other wavefronts never wait for it, and it issues its own
-  // first ring requests only then: its vector memory queue is then the same
-  // (ring requests last) on every path into the loop.
+  // ---- decode step (APPEND): the sequence's last position, len - 1, is the
+  // token this step adds. The one wavefront whose units cover its block (the
+  // owner) appends it in registers: the block's units reach it through the
+  // ring like any others; when it comes to them it re-encodes their old rows
+  // if the block's scale grows, puts the new row in, stores the changed
+  // 16-byte chunks back and decodes them from its registers. Nothing is read
+  // back after those stores, so the owner streams from the start like every
+  // other wavefront. Whether the scale grows is decided before the loop from
+  // the new row, the block's scale and the largest |code| of its rows. No
+  // other wavefront or workgroup reads that block (it is not shared).
   const int pos = len - 1;
   const int nb_rel = (pos >> (lupb + 4)) - (u0 >> lupb);  // the new token's block within the partition
-  const bool owner = APPEND && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
   const int i_new = (nb_rel >> 2) << lupb;  // owner: its unit index of that block's first unit
+  const int row0 = pos & (bs - 1);          // the new token's row in its block
+  bool owner = APPEND && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
+  int a_entry = 0;
+  constexpr int NPL = D / 64;  // new-row elements per lane: dims lane + 64*k
+  float nk[NPL], nv[NPL];
+  int a_qk = 0, a_qv = 0;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) nk[k] = nv[k] = 0.f;
+  if constexpr (APPEND) {
+    if (owner) {
+      a_entry = __builtin_amdgcn_readlane(tentry, i_new);  // i_new < nu <= 64
+      owner = a_entry >= 0 && a_entry < a.lv.num_blocks;  // a bad entry is not written
+    }
+    if (owner) {
+      const size_t rowbase = ((size_t)s * hkv + g) * D;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        nk[k] = load_elem<QT>(a.k_new, rowbase + lane + 64 * k);
+        nv[k] = load_elem<QT>(a.v_new, rowbase + lane + 64 * k);
+      }
+      if constexpr (I8) {
+        a_qk = a.lv.k_qmax[(size_t)a_entry * hkv + g];
+        a_qv = a.lv.v_qmax[(size_t)a_entry * hkv + g];
+      }
+    }
+  }
 
   set_blocks(0, tentry);
   gather_scales();
-  if (!owner) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
-  }
+  for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -590,32 +648,59 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // loads behind the branch, each then waited for before the next.
   if (t0 >= len) return;
 
+  // The owner's decision, and the new row's codes in LDS for the lanes that
+  // hold that row in the ring: K codes in dim order, V codes as [dm][dt]
+  // (dim = 16*dt + dm), V biased like the stored ones. The largest |code| of
+  // the old rows after a re-encode is that of the largest old code: the
+  // encoding is odd and non-decreasing.
+  __shared__ __align__(16) unsigned char sm_new[2][APPEND ? D * ESZ : 16];
+  float sk_new = 1.f, sv_new = 1.f, sk_old = 1.f, sv_old = 1.f;
+  bool rq_k = false, rq_v = false;
+  int qmax_k = 0, qmax_v = 0;
   if constexpr (APPEND) {
     if (owner) {
-      const int entry = __builtin_amdgcn_readlane(tentry, i_new);  // i_new < nu <= 64
-      if (entry >= 0 && entry < a.lv.num_blocks) {  // a bad entry is not written
-        const int row = pos & (bs - 1);
-        if constexpr (I8) {
-          I8Append<QT> ak, av;
-          ak.issue(a.lv, 0, g, entry, row, 1, a.k_new, s);
-          av.issue(a.lv, 1, g, entry, row, 1, a.v_new, s);
-          const float sk = ak.finish();
-          const float sv = av.finish();
-          if (lane >= i_new && lane < i_new + upb) {  // this block's units: the new scales
-            uks = sk;
-            uvs = sv;
+      auto put = [&](int kv, int dim, uint32_t code) {
+        const int at = kv ? (dim & 15) * NDT + (dim >> 4) : dim;
+        if constexpr (I8) sm_new[kv][at] = (unsigned char)code;
+        else ((uint16_t*)sm_new[kv])[at] = (uint16_t)code;
+      };
+      if constexpr (I8) {
+        sk_old = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i_new));
+        sv_old = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i_new));
+        auto decide = [&](int kv, const float (&x)[NPL], float s_old, int q_old, float& s_new, bool& rq) {
+          float mx = 0.f;
+#pragma unroll
+          for (int k = 0; k < NPL; ++k) mx = fmaxf(mx, fabsf(x[k]));
+          mx = wave_max(mx);
+          int qo = 0;
+          if (row0 == 0) {
+            s_new = scale_of(mx);
+          } else if (mx <= (float)q_old * s_old) {
+            s_new = s_old;
+            qo = q_old;
+          } else {
+            s_new = scale_of(mx);
+            rq = true;
+            qo = encode((float)q_old * s_old, s_new);
           }
-        } else {
-          constexpr int CH = D / 8;  // 8-element chunks per row
-          if (lane < 2 * CH)
-            append_f16_chunk<QT>(a.lv, lane / CH, g, entry, row, lane < CH ? a.k_new : a.v_new, s, lane % CH);
+          int qn = 0;
+#pragma unroll
+          for (int k = 0; k < NPL; ++k) {
+            const int8_t q = encode(x[k], s_new);
+            qn = max(qn, abs((int)q));
+            put(kv, lane + 64 * k, (uint8_t)q ^ (kv ? 0x80u : 0u));
+          }
+          return max(qo, wave_max_int(qn));
+        };
+        qmax_k = decide(0, nk, sk_old, a_qk, sk_new, rq_k);
+        qmax_v = decide(1, nv, sv_old, a_qv, sv_new, rq_v);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+          put(0, lane + 64 * k, __builtin_bit_cast(uint16_t, (_Float16)nk[k]));
+          put(1, lane + 64 * k, __builtin_bit_cast(uint16_t, (_Float16)nv[k]));
         }
       }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0);  // the stores have completed
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
     }
   }
 
@@ -757,6 +842,74 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   };
 
+  // The owner's unit of the new token's block that starts at block row rb
+  // (its unit i): old rows re-encoded if the scale grew, the new row put in,
+  // and every 16-byte chunk that changed stored back.
+  auto patch = [&](uint4 (&kr)[NCH], uint4 (&vr)[NCH], int rb, int i) {
+    const uint64_t sub = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(usub_hi, i) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane(usub_lo, i);
+    char* kt = (char*)a.lv.k_codes + sub + n16 * RB + 16 * gq;
+    char* vt = (char*)a.lv.v_codes + sub + lane * (16 * NCH);
+    // K: this lane holds row rb + n16, bytes 16*gq + 64*c of it
+    const int krow = rb + n16;
+    bool kst = false;
+    if (krow == row0) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) kr[c] = *(const uint4*)&sm_new[0][16 * gq + 64 * c];
+      kst = true;
+    } else if (I8 && rq_k && krow < row0) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        kr[c] = make_uint4(requant_word(kr[c].x, ~0u, sk_old, sk_new, 0u), requant_word(kr[c].y, ~0u, sk_old, sk_new, 0u),
+                           requant_word(kr[c].z, ~0u, sk_old, sk_new, 0u), requant_word(kr[c].w, ~0u, sk_old, sk_new, 0u));
+      kst = true;
+    }
+    if (kst) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) *(uint4*)(kt + 64 * c) = kr[c];
+    }
+    // V: this lane holds rows rb + 4*gq + ti (ti < 4) of dims 16*dt + n16:
+    // element 4*dt + ti of its slice
+    const int ti0 = row0 - (rb + 4 * gq);  // the new row's ti, when in [0, 4)
+    uint32_t vw[4 * NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      vw[4 * c] = vr[c].x; vw[4 * c + 1] = vr[c].y; vw[4 * c + 2] = vr[c].z; vw[4 * c + 3] = vr[c].w;
+    }
+    bool vst = false;
+    if constexpr (I8) {
+      if (rq_v && ti0 > 0) {  // its rows below the new one are old
+        const uint32_t m = ti0 >= 4 ? ~0u : (1u << (8 * ti0)) - 1u;
+#pragma unroll
+        for (int w = 0; w < 4 * NCH; ++w) vw[w] = requant_word(vw[w], m, sv_old, sv_new, 0x80808080u);
+        vst = true;
+      }
+      if (ti0 >= 0 && ti0 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vw[dt] = (vw[dt] & ~(0xFFu << (8 * ti0))) | ((uint32_t)sm_new[1][n16 * NDT + dt] << (8 * ti0));
+        vst = true;
+      }
+    } else {
+      if (ti0 >= 0 && ti0 < 4) {
+        const int sh = 16 * (ti0 & 1);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int w = 2 * dt + (ti0 >> 1);
+          vw[w] = (vw[w] & ~(0xFFFFu << sh)) | ((uint32_t)((const uint16_t*)sm_new[1])[n16 * NDT + dt] << sh);
+        }
+        vst = true;
+      }
+    }
+    if (vst) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        vr[c] = make_uint4(vw[4 * c], vw[4 * c + 1], vw[4 * c + 2], vw[4 * c + 3]);
+        *(uint4*)(vt + 16 * c) = vr[c];
+      }
+    }
+  };
+
   // The scales reach the loop through a register move the compiler cannot
   // see into: it waits once for their loads here, and the loop's readlanes
   // then carry no wait. (Otherwise, where the scales' registers were
@@ -776,8 +929,15 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     for (int b = 0; b < NB; ++b) {
       const int i = i0 + b;
       if (i < nu) {
-        const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
-        const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
+        float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
+        float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
+        if constexpr (APPEND) {
+          if (owner && i >= i_new) {  // a unit of the new token's block (wave-uniform)
+            patch(kb[b], vb[b], (i - i_new) * kUnit, i);
+            ks = sk_new;
+            vs = sv_new;
+          }
+        }
         process(kb[b], vb[b], ks, vs, unit_of(i) * kUnit);
       } else {
 #pragma unroll
@@ -787,6 +947,16 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
         }
       }
       issue(i + NB, nu, kb[b], vb[b]);
+    }
+  }
+
+  if constexpr (APPEND && I8) {  // the new token's block: its scales and largest codes
+    if (owner && lane == 0) {
+      const size_t at = (size_t)a_entry * hkv + g;
+      a.lv.k_scales[at] = sk_new;
+      a.lv.v_scales[at] = sv_new;
+      a.lv.k_qmax[at] = qmax_k;
+      a.lv.v_qmax[at] = qmax_v;
     }
   }
 

@@ -9,7 +9,9 @@
 // block copies it first (copy-on-write, same section).
 //
 // Device memory (one arena): codes [L][2][N][Hkv][bs][d] followed, for an
-// INT8 cache, by scales [L][2][N][Hkv] fp32.
+// INT8 cache, by per-(block, head) metadata [L][2][2][N][Hkv] of 4-byte words:
+// for each layer and K|V, the fp32 scales, then the largest |code| of each
+// (block, head) among its written rows (int32).
 
 #include <hip/hip_runtime_api.h>
 
@@ -69,7 +71,7 @@ struct pkv_pool {
   size_t tile_elems = 0;    // bs * d
   size_t slice_bytes = 0;   // one (layer, K|V) slice of codes: N*Hkv*bs*d*elem
   size_t codes_bytes = 0;   // all layers
-  float* scales = nullptr;  // [L][2][N][Hkv] (int8)
+  float* scales = nullptr;  // metadata [L][2][scale | qmax][N][Hkv] (int8)
 
   int32_t pop_front() {
     const int32_t b = ring[head];
@@ -87,8 +89,10 @@ struct pkv_pool {
     lv.k_codes = arena + (size_t)(2 * layer) * slice_bytes;
     lv.v_codes = arena + (size_t)(2 * layer + 1) * slice_bytes;
     const size_t sc_slice = (size_t)cfg.num_blocks * cfg.num_kv_heads;
-    lv.k_scales = scales ? scales + (size_t)(2 * layer) * sc_slice : nullptr;
-    lv.v_scales = scales ? scales + (size_t)(2 * layer + 1) * sc_slice : nullptr;
+    lv.k_scales = scales ? scales + (size_t)(4 * layer) * sc_slice : nullptr;
+    lv.k_qmax = scales ? (int32_t*)(scales + (size_t)(4 * layer + 1) * sc_slice) : nullptr;
+    lv.v_scales = scales ? scales + (size_t)(4 * layer + 2) * sc_slice : nullptr;
+    lv.v_qmax = scales ? (int32_t*)(scales + (size_t)(4 * layer + 3) * sc_slice) : nullptr;
     lv.num_blocks = cfg.num_blocks;
     lv.num_kv_heads = cfg.num_kv_heads;
     lv.head_dim = cfg.head_dim;
@@ -118,7 +122,7 @@ size_t required_bytes(const pkv_pool_config* c) {
                        elem_bytes(c->kv_dtype);
   size_t total = round_up(slice * 2 * c->num_layers, 256);
   if (c->kv_dtype == PKV_I8)
-    total += round_up((size_t)c->num_layers * 2 * c->num_blocks * c->num_kv_heads * sizeof(float), 256);
+    total += round_up((size_t)c->num_layers * 4 * c->num_blocks * c->num_kv_heads * sizeof(float), 256);
   return total;
 }
 
@@ -263,7 +267,8 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
         pool->cow_total += 1;
         if (pool->arena) {
           // whole (block, head) tiles of every layer and K/V: a 2-D copy with
-          // one row per (layer, K|V) slice; then the scales the same way
+          // one row per (layer, K|V) slice; then the scales and largest codes
+          // the same way, one row per (layer, K|V, scale|qmax)
           const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems *
                                     elem_bytes(pool->cfg.kv_dtype);
           hipError_t e = hipMemcpy2DAsync(pool->arena + (size_t)fresh * tile_bytes, pool->slice_bytes,
@@ -275,7 +280,7 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
             const size_t sc_pitch = (size_t)pool->cfg.num_blocks * sc_row;
             e = hipMemcpy2DAsync((char*)pool->scales + (size_t)fresh * sc_row, sc_pitch,
                                  (char*)pool->scales + (size_t)old * sc_row, sc_pitch, sc_row,
-                                 2 * (size_t)pool->cfg.num_layers, hipMemcpyDeviceToDevice, st);
+                                 4 * (size_t)pool->cfg.num_layers, hipMemcpyDeviceToDevice, st);
           }
           if (e != hipSuccess) return hip_fail(e, "copy-on-write copy");
         }

@@ -264,12 +264,15 @@ def run_decode_case(case: Case, partition_tokens=0, layers=None, compare_cache=T
     return res
 
 
-def run_step_case(case: Case, partition_tokens=0, flags=0):
-    """One decode step (one new token for every decode sequence), done two ways
-    on two pools built from the same script: pkv_append_kv then
-    pkv_decode_attention, and the single-launch pkv_decode_step. Both caches
-    must equal the oracle's bit for bit, the two outputs must be identical
-    bits, and the step's output must match the FP64 oracle over its cache."""
+def run_step_case(case: Case, partition_tokens=0, flags=0, steps=1, alternate=False):
+    """Decode steps (one new token for every decode sequence per step), done
+    two ways on two pools built from the same script: pkv_append_kv then
+    pkv_decode_attention on one, the single-launch pkv_decode_step on the
+    other (with alternate=True, every second step of the latter also goes
+    through append + decode, so each path continues from blocks the other
+    wrote). Both caches must equal the oracle's bit for bit after the last
+    step, the two outputs must be identical bits at every step, and the last
+    step's output must match the FP64 oracle over the cache."""
     import torch
     sh = case.shape
     assert sh.in_dtype == sh.q_dtype, "the fused step takes K/V rows in q's dtype"
@@ -278,42 +281,48 @@ def run_step_case(case: Case, partition_tokens=0, flags=0):
     replay(case, pools[1])
     seqs = case.decode_seqs
     ones = [1] * len(seqs)
-    st, slots = o.alloc.append(seqs, ones)
-    assert st == orc.OK
-    for src, dst, rows in o.alloc.take_cows():
-        o.cache.copy_block(int(src), int(dst), int(rows))
-    for p in pools:
-        np.testing.assert_array_equal(p.append_slots(seqs, ones), slots)
-    maxb = max((int(pools[0].length(s)) + sh.bs - 1) // sh.bs for s in seqs)
-    st, table, lens = o.alloc.table(seqs, maxb)
-    assert st == orc.OK
-    for p in pools:
-        g_table, g_lens = p.block_table(seqs, maxb)
-        np.testing.assert_array_equal(g_table, table)
-        np.testing.assert_array_equal(g_lens, lens)
     dev = pools[0].arena.device
-    t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
-    t_slots = torch.from_numpy(np.ascontiguousarray(slots)).to(dev)
     q = q_values(sh, case.seed, len(seqs)).to(dev)
     sig = sigmas(sh, case.seed)
-    op = len(case.script)
-    outs = [[], []]
-    for layer in range(sh.layers):
-        k, v = kv_values(sh, case.seed, op, layer, len(seqs), sig)
-        assert o.cache.append(layer, synth.as_f32(k), synth.as_f32(v), slots) == orc.OK
-        k, v = k.to(dev), v.to(dev)
-        pools[0].append_kv(layer, k, v, t_slots)
-        outs[0].append(pools[0].decode(layer, q, t_table, t_lens, int(lens.max()), sh.scale,
-                                       partition_tokens=partition_tokens, flags=flags))
-        outs[1].append(pools[1].decode_step(layer, q, k, v, t_table, t_lens, int(lens.max()), sh.scale,
-                                            partition_tokens=partition_tokens, flags=flags))
-    torch.cuda.synchronize()
+    for step in range(steps):
+        st, slots = o.alloc.append(seqs, ones)
+        assert st == orc.OK
+        for src, dst, rows in o.alloc.take_cows():
+            o.cache.copy_block(int(src), int(dst), int(rows))
+        for p in pools:
+            np.testing.assert_array_equal(p.append_slots(seqs, ones), slots)
+        maxb = max((int(pools[0].length(s)) + sh.bs - 1) // sh.bs for s in seqs)
+        st, table, lens = o.alloc.table(seqs, maxb)
+        assert st == orc.OK
+        for p in pools:
+            g_table, g_lens = p.block_table(seqs, maxb)
+            np.testing.assert_array_equal(g_table, table)
+            np.testing.assert_array_equal(g_lens, lens)
+        t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+        t_slots = torch.from_numpy(np.ascontiguousarray(slots)).to(dev)
+        op = len(case.script) + step
+        fused = not (alternate and step % 2 == 1)
+        outs = [[], []]
+        for layer in range(sh.layers):
+            k, v = kv_values(sh, case.seed, op, layer, len(seqs), sig)
+            assert o.cache.append(layer, synth.as_f32(k), synth.as_f32(v), slots) == orc.OK
+            k, v = k.to(dev), v.to(dev)
+            for side in (0, 1):
+                p = pools[side]
+                if side == 1 and fused:
+                    outs[1].append(p.decode_step(layer, q, k, v, t_table, t_lens, int(lens.max()), sh.scale,
+                                                 partition_tokens=partition_tokens, flags=flags))
+                else:
+                    p.append_kv(layer, k, v, t_slots)
+                    outs[side].append(p.decode(layer, q, t_table, t_lens, int(lens.max()), sh.scale,
+                                               partition_tokens=partition_tokens, flags=flags))
+        torch.cuda.synchronize()
+        a = np.stack([x.cpu().numpy() for x in outs[0]])
+        b = np.stack([x.cpu().numpy() for x in outs[1]])
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32),
+                                      err_msg=f"decode step differs from append + decode at step {step}")
     for p in pools:
         compare_caches(case, o, p, seqs, maxb)
-    a = np.stack([x.cpu().numpy() for x in outs[0]])
-    b = np.stack([x.cpu().numpy() for x in outs[1]])
-    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32),
-                                  err_msg="decode step differs from append + decode")
     rows = used_blocks_with_rows(o, seqs, maxb)
     refs = []
     for layer in range(sh.layers):

@@ -71,8 +71,8 @@ def test_required_bytes():
     from paged_kv_cache_62_amd import pkv
     cfg = pkv.pkv_pool_config(28, 8, 128, 16, 2048, pkv.PKV_I8, None, None, 0, 0)
     codes = 28 * 2 * 2048 * 8 * 16 * 128
-    scales = 28 * 2 * 2048 * 8 * 4
-    assert pkv.pkv_pool_required_bytes(cfg) == codes + scales
+    scales = 28 * 2 * 2048 * 8 * 4  # fp32 scales, and as many int32 largest |codes|
+    assert pkv.pkv_pool_required_bytes(cfg) == codes + 2 * scales
     cfg.kv_dtype = pkv.PKV_F16
     assert pkv.pkv_pool_required_bytes(cfg) == 2 * codes
 

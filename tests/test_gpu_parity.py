@@ -150,6 +150,27 @@ def test_decode_step_after_copy_on_write(gpu, kv):
     H.assert_attention_close(res["gpu"], res["ref"])
 
 
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("alternate", [False, True])
+def test_decode_step_many_steps(gpu, kv, bs, alternate):
+    """24 consecutive decode steps: blocks fill, new ones open, INT8 scales
+    grow or stay; each step's decision rests on the block state (scale and
+    largest code) left by the steps before, written by the step itself or,
+    with alternate, every second time by the append kernel."""
+    steps = 24
+    lens = [1, bs - 3, 3 * bs - 20, 5 * bs + 7]
+    nblocks = sum((n + steps + bs - 1) // bs for n in lens) + 7
+    sh = H.Shape(layers=2, hq=8, hkv=2, dim=128, bs=bs, nblocks=nblocks, kv_dtype=kv,
+                 in_dtype="bf16", q_dtype="bf16", free_order_seed=5, sigma_kv="per_head",
+                 outlier_p=0.01)
+    case = H.Case(sh, 62500 + bs + alternate, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=[0, 1, 2, 3])
+    res = H.run_step_case(case, steps=steps, alternate=alternate)
+    _report(f"{steps} steps kv={kv} bs={bs} alternate={alternate}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
 def test_f16_cache_special_values(gpu):
     """binary16 rounding of edge values (ties, subnormals, overflow)."""
     import torch
