@@ -3,8 +3,11 @@
 One step = one decode step of every sequence through all layers: the host
 allocator reserves one new slot per sequence and rebuilds the block tables,
 they are uploaded, then per layer the new token's K/V are appended (quantized
-for an INT8 cache) and the split-context decode runs. Inputs are seeded
-synthetic tensors already resident in HBM; the cache is filled before timing.
+for an INT8 cache) and the split-context decode runs, in one launch per layer
+(pkv_decode_step; --unfused: pkv_append_kv + pkv_decode_attention). Inputs
+are seeded synthetic tensors already resident in HBM; the cache is filled
+before timing, to lengths at which the first timed step decodes at the
+configured context.
 
 Prints one JSON line: tokens/s (one new token per sequence per step), the
 decode kernel's KV-read bandwidth against the 8 TB/s HBM peak, and the FP64
@@ -55,7 +58,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The HIP runtime's first few dozen asynchronous uploads from pinned
+    # memory include a handful that block the host for ~6 ms (measured on
+    # MI355X with ROCm 7); 50 untimed steps leave them behind.
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
     ap.add_argument("--merge", choices=["auto", "fused", "separate"], default="auto",
@@ -114,7 +120,7 @@ def mix_suffix_lengths(seed, n):
 
 
 class Workload:
-    def __init__(self, name, steps_total, partition=0, flags=0, fused=True):
+    def __init__(self, name, steps_total, partition=0, flags=0, fused=True, warmup=0):
         import torch
         from paged_kv_cache_62_amd import pkv, synth
         self.torch, self.pkv = torch, pkv
@@ -135,8 +141,9 @@ class Workload:
             self.suffix = mix_suffix_lengths(seed, self.B)
             lens0 = 200 + self.suffix
         else:
-            lens0 = np.full(self.B, c["ctx"] - 1, dtype=np.int64)  # step 0 decodes at ctx
-        appends = steps_total if not self.rotate else (steps_total + 1) // 2 + 1
+            # the first timed step (after `warmup` steps) decodes at ctx
+            lens0 = np.full(self.B, c["ctx"] - 1 - warmup, dtype=np.int64)
+        appends = steps_total  # one new slot per sequence per step (shared by all layers)
         need = int(sum((int(n) + appends + self.bs - 1) // self.bs for n in lens0)) + 8
         nblocks = c["nblocks"] if c["nblocks"] is not None else need
         if need > nblocks:
@@ -190,17 +197,25 @@ class Workload:
         self.max_ctx = max_ctx = int(lens0.max()) + appends
         ws = self.pool.workspace_bytes(self.B, self.hq, max_ctx, self.partition)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.dev)
-        # pinned staging ring for the per-step uploads
+        # Per-step uploads: slots int64[B], lengths int32[B] and the block
+        # table int32[B][max_blocks], packed in one buffer so a step makes one
+        # host-to-device copy; a ring of pinned staging buffers lets the host
+        # prepare the next steps while earlier uploads are in flight.
+        self.up_bytes = 8 * self.B + 4 * self.B + 4 * self.B * self.max_blocks
+
+        def views(buf):
+            B, mb = self.B, self.max_blocks
+            return (buf[: 8 * B].view(torch.int64), buf[8 * B: 12 * B].view(torch.int32),
+                    buf[12 * B: 12 * B + 4 * B * mb].view(torch.int32).view(B, mb))
         self.ring = []
         for _ in range(4):
-            self.ring.append(dict(
-                slots=torch.empty(self.B, dtype=torch.int64, pin_memory=True),
-                table=torch.empty(self.B, self.max_blocks, dtype=torch.int32, pin_memory=True),
-                lens=torch.empty(self.B, dtype=torch.int32, pin_memory=True),
-                ev=torch.cuda.Event()))
-        self.d_slots = torch.empty(self.B, dtype=torch.int64, device=self.dev)
-        self.d_table = torch.empty(self.B, self.max_blocks, dtype=torch.int32, device=self.dev)
-        self.d_lens = torch.empty(self.B, dtype=torch.int32, device=self.dev)
+            buf = torch.empty(self.up_bytes, dtype=torch.uint8, pin_memory=True)
+            sl, ln, tb = views(buf)
+            self.ring.append(dict(buf=buf, slots=sl.numpy(), lens=ln.numpy(), table=tb.numpy(),
+                                  ev=torch.cuda.Event()))
+        self.d_up = torch.empty(self.up_bytes, dtype=torch.uint8, device=self.dev)
+        self.d_slots, self.d_lens, self.d_table = views(self.d_up)
+        self.ones = np.ones(self.B, dtype=np.int32)
         self.step_i = 0
 
     def _append_all(self, kv_fill, slots):
@@ -222,21 +237,17 @@ class Workload:
         return b
 
     def host_prep(self):
-        """Host side of a step: one new slot per sequence from the allocator,
-        the block tables rebuilt, both staged in pinned memory and uploaded."""
+        """Host side of a step: one new slot per sequence from the allocator
+        and the block tables rebuilt, written into a pinned staging buffer
+        and uploaded with one copy."""
         slot = self.ring[self.step_i % len(self.ring)]
-        slot["ev"].synchronize()  # the upload that last used this staging slot is done
-        slots = self.pool.append_slots(self.seqs, np.ones(self.B, dtype=np.int32))
-        table, lens = self.pool.block_table(self.seqs, self.max_blocks)
-        slot["slots"].numpy()[:] = slots
-        slot["table"].numpy()[:] = table
-        slot["lens"].numpy()[:] = lens
-        self.d_slots.copy_(slot["slots"], non_blocking=True)
-        self.d_table.copy_(slot["table"], non_blocking=True)
-        self.d_lens.copy_(slot["lens"], non_blocking=True)
+        slot["ev"].synchronize()  # the upload that last used this staging buffer is done
+        self.pool.append_slots(self.seqs, self.ones, out=slot["slots"])
+        self.pool.block_table(self.seqs, self.max_blocks, table=slot["table"], lens=slot["lens"])
+        self.d_up.copy_(slot["buf"], non_blocking=True)
         slot["ev"].record()
         self.step_i += 1
-        return lens
+        return slot["lens"].copy()
 
     def device_step(self, layers=None, decode_only=False):
         """Device side of a step: per layer, the new tokens' K/V are appended
@@ -342,7 +353,7 @@ def run(args, stream):
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
     merge_flags = {"auto": 0, "fused": pkv.PKV_DECODE_FUSED_MERGE, "separate": pkv.PKV_DECODE_SEPARATE_MERGE}
     w = Workload(args.config, args.warmup + args.steps, args.partition, flags=merge_flags[args.merge],
-                 fused=not args.unfused)
+                 fused=not args.unfused, warmup=args.warmup)
     graphs = {}
     if not args.no_graph:
         # The device work of a step, captured once as a HIP graph per layer

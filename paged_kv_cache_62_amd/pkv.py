@@ -146,14 +146,18 @@ def pkv_seq_allocate(h, seq: int, n_tokens: int, want_slots: bool = True) -> np.
     return slots[:n_tokens]
 
 
-def pkv_seq_append_slots(h, seqs, n_new, stream=None) -> np.ndarray:
+def pkv_seq_append_slots(h, seqs, n_new, stream=None, out=None) -> np.ndarray:
+    """Slots of the appended tokens; `out` (int64, contiguous, at least that
+    many entries) receives them in place when given."""
     seqs = np.ascontiguousarray(seqs, dtype=np.int64)
     n_new = np.ascontiguousarray(n_new, dtype=np.int32)
     total = int(n_new.sum()) if n_new.size else 0
-    slots = np.zeros(max(total, 1), dtype=np.int64)
+    if out is None:
+        out = np.zeros(max(total, 1), dtype=np.int64)
+    assert out.dtype == np.int64 and out.flags.c_contiguous and out.size >= total
     _check(lib().pkv_seq_append_slots(h, _np_ptr(seqs), len(seqs), _np_ptr(n_new),
-                                      _np_ptr(slots), stream))
-    return slots[:total]
+                                      _np_ptr(out), stream))
+    return out[:total]
 
 
 def pkv_seq_fork(h, parent: int, child: int) -> None:
@@ -164,10 +168,16 @@ def pkv_seq_free(h, seq: int) -> None:
     _check(lib().pkv_seq_free(h, seq))
 
 
-def pkv_seq_block_table(h, seqs, max_blocks: int):
+def pkv_seq_block_table(h, seqs, max_blocks: int, table=None, lens=None):
+    """Block tables [n][max_blocks] (pad -1) and lengths [n]; `table` and
+    `lens` (int32, contiguous) receive them in place when given."""
     seqs = np.ascontiguousarray(seqs, dtype=np.int64)
-    table = np.zeros((len(seqs), max_blocks), dtype=np.int32)
-    lens = np.zeros(len(seqs), dtype=np.int32)
+    if table is None:
+        table = np.zeros((len(seqs), max_blocks), dtype=np.int32)
+    if lens is None:
+        lens = np.zeros(len(seqs), dtype=np.int32)
+    assert table.dtype == np.int32 and table.flags.c_contiguous and table.size >= len(seqs) * max_blocks
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous and lens.size >= len(seqs)
     _check(lib().pkv_seq_block_table(h, _np_ptr(seqs), len(seqs), max_blocks, _np_ptr(table),
                                      _np_ptr(lens)))
     return table, lens
@@ -313,11 +323,11 @@ class Pool:
     def allocate(self, seq, n_tokens):
         return pkv_seq_allocate(self.h, seq, n_tokens)
 
-    def append_slots(self, seqs, n_new, stream=None):
+    def append_slots(self, seqs, n_new, stream=None, out=None):
         sp = None
         if self.arena is not None:
             sp = _stream_ptr(stream)
-        return pkv_seq_append_slots(self.h, seqs, n_new, sp)
+        return pkv_seq_append_slots(self.h, seqs, n_new, sp, out)
 
     def fork(self, parent, child):
         pkv_seq_fork(self.h, parent, child)
@@ -325,8 +335,8 @@ class Pool:
     def free(self, seq):
         pkv_seq_free(self.h, seq)
 
-    def block_table(self, seqs, max_blocks):
-        return pkv_seq_block_table(self.h, seqs, max_blocks)
+    def block_table(self, seqs, max_blocks, table=None, lens=None):
+        return pkv_seq_block_table(self.h, seqs, max_blocks, table, lens)
 
     def length(self, seq):
         return pkv_seq_length(self.h, seq)
