@@ -82,7 +82,8 @@ typedef struct {
 } pkv_stats;
 
 /* Device bytes a pool with this configuration needs (codes for all layers,
- * K and V, plus the fp32 scales for INT8), rounded up to 256 bytes. */
+ * K and V, plus for INT8 the fp32 scales and the int32 largest |code| of
+ * each (block, head)), rounded up to 256 bytes. */
 size_t pkv_pool_required_bytes(const pkv_pool_config* cfg);
 
 /* Create a pool. Validates the configuration (including that
@@ -247,6 +248,114 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
  * [n][2][Hkv] fp32. */
 pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
                            void* codes_out, float* scales_out);
+
+/* ------------------- continuous-batching step scheduler -------------------
+ * The per-step micro-decisions of "无 vLLM 环境下的 Paged-KV 与连续批处理调度"
+ * §3.1 (admit while page blocks remain, step the mixed batch, evict on EOS
+ * (event kind 2) or on the length limit (kind 3) and reclaim the blocks at
+ * once), in the order "vLLM核心概念" §3.3 gives (retire finished requests and
+ * free their blocks, keep the others, admit from the waiting queue while free
+ * blocks allow, decode every active request), over the pool's allocator
+ * ("连续批处理与KV缓存" §4.2: append_block reports "wait" when the queue is
+ * empty; §4.4: on running out of memory, pause new requests until blocks come
+ * back). Requests are admitted first come, first served. Host only: the
+ * scheduler plans a step; the caller writes the admitted prompts' K/V
+ * (pkv_append_kv at prefill_slots) and runs the decode (pkv_decode_step over
+ * the batch) on the stream given to pkv_sched_step, which also carries any
+ * copy-on-write copies. Request ids are pool sequence ids: the caller keeps
+ * its own sequences (shared prefixes) on other ids. Not thread-safe. */
+typedef struct pkv_sched pkv_sched;
+
+typedef struct {
+  int32_t max_batch;      /* most requests decoded per step (>= 1; "--max-num-seqs") */
+  int32_t max_model_len;  /* most tokens a request may hold, prompt included (>= 2);
+                             a request that reaches it ends with PKV_EV_MAX_LENGTH */
+  int32_t reserve_blocks; /* admission needs this many free blocks beyond those of the
+                             prompt (>= 0; 1 leaves room for the first decode token) */
+} pkv_sched_config;
+
+/* event kinds (2 and 3 as in "无 vLLM 环境下的 Paged-KV 与连续批处理调度" §3.1) */
+#define PKV_EV_ADMIT 1      /* admitted: its prompt is in this step's prefill list */
+#define PKV_EV_EOS 2        /* finished: the caller reported end of sequence */
+#define PKV_EV_MAX_LENGTH 3 /* finished: max_new_tokens generated or max_model_len reached */
+#define PKV_EV_PREEMPT 4    /* every running request was waiting for a block: the most
+                               recently admitted one gave its blocks back and returned to
+                               the front of the queue, to be written again in full */
+#define PKV_EV_WAIT 5       /* no free block for its next token: not decoded this step */
+
+typedef struct {
+  int64_t request;
+  int32_t kind;
+  int32_t pad_;
+} pkv_event;
+
+/* A step's plan. The arrays are host memory owned by the scheduler, valid
+ * until the next pkv_sched_step or pkv_sched_destroy. */
+typedef struct {
+  int32_t num_seqs;             /* requests decoded this step, in admission order */
+  int32_t max_blocks;           /* width of block_tables rows: ceil(max_model_len / bs) */
+  int32_t max_context_len;      /* max of context_lens (0 when num_seqs is 0) */
+  int32_t num_prefill;          /* requests admitted this step */
+  int32_t prefill_total;        /* sum of prefill_tokens */
+  int32_t num_events;
+  const int64_t* seqs;          /* [num_seqs] request ids */
+  const int64_t* slots;         /* [num_seqs] slot of each one's new token (position len - 1) */
+  const int32_t* block_tables;  /* [num_seqs][max_blocks], padded with -1 */
+  const int32_t* context_lens;  /* [num_seqs], counting the new token */
+  const int64_t* prefill_seqs;  /* [num_prefill] */
+  const int32_t* prefill_first; /* [num_prefill] first position to write (the shared
+                                   prefix length, 0 without one) */
+  const int32_t* prefill_tokens;/* [num_prefill] tokens to write from there */
+  const int64_t* prefill_slots; /* [prefill_total] their slots, request after request */
+  const pkv_event* events;      /* [num_events] in the order they happened */
+} pkv_step_plan;
+
+typedef struct {
+  int64_t waiting, running;     /* requests in the queue / admitted and not finished */
+  int64_t admitted, finished_eos, finished_max_length, preempted;  /* totals */
+  int64_t generated;            /* tokens decoded so far */
+  int64_t used_blocks, total_blocks;  /* the pool's, as in "12000 used / 15000 total" */
+  int32_t paused;               /* admissions paused: a decode token found no free block */
+  int32_t pad_;
+} pkv_sched_stats;
+
+pkv_status pkv_sched_create(pkv_pool* pool, const pkv_sched_config* cfg, pkv_sched** out);
+
+/* Destroy the scheduler; the blocks of its requests go back to the pool. */
+void pkv_sched_destroy(pkv_sched* sched);
+
+/* Queue a request: prompt_len >= 1 prompt tokens, then at most max_new_tokens
+ * >= 1 decoded ones. prefix_seq >= 0 names a live pool sequence of length
+ * p <= prompt_len whose tokens are the prompt's first p (shared blocks,
+ * forked at admission; the caller keeps it unchanged while requests may
+ * use it); -1 = none. PKV_ERR_SEQ_EXISTS if the id is queued, running or a
+ * pool sequence; PKV_ERR_INVALID_ARG if prompt_len >= max_model_len or if
+ * min(prompt_len + max_new_tokens, max_model_len) tokens need more blocks
+ * than the pool has (such a request could never finish). */
+pkv_status pkv_sched_submit(pkv_sched* sched, int64_t request, int32_t prompt_len,
+                            int32_t max_new_tokens, int64_t prefix_seq);
+
+/* Plan one step. eos[0..n_eos) are requests of the previous step's batch
+ * whose decoded token ended the sequence (the caller's sampling).
+ *  1. Retire, in admission order: a request in eos (PKV_EV_EOS), or one that
+ *     has decoded max_new_tokens tokens or holds max_model_len tokens
+ *     (PKV_EV_MAX_LENGTH), frees its blocks; freed blocks lift a pause.
+ *  2. Admit, unless paused, first come first served: while the batch has
+ *     room and the queue front's prompt needs at most free - reserve_blocks
+ *     new blocks, allocate it (or fork its prefix and reserve the rest) and
+ *     list it for prefill (PKV_EV_ADMIT). The first request that does not fit
+ *     stops admission.
+ *  3. Decode: in admission order, each running request takes one new token
+ *     position; one that needs a block the queue cannot give waits
+ *     (PKV_EV_WAIT) and pauses admissions. If every running request waits,
+ *     the most recently admitted one is preempted (PKV_EV_PREEMPT) and the
+ *     others try again.
+ * The requests that got a position form the batch; each counts one decoded
+ * token. Argument errors (an eos id not in the previous batch) change nothing. */
+pkv_status pkv_sched_step(pkv_sched* sched, const int64_t* eos, int32_t n_eos, pkv_step_plan* plan,
+                          void* stream);
+
+pkv_status pkv_sched_get_stats(const pkv_sched* sched, pkv_sched_stats* out);
 
 /* The KV-bytes formula 2*L*H*d*s*B*bytes ("无 vLLM 环境下的 Paged-KV" §2). */
 uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,

@@ -24,6 +24,7 @@
 #include <vector>
 
 #include "../../include/pkv.h"
+#include "host.h"
 #include "kernels.h"
 
 namespace {
@@ -133,6 +134,11 @@ pkv_status hip_fail(hipError_t e, const char* what) {
 int64_t nblocks_for(int64_t len, int64_t bs) { return (len + bs - 1) / bs; }
 
 }  // namespace
+
+namespace pkv {
+void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
+int32_t pool_block_size(const pkv_pool* pool) { return pool->cfg.block_size; }
+}  // namespace pkv
 
 extern "C" {
 

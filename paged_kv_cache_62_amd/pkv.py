@@ -52,6 +52,34 @@ class pkv_stats(C.Structure):
                 ("cow_copies", _i64), ("num_seqs", _i64), ("total_blocks", _i64)]
 
 
+PKV_EV_ADMIT, PKV_EV_EOS, PKV_EV_MAX_LENGTH, PKV_EV_PREEMPT, PKV_EV_WAIT = 1, 2, 3, 4, 5
+
+
+class pkv_sched_config(C.Structure):
+    _fields_ = [("max_batch", _i32), ("max_model_len", _i32), ("reserve_blocks", _i32)]
+
+
+class pkv_event(C.Structure):
+    _fields_ = [("request", _i64), ("kind", _i32), ("pad_", _i32)]
+
+
+class pkv_step_plan(C.Structure):
+    _fields_ = [
+        ("num_seqs", _i32), ("max_blocks", _i32), ("max_context_len", _i32), ("num_prefill", _i32),
+        ("prefill_total", _i32), ("num_events", _i32),
+        ("seqs", C.POINTER(_i64)), ("slots", C.POINTER(_i64)), ("block_tables", C.POINTER(_i32)),
+        ("context_lens", C.POINTER(_i32)), ("prefill_seqs", C.POINTER(_i64)),
+        ("prefill_first", C.POINTER(_i32)), ("prefill_tokens", C.POINTER(_i32)),
+        ("prefill_slots", C.POINTER(_i64)), ("events", C.POINTER(pkv_event)),
+    ]
+
+
+class pkv_sched_stats(C.Structure):
+    _fields_ = [("waiting", _i64), ("running", _i64), ("admitted", _i64), ("finished_eos", _i64),
+                ("finished_max_length", _i64), ("preempted", _i64), ("generated", _i64),
+                ("used_blocks", _i64), ("total_blocks", _i64), ("paused", _i32), ("pad_", _i32)]
+
+
 SIGNATURES = {
     "pkv_pool_required_bytes": (_sz, [_vp]),
     "pkv_pool_create": (C.c_int, [_vp, _vp]),
@@ -73,6 +101,11 @@ SIGNATURES = {
     "pkv_decode_step": (C.c_int, [_vp, _i32, _vp, _vp, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
                                   _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
+    "pkv_sched_create": (C.c_int, [_vp, _vp, _vp]),
+    "pkv_sched_destroy": (None, [_vp]),
+    "pkv_sched_submit": (C.c_int, [_vp, _i64, _i32, _i32, _i64]),
+    "pkv_sched_step": (C.c_int, [_vp, _vp, _i32, _vp, _vp]),
+    "pkv_sched_get_stats": (C.c_int, [_vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
 }
@@ -390,3 +423,63 @@ class Pool:
     def read_blocks(self, layer, blocks):
         return pkv_read_blocks(self.h, layer, blocks, self.num_kv_heads, self.block_size,
                                self.head_dim, self.kv_dtype)
+
+
+# ------------------------------------------------------- Scheduler ----
+def _arr(ptr, n, dtype):
+    if n <= 0:
+        return np.zeros(0, dtype=dtype)
+    return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+
+class Scheduler:
+    """Continuous-batching step scheduler over a Pool (pkv_sched_* in
+    include/pkv.h). step() returns the plan as numpy copies."""
+
+    def __init__(self, pool: Pool, max_batch: int, max_model_len: int, reserve_blocks: int = 1):
+        self.pool = pool
+        cfg = pkv_sched_config(max_batch, max_model_len, reserve_blocks)
+        h = _vp()
+        _check(lib().pkv_sched_create(pool.h, C.byref(cfg), C.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().pkv_sched_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, request: int, prompt_len: int, max_new_tokens: int, prefix_seq: int = -1):
+        _check(lib().pkv_sched_submit(self.h, request, prompt_len, max_new_tokens, prefix_seq))
+
+    def step(self, eos=(), stream=None) -> dict:
+        eos = np.ascontiguousarray(list(eos), dtype=np.int64)
+        plan = pkv_step_plan()
+        sp = _stream_ptr(stream) if self.pool.arena is not None else None
+        _check(lib().pkv_sched_step(self.h, _np_ptr(eos) if eos.size else None, int(eos.size),
+                                    C.byref(plan), sp))
+        n, mb = plan.num_seqs, plan.max_blocks
+        ev = [(int(plan.events[i].request), int(plan.events[i].kind)) for i in range(plan.num_events)]
+        return {
+            "seqs": _arr(plan.seqs, n, np.int64),
+            "slots": _arr(plan.slots, n, np.int64),
+            "block_tables": _arr(plan.block_tables, n * mb, np.int32).reshape(n, mb),
+            "context_lens": _arr(plan.context_lens, n, np.int32),
+            "max_blocks": mb,
+            "max_context_len": int(plan.max_context_len),
+            "prefill_seqs": _arr(plan.prefill_seqs, plan.num_prefill, np.int64),
+            "prefill_first": _arr(plan.prefill_first, plan.num_prefill, np.int32),
+            "prefill_tokens": _arr(plan.prefill_tokens, plan.num_prefill, np.int32),
+            "prefill_slots": _arr(plan.prefill_slots, plan.prefill_total, np.int64),
+            "events": ev,
+        }
+
+    def stats(self) -> dict:
+        st = pkv_sched_stats()
+        _check(lib().pkv_sched_get_stats(self.h, C.byref(st)))
+        return {k: int(getattr(st, k)) for k, _ in pkv_sched_stats._fields_ if k != "pad_"}
