@@ -57,11 +57,11 @@ def measured_traffic(config):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (40; serving configs 400)")
     # The HIP runtime's first few dozen asynchronous uploads from pinned
     # memory include a handful that block the host for ~6 ms (measured on
     # MI355X with ROCm 7); 50 untimed steps leave them behind.
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (50; serving configs 100)")
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
     ap.add_argument("--merge", choices=["auto", "fused", "separate"], default="auto",
@@ -100,7 +100,23 @@ CONFIGS = {
                      rotate=True),
 }
 
+# Continuous-batching serving ("vLLM核心概念" §3.6 after tuning: max-num-seqs
+# 128, max-model-len 1024, a ~200-token system prompt shared by every request,
+# average generation 300 tokens; 15000 blocks as in its "used / total" log).
+SERVE_CONFIGS = {
+    "serve16": dict(layers=32, hq=32, hkv=8, dim=128, bs=16, nblocks=15000, max_batch=128,
+                    max_model_len=1024, prefix=200, requests=1024, seed=62006),
+    "serve32": dict(layers=32, hq=32, hkv=8, dim=128, bs=32, nblocks=15000, max_batch=128,
+                    max_model_len=1024, prefix=200, requests=1024, seed=62006),
+}
+
 WORKLOAD_NAMES = {
+    "serve16": ("continuous-batching serving: 32 layers, 32q/8kv, d128, bs16, int8 kv; 1024 queued requests, "
+                "each a shared 200-token system prompt + lognormal(mean 300) suffix, ended by EOS after "
+                "lognormal(mean 300) tokens or at max-model-len 1024; max batch 128; pkv_sched plans each step"),
+    "serve32": ("continuous-batching serving: 32 layers, 32q/8kv, d128, bs32, int8 kv; 1024 queued requests, "
+                "each a shared 200-token system prompt + lognormal(mean 300) suffix, ended by EOS after "
+                "lognormal(mean 300) tokens or at max-model-len 1024; max batch 128; pkv_sched plans each step"),
     "qwen": "qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, int8 kv",
     "llama29": "llama-2-7b decode: 32 layers, B=29 x 4096 ctx, 32q/32kv, d128, bs16, fp16 kv",
     "llama128": "llama-2-7b decode: 32 layers, B=128 x 1024 ctx, 32q/32kv, d128, bs16, fp16 kv",
@@ -316,11 +332,16 @@ def cpu_baseline(w: Workload, target_s: float):
 
 def main():
     args = parse()
+    serve = args.config in SERVE_CONFIGS
+    if args.steps is None:
+        args.steps = 400 if serve else 40
+    if args.warmup is None:
+        args.warmup = 100 if serve else 50
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
-    if args.config not in CONFIGS:
-        sys.exit(f"unknown --config {args.config}; choose from {sorted(CONFIGS)}")
+    if args.config not in CONFIGS and args.config not in SERVE_CONFIGS:
+        sys.exit(f"unknown --config {args.config}; choose from {sorted(CONFIGS) + sorted(SERVE_CONFIGS)}")
     import torch
     from paged_kv_cache_62_amd import pkv
     pkv.lib()
@@ -338,7 +359,7 @@ def main():
         return
     stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
     with torch.cuda.stream(stream):
-        res = run(args, stream)
+        res = (run_serve if args.config in SERVE_CONFIGS else run)(args, stream)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(res.pop("_workload"), args.cpu_seconds)
@@ -448,6 +469,166 @@ def run(args, stream):
     }
     res["_workload"] = w
     return res
+
+class _ServeView:
+    """What cpu_baseline reads, for the serving loop's last batch."""
+
+    def __init__(self, pool, seqs, max_blocks, c, q, scale):
+        import paged_kv_cache_62_amd.pkv as pkv
+        self.pkv, self.pool, self.seqs = pkv, pool, seqs
+        self.B, self.L, self.bs, self.max_blocks = len(seqs), c["layers"], c["bs"], max_blocks
+        self.nblocks, self.hkv, self.dim = c["nblocks"], c["hkv"], c["dim"]
+        self.kv_code, self.rotate, self.scale = pkv.PKV_I8, False, scale
+        self.q = [q[: len(seqs)]] * self.L
+
+
+def run_serve(args, stream):
+    """The serving loop: pkv_sched plans every step; admitted prompts' K/V are
+    written with pkv_append_kv, the batch runs pkv_decode_step per layer; a
+    request ends with EOS after its drawn generation length. All queued at
+    the start; W untimed steps fill the batch, then K steps are timed."""
+    import torch
+    from paged_kv_cache_62_amd import pkv, synth
+    c = SERVE_CONFIGS[args.config]
+    print(f"# building serving workload {args.config}", file=sys.stderr, flush=True)
+    L, hq, hkv, dim, bs = c["layers"], c["hq"], c["hkv"], c["dim"], c["bs"]
+    seed, R, mb, mml = c["seed"], c["requests"], c["max_batch"], c["max_model_len"]
+    dev = torch.device("cuda")
+    scale = 1.0 / math.sqrt(dim)
+    order = synth.permutation(synth.stream_seed(seed, 1), c["nblocks"])
+    pool = pkv.Pool(L, hkv, dim, bs, c["nblocks"], pkv.PKV_I8, initial_free_order=order)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    # K/V rows written at admission and per decoded token (the values do not
+    # change the work; every write still quantizes and stores)
+    src_rows = 131072
+    ksrc = torch.randn(src_rows, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+    vsrc = torch.randn(src_rows, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+    q = torch.randn(mb, hq, dim, generator=gen, device=dev).to(torch.bfloat16)
+    knew = torch.randn(mb, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+    vnew = torch.randn(mb, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+    PREFIX = 1 << 40
+    slots = pool.allocate(PREFIX, c["prefix"])
+    d = torch.from_numpy(slots).to(dev)
+    for layer in range(L):
+        pool.append_kv(layer, ksrc[: len(slots)], vsrc[: len(slots)], d)
+    sched = pkv.Scheduler(pool, mb, mml, reserve_blocks=1)
+    suffix = np.minimum(mix_suffix_lengths(seed, R), mml - c["prefix"] - 1)
+    z = synth.normal(synth.stream_seed(seed, 4343), R)
+    eos_at = np.maximum(np.rint(np.exp(math.log(300.0) - 0.32 + 0.8 * z)), 1).astype(np.int64)
+    for r in range(R):
+        sched.submit(r, int(c["prefix"] + suffix[r]), mml, PREFIX)
+    made = np.zeros(R, dtype=np.int64)
+    maxb = (mml + bs - 1) // bs
+    d_table = torch.empty(mb * maxb, dtype=torch.int32, device=dev)
+    d_lens = torch.empty(mb, dtype=torch.int32, device=dev)
+    d_pslots = torch.empty(src_rows, dtype=torch.int64, device=dev)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    out = torch.empty(mb, hq, dim, dtype=torch.float32, device=dev)
+    counts = dict(generated=0, prefill=0, steps=0)
+    eos = []
+    last = {}
+
+    def one_step():
+        nonlocal eos, ws
+        p = sched.step(eos, stream)
+        n, npf = len(p["seqs"]), int(p["prefill_slots"].size)
+        if npf:
+            assert npf <= src_rows
+            d_pslots[:npf].copy_(torch.from_numpy(p["prefill_slots"]), non_blocking=True)
+        if n:
+            d_table[: n * maxb].copy_(torch.from_numpy(p["block_tables"].reshape(-1)), non_blocking=True)
+            d_lens[:n].copy_(torch.from_numpy(p["context_lens"]), non_blocking=True)
+            need = pool.workspace_bytes(n, hq, p["max_context_len"])
+            if need > ws.numel():
+                ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        for layer in range(L):
+            if npf:
+                pool.append_kv(layer, ksrc[:npf], vsrc[:npf], d_pslots[:npf], stream)
+            if n:
+                pool.decode_step(layer, q[:n], knew[:n], vnew[:n], d_table[: n * maxb].view(n, maxb), d_lens[:n],
+                                 p["max_context_len"], scale, out=out[:n], workspace=ws, stream=stream)
+        ids = p["seqs"]
+        made[ids] += 1
+        eos = [int(r) for r in ids[made[ids] >= eos_at[ids]]]
+        counts["generated"] += n
+        counts["prefill"] += npf
+        counts["steps"] += 1
+        last.update(p)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    print(f"# warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    st0 = sched.stats()
+    counts.update(generated=0, prefill=0, steps=0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    st1 = sched.stats()
+
+    # the decode-step kernel alone, over the last batch (graph of its L launches)
+    n, mctx = len(last["seqs"]), last["max_context_len"]
+    tab = d_table[: n * maxb].view(n, maxb)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for layer in range(L):
+            pool.decode_step(layer, q[:n], knew[:n], vnew[:n], tab, d_lens[:n], mctx, scale, out=out[:n],
+                             workspace=ws, stream=stream)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(5, int(args.kernel_reps))
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    avg_dur_s = k0.elapsed_time(k1) / 1e3 / (reps * L)
+    lens = last["context_lens"].astype(np.int64)
+    bytes_launch = float(lens.sum() * hkv * dim * 2 + ((lens + bs - 1) // bs).sum() * hkv * 2 * 4)
+    achieved = bytes_launch / avg_dur_s / 1e9
+    plan = pool.decode_plan(n, mctx, 0, 0)
+    res = {
+        "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": counts["generated"] / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 kv / fp32 accumulate",
+        "data": "synthetic (seeded request lengths and K/V), queued before timing",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "avg_batch": counts["generated"] / args.steps,
+            "prefill_tokens_per_s": counts["prefill"] / (total_ms / 1e3),
+            "admitted": st1["admitted"] - st0["admitted"],
+            "finished_eos": st1["finished_eos"] - st0["finished_eos"],
+            "finished_max_length": st1["finished_max_length"] - st0["finished_max_length"],
+            "preempted": st1["preempted"] - st0["preempted"],
+            "kv_cache_blocks": f"{st1['used_blocks']} used / {st1['total_blocks']} total",
+            "waiting": st1["waiting"],
+            "last_batch": {"seqs": n, "max_context_len": mctx, "partition_tokens": plan[0],
+                           "partitions": plan[1]},
+            "launches_per_layer": "pkv_decode_step, plus pkv_append_kv on steps that admit",
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_kernel, decode step over the last batch",
+                     "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
+                     "timing": f"HIP events around {reps} replays of a graph of the {L} decode launches"},
+    }
+    res["_workload"] = _ServeView(pool, [int(x) for x in last["seqs"]], maxb, c, q, scale)
+    return res
+
 
 if __name__ == "__main__":
     main()
