@@ -81,6 +81,9 @@ CONFIGS = {
     # Qwen3-TTS talker: 28 layers, 8 KV / 16 query heads, d 128, bs 16, B=4 x 8000, INT8.
     "qwen": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, nblocks=2048, B=4, ctx=8000, kv="i8",
                  q="bf16", kvin="bf16", sigma="per_head", seed=62002, outlier=0.0),
+    # the same with FP16 first and last layers, INT8 in between ("轻量级推理引擎实战" §3.2)
+    "qwen_mixed": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, nblocks=2048, B=4, ctx=8000, kv="i8",
+                       q="bf16", kvin="bf16", sigma="per_head", seed=62002, outlier=0.0, fp16_ends=True),
     # Llama-2-7B MHA, FP16 KV: 29 x 4096 (the A100 sizing case) and 128 x 1024.
     "llama29": dict(layers=32, hq=32, hkv=32, dim=128, bs=16, nblocks=8192, B=29, ctx=4096, kv="f16",
                     q="f16", kvin="f16", sigma="unit", seed=62003, outlier=0.0),
@@ -118,6 +121,8 @@ WORKLOAD_NAMES = {
                 "each a shared 200-token system prompt + lognormal(mean 300) suffix, ended by EOS after "
                 "lognormal(mean 300) tokens or at max-model-len 1024; max batch 128; pkv_sched plans each step"),
     "qwen": "qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, int8 kv",
+    "qwen_mixed": ("qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, fp16 kv in the "
+                   "first and last layers, int8 kv in the other 26"),
     "llama29": "llama-2-7b decode: 32 layers, B=29 x 4096 ctx, 32q/32kv, d128, bs16, fp16 kv",
     "llama128": "llama-2-7b decode: 32 layers, B=128 x 1024 ctx, 32q/32kv, d128, bs16, fp16 kv",
     "mix16": "continuous-batching mix: 32 layers, 128 seqs, shared 200-token prefix + lognormal suffix, 32q/8kv, bs16, int8 kv",
@@ -166,7 +171,12 @@ class Workload:
             nblocks = need  # headroom for the blocks the timed steps append
         self.nblocks = nblocks
         order = synth.permutation(synth.stream_seed(seed, 1), nblocks)
+        # per-layer element types: FP16 for the first and last layers when the
+        # configuration asks for it ("轻量级推理引擎实战" §3.2)
+        self.layer_kv = ([pkv.PKV_F16] + [self.kv_code] * (self.L - 2) + [pkv.PKV_F16]
+                         if c.get("fp16_ends") else [self.kv_code] * self.L)
         self.pool = pkv.Pool(self.L, self.hkv, self.dim, self.bs, nblocks, self.kv_code,
+                             layer_kv_dtypes=self.layer_kv if c.get("fp16_ends") else None,
                              initial_free_order=order)
         self.seqs = np.arange(self.B, dtype=np.int64)
         gen = torch.Generator(device=self.dev)
@@ -243,10 +253,10 @@ class Workload:
                 k, v = kv_fill(layer, min(chunk, len(slots) - i))
                 self.pool.append_kv(layer, k, v, d_slots[i:i + chunk])
 
-    def kv_read_bytes(self, lens):
+    def kv_read_bytes(self, lens, layer=0):
         """Algorithmic bytes one decode launch reads: K and V payload of the
         valid tokens plus one fp32 scale per (block, head, K|V) for INT8."""
-        elem = 1 if self.kv_code == self.pkv.PKV_I8 else 2
+        elem = 1 if self.layer_kv[layer] == self.pkv.PKV_I8 else 2
         b = int(lens.sum()) * self.hkv * self.dim * 2 * elem
         if elem == 1:
             b += int(sum((int(n) + self.bs - 1) // self.bs for n in lens)) * self.hkv * 2 * 4
@@ -299,11 +309,11 @@ def cpu_baseline(w: Workload, target_s: float):
     table, lens = w.pool.block_table(w.seqs, w.max_blocks)
     blocks = sorted({int(b) for i in range(w.B) for b in table[i, : (int(lens[i]) + w.bs - 1) // w.bs]})
     threads = max(1, min(16, os.cpu_count() or 1))
-    kvd = orc.I8 if w.kv_code == w.pkv.PKV_I8 else orc.F16
-    dt = np.int8 if kvd == orc.I8 else np.uint16
     done, elapsed = 0, 0.0
     layers = range(w.L) if not w.rotate else [0]
     for layer in layers:
+        kvd = orc.I8 if w.pool.layer_kv_dtypes[layer] == w.pkv.PKV_I8 else orc.F16
+        dt = np.int8 if kvd == orc.I8 else np.uint16
         codes, scales = w.pool.read_blocks(layer, blocks)
         kc = np.zeros((w.nblocks, w.hkv, w.bs, w.dim), dtype=dt)
         vc = np.zeros_like(kc)
@@ -408,7 +418,7 @@ def run(args, stream):
     tokens = 0
     for _ in range(args.steps):
         lens = run_step()
-        step_bytes.append(w.kv_read_bytes(lens) * len(w.decode_layers(0)))
+        step_bytes.append(sum(w.kv_read_bytes(lens, l) for l in w.decode_layers(w.step_i - 1)))
         tokens += w.B
     end.record()
     torch.cuda.synchronize()
@@ -435,7 +445,7 @@ def run(args, stream):
     torch.cuda.synchronize()
     avg_dur_s = e0.elapsed_time(e1) / 1e3 / (reps * len(layers))
     _, lens_now = w.pool.block_table(w.seqs, w.max_blocks)
-    bytes_launch = float(w.kv_read_bytes(lens_now))
+    bytes_launch = float(np.mean([w.kv_read_bytes(lens_now, l) for l in layers]))  # per launch, averaged
     achieved = bytes_launch / avg_dur_s / 1e9
     kv_gbs_step = float(np.sum(step_bytes)) / (total_ms / 1e3) / 1e9
     plan = w.pool.decode_plan(w.B, w.max_ctx, w.partition, w.flags)
@@ -450,7 +460,8 @@ def run(args, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 kv / fp32 accumulate" if w.kv_code == pkv.PKV_I8 else "fp16 kv / fp32 accumulate",
+        "dtype": ("int8 kv (fp16 first and last layers) / fp32 accumulate" if w.c.get("fp16_ends") else
+                  "int8 kv / fp32 accumulate" if w.kv_code == pkv.PKV_I8 else "fp16 kv / fp32 accumulate"),
         "data": "synthetic (seeded), cache filled through pkv_append_kv before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": w.B,
                    "layers_per_step": len(layers),

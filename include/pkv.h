@@ -70,6 +70,12 @@ typedef struct {
   size_t arena_bytes;    /* size of device_arena */
   int32_t host_only;     /* 1 = allocator only, no device memory or HIP calls
                             (device entry points then return PKV_ERR_UNSUPPORTED) */
+  const int32_t* layer_kv_dtype; /* host, optional: num_layers entries of PKV_F16 / PKV_I8,
+                            the element type of each layer ("轻量级推理引擎实战" §3.2:
+                            FP16 for the accuracy-sensitive first and last layers,
+                            INT8 in between); NULL = kv_dtype for every layer.
+                            Copied at create time. The automatic decode plan and
+                            the workspace size follow kv_dtype for every layer. */
 } pkv_pool_config;
 
 typedef struct {
@@ -244,8 +250,8 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
 
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as
- * uint16 for an F16 cache); scales_out (host, may be NULL; INT8 only)
- * [n][2][Hkv] fp32. */
+ * uint16 for an F16 layer); scales_out (host, may be NULL; written for an
+ * INT8 layer only) [n][2][Hkv] fp32. */
 pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
                            void* codes_out, float* scales_out);
 

@@ -8,10 +8,12 @@
 // can share a prefix, and the first write into a shared, partly filled
 // block copies it first (copy-on-write, same section).
 //
-// Device memory (one arena): codes [L][2][N][Hkv][bs][d] followed, for an
-// INT8 cache, by per-(block, head) metadata [L][2][2][N][Hkv] of 4-byte words:
-// for each layer and K|V, the fp32 scales, then the largest |code| of each
-// (block, head) among its written rows (int32).
+// Device memory (one arena): codes [L][2][N][Hkv][bs][d], each layer in its
+// own element type (one for all, or per layer: "轻量级推理引擎实战" §3.2 keeps
+// the first and last layers in FP16), followed, when any layer is INT8, by
+// per-(block, head) metadata [L][2][2][N][Hkv] of 4-byte words: for each layer
+// and K|V, the fp32 scales, then the largest |code| of each (block, head)
+// among its written rows (int32).
 
 #include <hip/hip_runtime_api.h>
 
@@ -69,10 +71,16 @@ struct pkv_pool {
   int device = -1;
   char* arena = nullptr;
   bool owns_arena = false;
-  size_t tile_elems = 0;    // bs * d
-  size_t slice_bytes = 0;   // one (layer, K|V) slice of codes: N*Hkv*bs*d*elem
-  size_t codes_bytes = 0;   // all layers
-  float* scales = nullptr;  // metadata [L][2][scale | qmax][N][Hkv] (int8)
+  size_t tile_elems = 0;               // bs * d
+  std::vector<pkv_dtype> ldt;           // element type of each layer
+  std::vector<size_t> layer_off;        // byte offset of each layer's K slice (V follows)
+  size_t codes_bytes = 0;               // all layers
+  float* scales = nullptr;              // metadata [L][2][scale | qmax][N][Hkv] (int8 layers)
+
+  // one (layer, K|V) slice of codes: N*Hkv*bs*d*elem
+  size_t slice_bytes(int32_t layer) const {
+    return (size_t)cfg.num_blocks * cfg.num_kv_heads * tile_elems * elem_bytes(ldt[layer]);
+  }
 
   int32_t pop_front() {
     const int32_t b = ring[head];
@@ -87,8 +95,8 @@ struct pkv_pool {
   }
   pkv::LayerView layer_view(int32_t layer) const {
     pkv::LayerView lv{};
-    lv.k_codes = arena + (size_t)(2 * layer) * slice_bytes;
-    lv.v_codes = arena + (size_t)(2 * layer + 1) * slice_bytes;
+    lv.k_codes = arena + layer_off[layer];
+    lv.v_codes = arena + layer_off[layer] + slice_bytes(layer);
     const size_t sc_slice = (size_t)cfg.num_blocks * cfg.num_kv_heads;
     lv.k_scales = scales ? scales + (size_t)(4 * layer) * sc_slice : nullptr;
     lv.k_qmax = scales ? (int32_t*)(scales + (size_t)(4 * layer + 1) * sc_slice) : nullptr;
@@ -98,7 +106,7 @@ struct pkv_pool {
     lv.num_kv_heads = cfg.num_kv_heads;
     lv.head_dim = cfg.head_dim;
     lv.block_size = cfg.block_size;
-    lv.kv_dtype = cfg.kv_dtype;
+    lv.kv_dtype = ldt[layer];
     return lv;
   }
 };
@@ -111,6 +119,10 @@ pkv_status check_config(const pkv_pool_config* c) {
     return fail(PKV_ERR_INVALID_ARG, "num_layers, num_kv_heads and num_blocks must be >= 1");
   if (c->kv_dtype != PKV_F16 && c->kv_dtype != PKV_I8)
     return fail(PKV_ERR_INVALID_ARG, "kv_dtype must be PKV_F16 or PKV_I8");
+  if (c->layer_kv_dtype)
+    for (int32_t l = 0; l < c->num_layers; ++l)
+      if (c->layer_kv_dtype[l] != PKV_F16 && c->layer_kv_dtype[l] != PKV_I8)
+        return fail(PKV_ERR_INVALID_ARG, "layer_kv_dtype[%d] must be PKV_F16 or PKV_I8", l);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", c->head_dim);
   if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
@@ -118,11 +130,20 @@ pkv_status check_config(const pkv_pool_config* c) {
   return PKV_OK;
 }
 
+pkv_dtype layer_dtype(const pkv_pool_config* c, int32_t layer) {
+  return c->layer_kv_dtype ? (pkv_dtype)c->layer_kv_dtype[layer] : c->kv_dtype;
+}
+
 size_t required_bytes(const pkv_pool_config* c) {
-  const size_t slice = (size_t)c->num_blocks * c->num_kv_heads * c->block_size * c->head_dim *
-                       elem_bytes(c->kv_dtype);
-  size_t total = round_up(slice * 2 * c->num_layers, 256);
-  if (c->kv_dtype == PKV_I8)
+  const size_t elems = (size_t)c->num_blocks * c->num_kv_heads * c->block_size * c->head_dim;
+  size_t codes = 0;
+  bool any_i8 = false;
+  for (int32_t l = 0; l < c->num_layers; ++l) {
+    codes += 2 * elems * elem_bytes(layer_dtype(c, l));
+    any_i8 = any_i8 || layer_dtype(c, l) == PKV_I8;
+  }
+  size_t total = round_up(codes, 256);
+  if (any_i8)
     total += round_up((size_t)c->num_layers * 4 * c->num_blocks * c->num_kv_heads * sizeof(float), 256);
   return total;
 }
@@ -178,9 +199,15 @@ pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
   p->head = 0;
   p->count = N;
   p->refcount.assign(N, 0);
+  p->cfg.layer_kv_dtype = nullptr;      // copied below, not retained
   p->tile_elems = (size_t)cfg->block_size * cfg->head_dim;
-  p->slice_bytes = (size_t)N * cfg->num_kv_heads * p->tile_elems * elem_bytes(cfg->kv_dtype);
-  p->codes_bytes = p->slice_bytes * 2 * cfg->num_layers;
+  bool any_i8 = false;
+  for (int32_t l = 0; l < cfg->num_layers; ++l) {
+    p->ldt.push_back(layer_dtype(cfg, l));
+    any_i8 = any_i8 || p->ldt[l] == PKV_I8;
+    p->layer_off.push_back(p->codes_bytes);
+    p->codes_bytes += 2 * p->slice_bytes(l);
+  }
   if (!cfg->host_only) {
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
@@ -191,7 +218,7 @@ pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
       if (e != hipSuccess) { delete p; return hip_fail(e, "hipMalloc(pool arena)"); }
       p->owns_arena = true;
     }
-    if (cfg->kv_dtype == PKV_I8) p->scales = (float*)(p->arena + round_up(p->codes_bytes, 256));
+    if (any_i8) p->scales = (float*)(p->arena + round_up(p->codes_bytes, 256));
   }
   *out = p;
   return ok();
@@ -272,21 +299,28 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
         s.blocks[j] = fresh;
         pool->cow_total += 1;
         if (pool->arena) {
-          // whole (block, head) tiles of every layer and K/V: a 2-D copy with
-          // one row per (layer, K|V) slice; then the scales and largest codes
-          // the same way, one row per (layer, K|V, scale|qmax)
-          const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems *
-                                    elem_bytes(pool->cfg.kv_dtype);
-          hipError_t e = hipMemcpy2DAsync(pool->arena + (size_t)fresh * tile_bytes, pool->slice_bytes,
-                                          pool->arena + (size_t)old * tile_bytes, pool->slice_bytes,
-                                          tile_bytes, 2 * (size_t)pool->cfg.num_layers,
-                                          hipMemcpyDeviceToDevice, st);
+          // whole (block, head) tiles of every layer and K/V: one 2-D copy per
+          // run of layers of one element type (one row per (layer, K|V)
+          // slice); then the scales and largest codes the same way, one row
+          // per (layer, K|V, scale|qmax)
+          hipError_t e = hipSuccess;
+          const int32_t L = pool->cfg.num_layers;
+          for (int32_t l0 = 0; l0 < L && e == hipSuccess;) {
+            int32_t l1 = l0 + 1;
+            while (l1 < L && pool->ldt[l1] == pool->ldt[l0]) ++l1;
+            const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * elem_bytes(pool->ldt[l0]);
+            char* base = pool->arena + pool->layer_off[l0];
+            e = hipMemcpy2DAsync(base + (size_t)fresh * tile_bytes, pool->slice_bytes(l0),
+                                 base + (size_t)old * tile_bytes, pool->slice_bytes(l0), tile_bytes,
+                                 2 * (size_t)(l1 - l0), hipMemcpyDeviceToDevice, st);
+            l0 = l1;
+          }
           if (e == hipSuccess && pool->scales) {
             const size_t sc_row = (size_t)pool->cfg.num_kv_heads * sizeof(float);
             const size_t sc_pitch = (size_t)pool->cfg.num_blocks * sc_row;
             e = hipMemcpy2DAsync((char*)pool->scales + (size_t)fresh * sc_row, sc_pitch,
                                  (char*)pool->scales + (size_t)old * sc_row, sc_pitch, sc_row,
-                                 4 * (size_t)pool->cfg.num_layers, hipMemcpyDeviceToDevice, st);
+                                 4 * (size_t)L, hipMemcpyDeviceToDevice, st);
           }
           if (e != hipSuccess) return hip_fail(e, "copy-on-write copy");
         }
@@ -413,6 +447,8 @@ static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t ma
   }
   // About 256 KiB of K and V per workgroup amortises its start-up and its
   // share of the merge: 1024 tokens of INT8 or 512 of FP16 at head_dim 128.
+  // (A pool with per-layer types plans by its kv_dtype, so one workspace
+  // size serves every layer.)
   const int64_t token_bytes = 2LL * c.head_dim * (c.kv_dtype == PKV_I8 ? 1 : 2);
   int32_t T = 128;
   while (T < 2048 && (int64_t)T * 2 * token_bytes <= 262144) T *= 2;
@@ -575,7 +611,8 @@ pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* b
       return fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", blocks[i], c.num_blocks);
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "synchronize before read-back");
-  const size_t esz = elem_bytes(c.kv_dtype);
+  const bool i8 = pool->ldt[layer] == PKV_I8;
+  const size_t esz = elem_bytes(pool->ldt[layer]);
   const size_t tile_bytes = (size_t)c.num_kv_heads * pool->tile_elems * esz;
   const pkv::LayerView lv = pool->layer_view(layer);
   std::vector<char> raw(tile_bytes);
@@ -592,10 +629,10 @@ pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* b
             for (int32_t d = 0; d < c.head_dim; ++d)
               std::memcpy(dst + (hd * te + (size_t)t * c.head_dim + d) * esz,
                           raw.data() + (hd * te + pkv::v_tile_offset(t, d, c.head_dim)) * esz, esz);
-        if (c.kv_dtype == PKV_I8)  // int8 V codes are stored biased by 128
+        if (i8)  // int8 V codes are stored biased by 128
           for (size_t b = 0; b < tile_bytes; ++b) dst[b] = (char)(dst[b] ^ 0x80);
       }
-      if (scales_out && pool->scales) {
+      if (scales_out && i8) {
         const float* ssrc = (kv ? lv.v_scales : lv.k_scales) + (size_t)blocks[i] * c.num_kv_heads;
         e = hipMemcpy(scales_out + ((size_t)i * 2 + kv) * c.num_kv_heads, ssrc,
                       c.num_kv_heads * sizeof(float), hipMemcpyDeviceToHost);

@@ -43,7 +43,7 @@ class pkv_pool_config(C.Structure):
         ("num_layers", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
         ("block_size", _i32), ("num_blocks", _i32), ("kv_dtype", C.c_int),
         ("initial_free_order", _vp), ("device_arena", _vp), ("arena_bytes", _sz),
-        ("host_only", _i32),
+        ("host_only", _i32), ("layer_kv_dtype", _vp),
     ]
 
 
@@ -322,14 +322,21 @@ class Pool:
     whose arena is a torch uint8 tensor owned by this object."""
 
     def __init__(self, num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
-                 initial_free_order=None, host_only=False, device="cuda"):
+                 initial_free_order=None, host_only=False, device="cuda", layer_kv_dtypes=None):
+        """layer_kv_dtypes: optional per-layer PKV_F16 / PKV_I8 (kv_dtype is then the
+        default the automatic decode plan follows)."""
         self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
         self.block_size, self.num_blocks, self.kv_dtype = block_size, num_blocks, kv_dtype
+        self.layer_kv_dtypes = ([kv_dtype] * num_layers if layer_kv_dtypes is None
+                                else [int(x) for x in layer_kv_dtypes])
+        assert len(self.layer_kv_dtypes) == num_layers
         self._order = (None if initial_free_order is None
                        else np.ascontiguousarray(initial_free_order, dtype=np.int32))
+        self._ldt = (None if layer_kv_dtypes is None
+                     else np.ascontiguousarray(self.layer_kv_dtypes, dtype=np.int32))
         cfg = pkv_pool_config(num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
                               None if self._order is None else _np_ptr(self._order), None, 0,
-                              1 if host_only else 0)
+                              1 if host_only else 0, None if self._ldt is None else _np_ptr(self._ldt))
         self.arena = None
         if not host_only:
             import torch
@@ -422,7 +429,7 @@ class Pool:
 
     def read_blocks(self, layer, blocks):
         return pkv_read_blocks(self.h, layer, blocks, self.num_kv_heads, self.block_size,
-                               self.head_dim, self.kv_dtype)
+                               self.head_dim, self.layer_kv_dtypes[layer])
 
 
 # ------------------------------------------------------- Scheduler ----

@@ -171,6 +171,36 @@ def test_decode_step_many_steps(gpu, kv, bs, alternate):
     H.assert_attention_close(res["gpu"], res["ref"])
 
 
+MIXED = [orc.F16, orc.I8, orc.I8, orc.F16]  # FP16 first and last layers ("轻量级推理引擎实战" §3.2)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_mixed_precision_layers(gpu, bs):
+    """Per-layer element types in one pool: every layer bit-exact with an oracle
+    cache of its own type (copy-on-write copies all of them), attention within
+    tolerance per layer."""
+    c = _growing_case(orc.I8, bs, 62900 + bs)
+    c.shape.layers = 4
+    c.shape.layer_kv_dtypes = MIXED
+    res = H.run_decode_case(c)
+    _report(f"mixed bs={bs}", res)
+    assert res["pool"].stats()["cow_copies"] > 0
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
+@pytest.mark.parametrize("alternate", [False, True])
+def test_mixed_precision_decode_steps(gpu, alternate):
+    lens = [1, 13, 40, 90]
+    sh = H.Shape(layers=4, hq=8, hkv=2, dim=128, bs=16, nblocks=40, kv_dtype=orc.I8,
+                 in_dtype="bf16", q_dtype="bf16", free_order_seed=7, sigma_kv="per_head",
+                 outlier_p=0.01, layer_kv_dtypes=MIXED)
+    case = H.Case(sh, 62950 + alternate, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=[0, 1, 2, 3])
+    res = H.run_step_case(case, steps=20, alternate=alternate)
+    _report(f"mixed steps alternate={alternate}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
 def test_f16_cache_special_values(gpu):
     """binary16 rounding of edge values (ties, subnormals, overflow)."""
     import torch
