@@ -84,6 +84,10 @@ CONFIGS = {
     # the same with FP16 first and last layers, INT8 in between ("轻量级推理引擎实战" §3.2)
     "qwen_mixed": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, nblocks=2048, B=4, ctx=8000, kv="i8",
                        q="bf16", kvin="bf16", sigma="per_head", seed=62002, outlier=0.0, fp16_ends=True),
+    # the same with lazy quantization: a sequence's partly filled last block stays FP16
+    # and is quantized when full ("轻量级推理引擎实战" §三); append + decode launches
+    "qwen_seal": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, nblocks=2048, B=4, ctx=8000, kv="i8",
+                      q="bf16", kvin="bf16", sigma="per_head", seed=62002, outlier=0.0, seal=True),
     # Llama-2-7B MHA, FP16 KV: 29 x 4096 (the A100 sizing case) and 128 x 1024.
     "llama29": dict(layers=32, hq=32, hkv=32, dim=128, bs=16, nblocks=8192, B=29, ctx=4096, kv="f16",
                     q="f16", kvin="f16", sigma="unit", seed=62003, outlier=0.0),
@@ -123,6 +127,8 @@ WORKLOAD_NAMES = {
     "qwen": "qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, int8 kv",
     "qwen_mixed": ("qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, fp16 kv in the "
                    "first and last layers, int8 kv in the other 26"),
+    "qwen_seal": ("qwen3-tts-talker decode: 28 layers, B=4 x 8000 ctx, 16q/8kv, d128, bs16, int8 kv "
+                  "quantized when a block fills (fp16 until then)"),
     "llama29": "llama-2-7b decode: 32 layers, B=29 x 4096 ctx, 32q/32kv, d128, bs16, fp16 kv",
     "llama128": "llama-2-7b decode: 32 layers, B=128 x 1024 ctx, 32q/32kv, d128, bs16, fp16 kv",
     "mix16": "continuous-batching mix: 32 layers, 128 seqs, shared 200-token prefix + lognormal suffix, 32q/8kv, bs16, int8 kv",
@@ -153,7 +159,9 @@ class Workload:
         self.rotate = c.get("rotate", False)
         self.partition = partition or c.get("partition", 0)
         self.flags = flags
-        self.fused = fused  # one pkv_decode_step launch per decoded layer instead of append + decode
+        # one pkv_decode_step launch per decoded layer instead of append + decode
+        # (not for a seal-on-full cache, which pkv_decode_step does not take)
+        self.fused = fused and not c.get("seal")
         self.scale = 1.0 / math.sqrt(self.dim)
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
         seed = c["seed"]
@@ -177,6 +185,7 @@ class Workload:
                          if c.get("fp16_ends") else [self.kv_code] * self.L)
         self.pool = pkv.Pool(self.L, self.hkv, self.dim, self.bs, nblocks, self.kv_code,
                              layer_kv_dtypes=self.layer_kv if c.get("fp16_ends") else None,
+                             seal_on_full=bool(c.get("seal")),
                              initial_free_order=order)
         self.seqs = np.arange(self.B, dtype=np.int64)
         gen = torch.Generator(device=self.dev)
@@ -257,6 +266,11 @@ class Workload:
         """Algorithmic bytes one decode launch reads: K and V payload of the
         valid tokens plus one fp32 scale per (block, head, K|V) for INT8."""
         elem = 1 if self.layer_kv[layer] == self.pkv.PKV_I8 else 2
+        if elem == 1 and self.c.get("seal"):  # full blocks INT8 + scales, partly filled ones FP16
+            lens = np.asarray(lens, dtype=np.int64)
+            full = lens // self.bs
+            return int((full * self.bs).sum() * self.hkv * self.dim * 2 + full.sum() * self.hkv * 2 * 4 +
+                       (lens - full * self.bs).sum() * self.hkv * self.dim * 2 * 2)
         b = int(lens.sum()) * self.hkv * self.dim * 2 * elem
         if elem == 1:
             b += int(sum((int(n) + self.bs - 1) // self.bs for n in lens)) * self.hkv * 2 * 4
@@ -461,6 +475,8 @@ def run(args, stream):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("int8 kv (fp16 first and last layers) / fp32 accumulate" if w.c.get("fp16_ends") else
+                  "int8 kv quantized when a block fills (fp16 partly filled blocks) / fp32 accumulate"
+                  if w.c.get("seal") else
                   "int8 kv / fp32 accumulate" if w.kv_code == pkv.PKV_I8 else "fp16 kv / fp32 accumulate"),
         "data": "synthetic (seeded), cache filled through pkv_append_kv before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": w.B,

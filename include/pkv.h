@@ -76,6 +76,14 @@ typedef struct {
                             INT8 in between); NULL = kv_dtype for every layer.
                             Copied at create time. The automatic decode plan and
                             the workspace size follow kv_dtype for every layer. */
+  int32_t seal_on_full;  /* 1 = lazy quantization of the INT8 layers ("轻量级推理引擎实战"
+                            §三, third design note): a block stays in FP16 (staging
+                            tiles, as much memory again as FP16 codes) while it is a
+                            sequence's partly filled last block, and is quantized once,
+                            all rows together, by the append that writes its last row
+                            (see pkv_append_kv). Decode reads the FP16 rows of a
+                            sequence's partly filled last block and INT8 elsewhere.
+                            pkv_decode_step does not support it. 0 = quantize on append. */
 } pkv_pool_config;
 
 typedef struct {
@@ -164,7 +172,11 @@ pkv_status pkv_pool_free_queue(const pkv_pool* pool, int32_t* out, int32_t cap, 
  *   max|old code| * old scale, X is encoded with the old scale when
  *   max|X| <= m_old, otherwise the scale becomes max|X|/127 and the old
  *   codes are re-encoded from their dequantized values. Encoding divides by
- *   the scale (IEEE binary32) and rounds half to even. */
+ *   the scale (IEEE binary32) and rounds half to even.
+ *   I8 layer of a seal_on_full pool: each value is rounded to binary16 and
+ *   staged; when a block's last row is written, the block's bs rows (as
+ *   binary16 values) are quantized together: scale max|x|/127 (1.0 when
+ *   <= 1e-6), codes as above. */
 pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const void* v,
                          pkv_dtype in_dtype, const int64_t* slot_mapping, int32_t n_tokens,
                          void* stream);
@@ -362,6 +374,14 @@ pkv_status pkv_sched_step(pkv_sched* sched, const int64_t* eos, int32_t n_eos, p
                           void* stream);
 
 pkv_status pkv_sched_get_stats(const pkv_sched* sched, pkv_sched_stats* out);
+
+/* Synchronous host export of the FP16 staging tiles of a seal-on-full INT8
+ * layer (pool created with seal_on_full): f16_out (host) [n][2 (K,V)][Hkv]
+ * [bs][d] binary16 bits in canonical order. Rows a block holds while it is
+ * partly filled are meaningful; after it is sealed they are stale.
+ * PKV_ERR_UNSUPPORTED for a layer without staging tiles. */
+pkv_status pkv_read_tail_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
+                                uint16_t* f16_out);
 
 /* The KV-bytes formula 2*L*H*d*s*B*bytes ("无 vLLM 环境下的 Paged-KV" §2). */
 uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,

@@ -21,6 +21,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 OK, INVALID, OOM, NO_FREE_BLOCK, UNKNOWN_SEQ, SEQ_EXISTS = 0, -1, -2, -3, -4, -5
 F16, I8 = 1, 3  # cache element types (binary16 bits / int8 codes)
+VALUES = 0      # decode_attention over float64 key/value numbers (mixed-format caches)
 
 
 def build(force: bool = True) -> str:
@@ -241,10 +242,13 @@ class Cache:
 def decode_attention(kv_dtype, k_codes, v_codes, k_scales, v_scales, q, table, lens,
                      softmax_scale, threads=0):
     """FP64 paged decode attention over one layer's cache arrays
-    (oracle layout [N][Hkv][bs][dim]). q: [B][Hq][dim] binary32.
+    (oracle layout [N][Hkv][bs][dim]): int8 codes (I8), binary16 bits (F16),
+    or the values themselves as float64 (VALUES). q: [B][Hq][dim] binary32.
     Returns [B][Hq][dim] float64."""
+    want = {I8: np.int8, F16: np.uint16, VALUES: np.float64}[kv_dtype]
     k_codes = np.ascontiguousarray(k_codes)
     v_codes = np.ascontiguousarray(v_codes)
+    assert k_codes.dtype == want and v_codes.dtype == want
     N, hkv, bs, dim = k_codes.shape
     k_scales = np.ascontiguousarray(k_scales, dtype=np.float32)
     v_scales = np.ascontiguousarray(v_scales, dtype=np.float32)

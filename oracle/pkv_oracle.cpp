@@ -488,9 +488,10 @@ void orc_cache_read_block(void* p, int32_t layer, int32_t block, void* codes_out
 // counts every token to attend to, including the one just appended.
 //
 // Cache arrays for ONE layer: k_codes, v_codes [nblocks][Hkv][bs][dim]
-// (int8, or binary16 bits when kv_dtype == 1); k_scales, v_scales
-// [nblocks][Hkv] (read only for int8). q: binary32 [B][Hq][dim] (exact
-// widening of the caller's query). out: [B][Hq][dim] FP64.
+// (int8 when kv_dtype == 3, binary16 bits when 1, or the key/value numbers
+// themselves as binary64 when 0 -- for caches whose blocks mix formats);
+// k_scales, v_scales [nblocks][Hkv] (read only for int8). q: binary32
+// [B][Hq][dim] (exact widening of the caller's query). out: [B][Hq][dim] FP64.
 // ---------------------------------------------------------------------------
 struct OrcAttnArgs {
   int32_t kv_dtype, nblocks, hkv, bs, dim;
@@ -506,6 +507,7 @@ static double orc_dequant(const OrcAttnArgs& a, const void* codes, const float* 
   const size_t idx = (((size_t)block * a.hkv + head) * a.bs + row) * a.dim + d;
   if (a.kv_dtype == 3)
     return (double)((const int8_t*)codes)[idx] * (double)scales[(size_t)block * a.hkv + head];
+  if (a.kv_dtype == 0) return ((const double*)codes)[idx];
   return (double)orc_f16_to_f32(((const uint16_t*)codes)[idx]);
 }
 

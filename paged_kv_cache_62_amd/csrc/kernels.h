@@ -43,6 +43,13 @@ struct LayerView {
   float* v_scales;
   int32_t* k_qmax;
   int32_t* v_qmax;
+  // Seal-on-full INT8 layer (seal != 0): FP16 staging tiles [N][Hkv][tile]
+  // per K and V, laid out as an FP16 cache's. A block's rows stay there
+  // while it is a sequence's partly filled last block; the append that
+  // writes its last row quantizes the whole block into the INT8 tile.
+  void* tail_k;
+  void* tail_v;
+  int32_t seal;
   int32_t num_blocks, num_kv_heads, head_dim, block_size, kv_dtype;
 };
 

@@ -420,6 +420,75 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
 }
 
 // ---------------------------------------------------------------------------
+// H1 for a seal-on-full INT8 layer (lazy quantization, "轻量级推理引擎实战"
+// §三, third design note): one wavefront per (run, head, K|V), runs found as
+// above. A run that leaves its block partly filled is stored as binary16
+// rows in the block's FP16 staging tile. The run that writes the block's last
+// row quantizes the whole block -- its staged rows and the run's own, all as
+// binary16 values -- with the section's quantize_block: one scale max|x|/127
+// (1.0 for an all-zero head), codes round(x / scale) to even, clamped to
+// [-127, 127]; it stores the codes, the scale and the largest |code|.
+// ---------------------------------------------------------------------------
+template <int IN>
+__global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, const void* k,
+                                                          const void* v, const int64_t* slots,
+                                                          int32_t n) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hkv = lv.num_kv_heads;
+  if (wid >= (int64_t)n * hkv * 2) return;
+  const int h = (int)(wid % hkv);
+  const int kv = (int)((wid / hkv) & 1);
+  const int64_t i = wid / hkv / 2;
+  const int bs = lv.block_size;
+  const int lbs = __builtin_ctz(bs);
+  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
+  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
+  const int64_t blk = slot0 >> lbs;
+  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
+  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
+  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
+  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
+  const int row0 = (int)(slot0 & (bs - 1));
+  const int nr = min(run, bs - row0);
+
+  const int D = lv.head_dim, ld = __builtin_ctz(D);
+  const void* src = kv ? v : k;
+  uint16_t* t16 = (uint16_t*)(kv ? lv.tail_v : lv.tail_k) + ((size_t)blk * hkv + h) * bs * D;
+  auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
+  // element e of the run (row e >> ld, dim e % D) as binary16 bits
+  auto run_bits = [&](int e) {
+    return __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))));
+  };
+  if (row0 + nr < bs) {  // the block stays partly filled: stage the rows
+    for (int e = lane; e < nr * D; e += 64) t16[off(row0 + (e >> ld), e & (D - 1))] = run_bits(e);
+    return;
+  }
+  // the block is complete: its bs rows as binary16 values, staged or new
+  auto value = [&](int e) {  // element e of the block (row e >> ld)
+    const int t = e >> ld, dd = e & (D - 1);
+    return f16_to_f32(t < row0 ? t16[off(t, dd)] : run_bits(((t - row0) << ld) | dd));
+  };
+  float mx = 0.f;
+  for (int e = lane; e < bs * D; e += 64) mx = fmaxf(mx, fabsf(value(e)));
+  mx = wave_max(mx);
+  const float sc = scale_of(mx);
+  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
+  const int8_t bias = kv ? (int8_t)0x80 : 0;  // V codes are stored biased by 128
+  int qm = 0;
+  for (int e = lane; e < bs * D; e += 64) {
+    const int8_t q = encode(value(e), sc);
+    qm = max(qm, abs((int)q));
+    tile[off(e >> ld, e & (D - 1))] = (int8_t)(q ^ bias);
+  }
+  qm = wave_max_int(qm);
+  if (lane == 0) {
+    (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
+    (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // H2: split-context decode on the matrix cores.
 //
 // Lane l of a wavefront: n16 = l % 16 (MFMA column / K row), gq = l / 16.
@@ -435,14 +504,16 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
 // the workspace and the last workgroup of the (sequence, KV head) to finish
 // merges all partitions.
 // ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT, bool APPEND>
+template <bool I8, int D, int G, int QT, bool APPEND, bool SEAL>
 __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
+  static_assert(!SEAL || (I8 && !APPEND), "seal-on-full: INT8 decode without append");
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int RB = D * ESZ;       // bytes per K row
   constexpr int NCH = RB / 64;      // 16-byte chunks per lane per unit (K, and V)
   constexpr int NDT = D / 16;       // 16-dim tiles of the PV product
   constexpr int UB = kUnit * RB;    // bytes of one 16-token sub-tile
   constexpr int NB = I8 ? 3 : 2;    // units in flight per wavefront
+  constexpr int NCH16 = D / 32;     // 16-byte chunks per lane of an FP16 unit (seal-on-full tail)
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: lets unit indices, table entries, scales and tile addresses
@@ -499,6 +570,16 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int nrem = max(u1 - u0, 0) & (upb - 1);
   const int nu = (nblk_full > wave ? ((nblk_full - wave + kWaves - 1) / kWaves) << lupb : 0) +
                  (nrem > 0 && (nblk_full & (kWaves - 1)) == wave ? nrem : 0);
+  // Seal-on-full cache: a partly filled last block of the sequence is still
+  // in FP16 (its staging tiles); the wavefront that holds it reads its units
+  // (its last ntail units) after the loop, from there.
+  int ntail = 0;
+  if constexpr (SEAL) {
+    const int r = len & (bs - 1);
+    const int nbl = ((len - 1) >> (lupb + 4)) - (u0 >> lupb);  // the last block within the partition
+    if (r > 0 && t1 == len && (nbl & (kWaves - 1)) == wave) ntail = (r + kUnit - 1) / kUnit;
+  }
+  const int nu8 = nu - ntail;  // units read through the ring
 
   // Lane i keeps unit i's block id, its byte offset in the K (and V) codes
   // of the layer and (int8) its scales; the loop reads them with readlane.
@@ -596,7 +677,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   set_blocks(0, tentry);
   gather_scales();
 #pragma unroll
-  for (int b = 0; b < NB; ++b) issue(b, nu, kb[b], vb[b]);
+  for (int b = 0; b < NB; ++b) issue(b, nu8, kb[b], vb[b]);
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -607,6 +688,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int pc = I8 ? (n16 >> 2) : (n16 >> 3);
   const bool qcol = hc < G && (I8 ? pc < 3 : (pc == 0 || QT == kF32));
   __shared__ __align__(16) uint32_t sm_qb[NCH * 64 * 4];  // [c][lane][16 bytes]
+  __shared__ __align__(16) uint32_t sm_qt[SEAL ? NCH16 * 64 * 4 : 4];  // fp16 form (SEAL)
+  if constexpr (SEAL) {  // unused column parts must read as zero
+    for (int w = threadIdx.x; w < NCH16 * 64 * 4; w += kThreads) sm_qt[w] = 0u;
+  }
   __shared__ int sm_hmax[G];
   if (threadIdx.x < G) sm_hmax[threadIdx.x] = 0;
   __syncthreads();
@@ -633,6 +718,14 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
       for (int d = 0; d < 3; ++d)
         b[((c * 64 + gql * 16 + 4 * d + h) << 4) + j] = (unsigned char)(((z >> (8 * d)) & 255u) ^ 0x80u);
+      if constexpr (SEAL) {  // the fp16 form too, for the FP16 tail units
+        const float y = ldexpf(qe[k], 15 - qexp);
+        const _Float16 hi = (_Float16)y;
+        const int c16 = dim >> 5, gql16 = (dim >> 3) & 3, j16 = dim & 7;
+        _Float16* bt = (_Float16*)sm_qt;
+        bt[((c16 * 64 + gql16 * 16 + h) << 3) + j16] = hi;
+        if constexpr (QT == kF32) bt[((c16 * 64 + gql16 * 16 + 8 + h) << 3) + j16] = (_Float16)(y - (float)hi);
+      }
     } else {
       const float y = ldexpf(qe[k], 15 - qexp);
       const _Float16 hi = (_Float16)y;
@@ -709,6 +802,23 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const float qconst = ldexpf(a.softmax_scale * kLog2e, (I8 ? qexp - 22 : qexp - 15));
   i32x4 qb[I8 ? NCH : 1];
   f16x8 qh[I8 ? 1 : NCH];
+  // SEAL: the fp16 operand for tail units, columns as in the FP16 kernel
+  // (hi part of head n16 < 8, lo part of head n16 - 8 for an fp32 query)
+  f16x8 qt[SEAL ? NCH16 : 1];
+  float qconst_t = 0.f;
+  if constexpr (SEAL) {
+    const int hc16 = n16 & 7, pc16 = n16 >> 3;
+    const bool qcol16 = hc16 < G && (pc16 == 0 || QT == kF32);
+    int qexp16;
+    frexpf(__int_as_float(sm_hmax[min(hc16, G - 1)]), &qexp16);
+    qconst_t = ldexpf(a.softmax_scale * kLog2e, qexp16 - 15);
+#pragma unroll
+    for (int c = 0; c < NCH16; ++c) {
+      uint4 w = *(const uint4*)&sm_qt[(c * 64 + lane) * 4];
+      if (!qcol16) w = make_uint4(0u, 0u, 0u, 0u);
+      qt[c] = __builtin_bit_cast(f16x8, w);
+    }
+  }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     uint4 w = *(const uint4*)&sm_qb[(c * 64 + lane) * 4];
@@ -736,13 +846,27 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](const uint4 (&kr)[NCH], const uint4 (&vr)[NCH], float kscale, float vscale,
-                     int tok0) {
+  // One unit of 16 tokens. TAIL: an FP16 unit in an INT8 kernel (a
+  // seal-on-full cache's partly filled last block), scored with the fp16
+  // query operand and taken with V scale 1; otherwise the kernel's own type.
+  auto process = [&](auto tail, const auto& kr, const auto& vr, float kscale, float vscale, int tok0) {
+    constexpr bool TAIL = decltype(tail)::value;
     const int nvalid = t1 - tok0;  // rows of this unit inside the partition
 
     // S^T = K Q^T: lane holds tokens 4*gq + i of column n16
     float sc[4];
-    if constexpr (I8) {
+    if constexpr (TAIL) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCH16; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[c]), qt[c], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[i];
+        if constexpr (QT == kF32) x += dpp_f<kRowShl8>(x);  // + the lo column
+        sc[i] = x * qconst_t;
+      }
+    } else if constexpr (I8) {
       i32x4 acc = {0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
@@ -821,15 +945,16 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     const f16x4 pb = __builtin_bit_cast(
         f16x4, make_uint2(hb.x | (uint32_t)dpp_i<kRowShr8>((int)lb.x), hb.y | (uint32_t)dpp_i<kRowShr8>((int)lb.y)));
 
-    uint32_t vw[4 * NCH];
+    constexpr int NV = TAIL ? NCH16 : NCH;
+    uint32_t vw[4 * NV];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < NV; ++c) {
       vw[4 * c] = vr[c].x; vw[4 * c + 1] = vr[c].y; vw[4 * c + 2] = vr[c].z; vw[4 * c + 3] = vr[c].w;
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       f16x4 av;
-      if constexpr (I8) {
+      if constexpr (I8 && !TAIL) {
         av = biased_i8x4_to_f16x4(vw[dt]);
       } else {
         av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
@@ -924,11 +1049,11 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // unit still consumes its (zero-size) loads, so that every path through
   // the loop leaves the same loads outstanding and the compiler's wait
   // counts stay exact.
-  for (int i0 = 0; i0 < nu; i0 += NB) {
+  for (int i0 = 0; i0 < nu8; i0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int i = i0 + b;
-      if (i < nu) {
+      if (i < nu8) {
         float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uks), i));
         float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, uvs), i));
         if constexpr (APPEND) {
@@ -938,7 +1063,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
             vs = sv_new;
           }
         }
-        process(kb[b], vb[b], ks, vs, unit_of(i) * kUnit);
+        process(std::false_type{}, kb[b], vb[b], ks, vs, unit_of(i) * kUnit);
       } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -946,7 +1071,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
           asm volatile("" ::"v"(vb[b][c].x), "v"(vb[b][c].y), "v"(vb[b][c].z), "v"(vb[b][c].w));
         }
       }
-      issue(i + NB, nu, kb[b], vb[b]);
+      issue(i + NB, nu8, kb[b], vb[b]);
     }
   }
 
@@ -957,6 +1082,24 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       a.lv.v_scales[at] = sv_new;
       a.lv.k_qmax[at] = qmax_k;
       a.lv.v_qmax[at] = qmax_v;
+    }
+  }
+
+  if constexpr (SEAL) {
+    if (ntail > 0) {  // wave-uniform: the FP16 tail, after the INT8 units
+      const int blk = min(max(__builtin_amdgcn_readlane(tentry, nu - 1), 0), a.lv.num_blocks - 1);
+      const size_t tile16 = (size_t)bs * D * 2;
+      const char* tk = (const char*)a.lv.tail_k + ((size_t)blk * hkv + g) * tile16;
+      const char* tv = (const char*)a.lv.tail_v + ((size_t)blk * hkv + g) * tile16;
+      for (int j = 0; j < ntail; ++j) {
+        uint4 kr[NCH16], vr[NCH16];
+#pragma unroll
+        for (int c = 0; c < NCH16; ++c) {
+          kr[c] = *(const uint4*)(tk + (size_t)(kUnit * j + n16) * D * 2 + 16 * gq + 64 * c);
+          vr[c] = *(const uint4*)(tv + (size_t)j * kUnit * D * 2 + lane * (16 * NCH16) + 16 * c);
+        }
+        process(std::true_type{}, kr, vr, 1.f, 1.f, unit_of(nu8 + j) * kUnit);
+      }
     }
   }
 
@@ -1070,15 +1213,15 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 // Both variants fit in 168 registers with their K/V rings: three wavefronts
 // (three workgroups) per SIMD pair of registers budget, i.e. 768 resident
 // workgroups on 256 CUs.
-template <int D, int G, int QT, bool APPEND>
+template <int D, int G, int QT, bool APPEND, bool SEAL = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_i8(const DecodeLaunch a) {
-  decode_body<true, D, G, QT, APPEND>(a);
+  decode_body<true, D, G, QT, APPEND, SEAL>(a);
 }
 template <int D, int G, int QT, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_kernel_f16(const DecodeLaunch a) {
-  decode_body<false, D, G, QT, APPEND>(a);
+  decode_body<false, D, G, QT, APPEND, false>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,6 +1264,8 @@ void launch_one(const DecodeLaunch& d, hipStream_t stream) {
   if constexpr (I8) {
     if (step)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true>), grid, dim3(kThreads), 0, stream, d);
+    else if (d.lv.seal)
+      hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, false, true>), grid, dim3(kThreads), 0, stream, d);
     else
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, false>), grid, dim3(kThreads), 0, stream, d);
   } else {
@@ -1198,6 +1343,15 @@ hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int 
       case kF32: hipLaunchKernelGGL(append_f16_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
       case kF16: hipLaunchKernelGGL(append_f16_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
       case kBF16: hipLaunchKernelGGL(append_f16_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (lv.seal) {
+    const int64_t waves = (int64_t)n * lv.num_kv_heads * 2;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    switch (in_dtype) {
+      case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
+      case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
+      case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
       default: return hipErrorInvalidValue;
     }
   } else {

@@ -76,6 +76,9 @@ struct pkv_pool {
   std::vector<size_t> layer_off;        // byte offset of each layer's K slice (V follows)
   size_t codes_bytes = 0;               // all layers
   float* scales = nullptr;              // metadata [L][2][scale | qmax][N][Hkv] (int8 layers)
+  char* tails = nullptr;                // seal_on_full: FP16 staging [INT8 layers][2][N][Hkv][tile]
+  std::vector<int32_t> tail_index;      // seal_on_full: each layer's index among the INT8 layers, or -1
+  size_t tail_slice = 0;                // bytes of one (INT8 layer, K|V) staging slice
 
   // one (layer, K|V) slice of codes: N*Hkv*bs*d*elem
   size_t slice_bytes(int32_t layer) const {
@@ -107,6 +110,11 @@ struct pkv_pool {
     lv.head_dim = cfg.head_dim;
     lv.block_size = cfg.block_size;
     lv.kv_dtype = ldt[layer];
+    if (tails && tail_index[layer] >= 0) {
+      lv.seal = 1;
+      lv.tail_k = tails + (size_t)(2 * tail_index[layer]) * tail_slice;
+      lv.tail_v = tails + (size_t)(2 * tail_index[layer] + 1) * tail_slice;
+    }
     return lv;
   }
 };
@@ -145,6 +153,11 @@ size_t required_bytes(const pkv_pool_config* c) {
   size_t total = round_up(codes, 256);
   if (any_i8)
     total += round_up((size_t)c->num_layers * 4 * c->num_blocks * c->num_kv_heads * sizeof(float), 256);
+  if (c->seal_on_full) {  // FP16 staging tiles for every INT8 layer
+    int32_t n_i8 = 0;
+    for (int32_t l = 0; l < c->num_layers; ++l) n_i8 += layer_dtype(c, l) == PKV_I8;
+    total += round_up(2 * (size_t)n_i8 * elems * 2, 256);
+  }
   return total;
 }
 
@@ -218,7 +231,17 @@ pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
       if (e != hipSuccess) { delete p; return hip_fail(e, "hipMalloc(pool arena)"); }
       p->owns_arena = true;
     }
-    if (any_i8) p->scales = (float*)(p->arena + round_up(p->codes_bytes, 256));
+    size_t at = round_up(p->codes_bytes, 256);
+    if (any_i8) {
+      p->scales = (float*)(p->arena + at);
+      at += round_up((size_t)cfg->num_layers * 4 * N * cfg->num_kv_heads * sizeof(float), 256);
+    }
+    if (cfg->seal_on_full && any_i8) {
+      p->tails = p->arena + at;
+      p->tail_slice = (size_t)N * cfg->num_kv_heads * p->tile_elems * 2;
+      int32_t k = 0;
+      for (int32_t l = 0; l < cfg->num_layers; ++l) p->tail_index.push_back(p->ldt[l] == PKV_I8 ? k++ : -1);
+    }
   }
   *out = p;
   return ok();
@@ -314,6 +337,14 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
                                  base + (size_t)old * tile_bytes, pool->slice_bytes(l0), tile_bytes,
                                  2 * (size_t)(l1 - l0), hipMemcpyDeviceToDevice, st);
             l0 = l1;
+          }
+          if (e == hipSuccess && pool->tails) {  // staged FP16 rows: one slice per (INT8 layer, K|V)
+            int32_t n_i8 = 0;
+            for (int32_t l = 0; l < L; ++l) n_i8 += pool->tail_index[l] >= 0;
+            const size_t t16 = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * 2;
+            e = hipMemcpy2DAsync(pool->tails + (size_t)fresh * t16, pool->tail_slice,
+                                 pool->tails + (size_t)old * t16, pool->tail_slice, t16, 2 * (size_t)n_i8,
+                                 hipMemcpyDeviceToDevice, st);
           }
           if (e == hipSuccess && pool->scales) {
             const size_t sc_row = (size_t)pool->cfg.num_kv_heads * sizeof(float);
@@ -593,6 +624,9 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
                            float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL k_new or v_new");
+  if (pool && pool->tails && layer >= 0 && layer < pool->cfg.num_layers && pool->tail_index[layer] >= 0)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_decode_step: layer %d quantizes on seal; use pkv_append_kv + "
+                "pkv_decode_attention", layer);
   return decode_launch(pool, layer, q, dtype, num_q_heads, k_new, v_new, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len, softmax_scale,
                        partition_tokens, flags, out, workspace, workspace_bytes, stream);
@@ -638,6 +672,41 @@ pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* b
                       c.num_kv_heads * sizeof(float), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_fail(e, "read-back of scales");
       }
+    }
+  }
+  return ok();
+}
+
+pkv_status pkv_read_tail_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
+                                uint16_t* f16_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
+  if (!pool->tails || pool->tail_index[layer] < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "layer %d has no FP16 staging tiles", layer);
+  if (n < 0 || (n > 0 && (!blocks || !f16_out))) return fail(PKV_ERR_INVALID_ARG, "bad arguments");
+  for (int32_t i = 0; i < n; ++i)
+    if (blocks[i] < 0 || blocks[i] >= c.num_blocks)
+      return fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", blocks[i], c.num_blocks);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronize before read-back");
+  const pkv::LayerView lv = pool->layer_view(layer);
+  const size_t te = pool->tile_elems;
+  const size_t tile = (size_t)c.num_kv_heads * te;  // elements of one block's K (or V) tiles
+  std::vector<uint16_t> raw(tile);
+  for (int32_t i = 0; i < n; ++i) {
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = (const uint16_t*)(kv ? lv.tail_v : lv.tail_k) + (size_t)blocks[i] * tile;
+      uint16_t* dst = f16_out + ((size_t)i * 2 + kv) * tile;
+      e = hipMemcpy(raw.data(), src, tile * 2, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "read-back of staging tiles");
+      for (int32_t hd = 0; hd < c.num_kv_heads; ++hd)
+        for (int32_t t = 0; t < c.block_size; ++t)
+          for (int32_t d = 0; d < c.head_dim; ++d)
+            dst[hd * te + (size_t)t * c.head_dim + d] =
+                raw[hd * te + (kv ? pkv::v_tile_offset(t, d, c.head_dim) : pkv::k_tile_offset(t, d, c.head_dim))];
     }
   }
   return ok();

@@ -43,7 +43,7 @@ class pkv_pool_config(C.Structure):
         ("num_layers", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
         ("block_size", _i32), ("num_blocks", _i32), ("kv_dtype", C.c_int),
         ("initial_free_order", _vp), ("device_arena", _vp), ("arena_bytes", _sz),
-        ("host_only", _i32), ("layer_kv_dtype", _vp),
+        ("host_only", _i32), ("layer_kv_dtype", _vp), ("seal_on_full", _i32),
     ]
 
 
@@ -106,6 +106,7 @@ SIGNATURES = {
     "pkv_sched_submit": (C.c_int, [_vp, _i64, _i32, _i32, _i64]),
     "pkv_sched_step": (C.c_int, [_vp, _vp, _i32, _vp, _vp]),
     "pkv_sched_get_stats": (C.c_int, [_vp, _vp]),
+    "pkv_read_tail_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
 }
@@ -322,7 +323,8 @@ class Pool:
     whose arena is a torch uint8 tensor owned by this object."""
 
     def __init__(self, num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
-                 initial_free_order=None, host_only=False, device="cuda", layer_kv_dtypes=None):
+                 initial_free_order=None, host_only=False, device="cuda", layer_kv_dtypes=None,
+                 seal_on_full=False):
         """layer_kv_dtypes: optional per-layer PKV_F16 / PKV_I8 (kv_dtype is then the
         default the automatic decode plan follows)."""
         self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
@@ -336,7 +338,9 @@ class Pool:
                      else np.ascontiguousarray(self.layer_kv_dtypes, dtype=np.int32))
         cfg = pkv_pool_config(num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
                               None if self._order is None else _np_ptr(self._order), None, 0,
-                              1 if host_only else 0, None if self._ldt is None else _np_ptr(self._ldt))
+                              1 if host_only else 0, None if self._ldt is None else _np_ptr(self._ldt),
+                              1 if seal_on_full else 0)
+        self.seal_on_full = bool(seal_on_full)
         self.arena = None
         if not host_only:
             import torch
@@ -425,6 +429,13 @@ class Pool:
             workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
         pkv_decode_step(self.h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
                         softmax_scale, out, workspace, partition_tokens, stream, flags)
+        return out
+
+    def read_tail_blocks(self, layer, blocks):
+        """FP16 staging tiles (seal_on_full pools): [n][2][Hkv][bs][d] binary16 bits."""
+        blocks = np.ascontiguousarray(blocks, dtype=np.int32)
+        out = np.zeros((len(blocks), 2, self.num_kv_heads, self.block_size, self.head_dim), dtype=np.uint16)
+        _check(lib().pkv_read_tail_blocks(self.h, layer, _np_ptr(blocks), len(blocks), _np_ptr(out)))
         return out
 
     def read_blocks(self, layer, blocks):
