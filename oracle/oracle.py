@@ -71,6 +71,8 @@ def lib():
             "orc_cache_read_block": (None, [vp, i32, i32, vp, vp]),
             "orc_decode_attention": (C.c_int, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                i32, vp, i32, vp, i32, f64, vp, i32]),
+            "orc_prefill_attention": (C.c_int, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                i32, vp, vp, i32, vp, i32, f64, vp, i32]),
             "orc_hardware_threads": (i32, []),
         }
         for name, (res, args) in sig.items():
@@ -263,6 +265,33 @@ def decode_attention(kv_dtype, k_codes, v_codes, k_scales, v_scales, q, table, l
                                     _p(out), threads)
     if st != OK:
         raise ValueError(f"oracle decode_attention rejected its arguments ({st})")
+    return out
+
+
+def prefill_attention(kv_dtype, k_codes, v_codes, k_scales, v_scales, q, query_start, table, lens,
+                      softmax_scale, threads=0):
+    """FP64 causal attention of each sequence's last q_len cached tokens
+    (query_start: [B+1] prefix offsets into q's rows) over its context.
+    q: [total][Hq][dim] binary32. Returns [total][Hq][dim] float64."""
+    want = {I8: np.int8, F16: np.uint16, VALUES: np.float64}[kv_dtype]
+    k_codes = np.ascontiguousarray(k_codes)
+    v_codes = np.ascontiguousarray(v_codes)
+    assert k_codes.dtype == want and v_codes.dtype == want
+    N, hkv, bs, dim = k_codes.shape
+    k_scales = np.ascontiguousarray(k_scales, dtype=np.float32)
+    v_scales = np.ascontiguousarray(v_scales, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    total, hq, _ = q.shape
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    assert qs[-1] == total
+    out = np.zeros((total, hq, dim), dtype=np.float64)
+    st = lib().orc_prefill_attention(kv_dtype, N, hkv, bs, dim, _p(k_codes), _p(v_codes), _p(k_scales),
+                                     _p(v_scales), _p(q), hq, _p(qs), _p(table), table.shape[1], _p(lens),
+                                     len(lens), float(softmax_scale), _p(out), threads)
+    if st != OK:
+        raise ValueError(f"oracle prefill_attention rejected its arguments ({st})")
     return out
 
 

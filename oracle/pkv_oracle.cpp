@@ -571,6 +571,60 @@ int orc_decode_attention(int32_t kv_dtype, int32_t nblocks, int32_t hkv, int32_t
   return ORC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Chunked prefill attention, FP64 ("轻量级推理引擎实战" §一: prefill handles the
+// prompt's tokens in parallel; the decode rule above, applied to every new
+// token at once). For sequence s the last qlen[s] = qstart[s+1] - qstart[s] of
+// its lens[s] cached tokens are queries: query i sits at position
+// p = lens[s] - qlen[s] + i and attends to positions 0..p (causal).
+// READING: the same scaled dot-product softmax as decode, one query at a time.
+// q: binary32 [total][Hq][dim]; out: FP64 [total][Hq][dim].
+// ---------------------------------------------------------------------------
+int orc_prefill_attention(int32_t kv_dtype, int32_t nblocks, int32_t hkv, int32_t bs, int32_t dim,
+                          const void* k_codes, const void* v_codes, const float* k_scales,
+                          const float* v_scales, const float* q, int32_t hq, const int32_t* qstart,
+                          const int32_t* table, int32_t max_blocks, const int32_t* lens, int32_t nseq,
+                          double softmax_scale, double* out, int32_t threads) {
+  if (hkv <= 0 || hq % hkv != 0 || bs <= 0 || dim <= 0 || qstart[0] != 0) return ORC_INVALID;
+  int64_t total = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    const int32_t ql = qstart[s + 1] - qstart[s];
+    if (ql < 1 || ql > lens[s] || lens[s] > (int64_t)max_blocks * bs) return ORC_INVALID;
+    for (int32_t j = 0; j < orc_num_blocks(lens[s], bs); ++j) {
+      const int32_t b = table[(size_t)s * max_blocks + j];
+      if (b < 0 || b >= nblocks) return ORC_INVALID;
+    }
+    total += ql;
+  }
+  // Query row r of sequence s is the decode of a sequence whose context ends
+  // at its position: run the decode rule with that length, one row at a time.
+  std::vector<int32_t> row_seq(total), row_len(total);
+  for (int32_t s = 0; s < nseq; ++s)
+    for (int32_t r = qstart[s]; r < qstart[s + 1]; ++r) {
+      row_seq[r] = s;
+      row_len[r] = lens[s] - (qstart[s + 1] - qstart[s]) + (r - qstart[s]) + 1;
+    }
+  const int64_t tasks = total * hq;
+  int32_t nt = threads > 0 ? threads : (int32_t)std::max(1u, std::thread::hardware_concurrency());
+  if (nt > tasks) nt = (int32_t)std::max<int64_t>(1, tasks);
+  std::vector<std::thread> pool;
+  for (int32_t w = 0; w < nt; ++w)
+    pool.emplace_back([&, w]() {
+      for (int64_t i = w; i < tasks; i += nt) {
+        const int64_t r = i / hq;
+        const int32_t h = (int32_t)(i % hq);
+        const int32_t s = row_seq[r];
+        // one sequence's view: its table row, this query's length, its query row
+        OrcAttnArgs a{kv_dtype, nblocks, hkv, bs, dim, k_codes, v_codes, k_scales, v_scales,
+                      q + (size_t)r * hq * dim, hq, table + (size_t)s * max_blocks, max_blocks,
+                      &row_len[r], 1, softmax_scale, out + (size_t)r * hq * dim};
+        orc_attend_one(a, 0, h);
+      }
+    });
+  for (auto& th : pool) th.join();
+  return ORC_OK;
+}
+
 int32_t orc_hardware_threads(void) { return (int32_t)std::thread::hardware_concurrency(); }
 
 }  // extern "C"
