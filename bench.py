@@ -117,7 +117,18 @@ SERVE_CONFIGS = {
                     max_model_len=1024, prefix=200, requests=1024, seed=62006),
 }
 
+# Chunked prefill ("轻量级推理引擎实战" §一), Qwen3-TTS talker shape, INT8 KV:
+# a 512-query chunk ending at context 8000, and whole 2048-token prompts.
+PREFILL_CONFIGS = {
+    "prefill512": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, B=4, ctx=8000, chunk=512, seed=62007),
+    "prefill2k": dict(layers=28, hq=16, hkv=8, dim=128, bs=16, B=4, ctx=2048, chunk=2048, seed=62008),
+}
+
 WORKLOAD_NAMES = {
+    "prefill512": ("qwen3-tts-talker chunked prefill: 28 layers, B=4, the last 512 of 8000 cached tokens as "
+                   "causal queries, 16q/8kv, d128, bs16, int8 kv"),
+    "prefill2k": ("qwen3-tts-talker prefill: 28 layers, B=4 whole 2048-token prompts as causal queries, "
+                  "16q/8kv, d128, bs16, int8 kv"),
     "serve16": ("continuous-batching serving: 32 layers, 32q/8kv, d128, bs16, int8 kv; 1024 queued requests, "
                 "each a shared 200-token system prompt + lognormal(mean 300) suffix, ended by EOS after "
                 "lognormal(mean 300) tokens or at max-model-len 1024; max batch 128; pkv_sched plans each step"),
@@ -357,15 +368,17 @@ def cpu_baseline(w: Workload, target_s: float):
 def main():
     args = parse()
     serve = args.config in SERVE_CONFIGS
+    prefill = args.config in PREFILL_CONFIGS
     if args.steps is None:
-        args.steps = 400 if serve else 40
+        args.steps = 400 if serve else 10 if prefill else 40
     if args.warmup is None:
-        args.warmup = 100 if serve else 50
+        args.warmup = 100 if serve else 2 if prefill else 50
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
-    if args.config not in CONFIGS and args.config not in SERVE_CONFIGS:
-        sys.exit(f"unknown --config {args.config}; choose from {sorted(CONFIGS) + sorted(SERVE_CONFIGS)}")
+    known = sorted(CONFIGS) + sorted(SERVE_CONFIGS) + sorted(PREFILL_CONFIGS)
+    if args.config not in known:
+        sys.exit(f"unknown --config {args.config}; choose from {known}")
     import torch
     from paged_kv_cache_62_amd import pkv
     pkv.lib()
@@ -383,10 +396,12 @@ def main():
         return
     stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
     with torch.cuda.stream(stream):
-        res = (run_serve if args.config in SERVE_CONFIGS else run)(args, stream)
+        res = (run_serve if args.config in SERVE_CONFIGS else
+               run_prefill if args.config in PREFILL_CONFIGS else run)(args, stream)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(res.pop("_workload"), args.cpu_seconds)
+        base = prefill_cpu_baseline if args.config in PREFILL_CONFIGS else cpu_baseline
+        res["cpu_baseline"] = base(res.pop("_workload"), args.cpu_seconds)
     else:
         res.pop("_workload")
     print(json.dumps(res), flush=True)
@@ -654,6 +669,130 @@ def run_serve(args, stream):
                      "timing": f"HIP events around {reps} replays of a graph of the {L} decode launches"},
     }
     res["_workload"] = _ServeView(pool, [int(x) for x in last["seqs"]], maxb, c, q, scale)
+    return res
+
+
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak
+
+
+class _PrefillView:
+    """What the prefill CPU baseline reads."""
+
+    def __init__(self, pool, c, q, qstart, table, lens, scale):
+        self.pool, self.c, self.q, self.qstart, self.table, self.lens, self.scale = pool, c, q, qstart, table, lens, scale
+
+
+def prefill_cpu_baseline(w, target_s):
+    """The FP64 prefill oracle on a bounded sample: one layer, sequences in
+    order until ~target_s of CPU time; tokens/s = query tokens / (layers x time)."""
+    from oracle import oracle as orc
+    from paged_kv_cache_62_amd import synth
+    c = w.c
+    threads = max(1, min(16, os.cpu_count() or 1))
+    blocks = sorted({int(b) for b in w.table.ravel() if b >= 0})
+    codes, scales = w.pool.read_blocks(0, blocks)
+    N = int(max(blocks)) + 1
+    kc = np.zeros((N, c["hkv"], c["bs"], c["dim"]), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.ones((N, c["hkv"]), np.float32)
+    vs = np.ones_like(ks)
+    kc[blocks], vc[blocks] = codes[:, 0], codes[:, 1]
+    ks[blocks], vs[blocks] = scales[:, 0], scales[:, 1]
+    q = synth.as_f32(w.q.cpu())
+    done_q, elapsed = 0, 0.0
+    for s in range(len(w.lens)):
+        a, b = int(w.qstart[s]), int(w.qstart[s + 1])
+        t0 = time.perf_counter()
+        orc.prefill_attention(orc.I8, kc, vc, ks, vs, q[a:b], np.array([0, b - a], np.int32), w.table[s:s + 1],
+                              w.lens[s:s + 1], w.scale, threads=threads)
+        elapsed += time.perf_counter() - t0
+        done_q += b - a
+        if elapsed >= target_s:
+            break
+    return {"value": done_q / (elapsed * c["layers"]), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"FP64 prefill oracle on layer 0 for {done_q} of {int(w.qstart[-1])} query tokens "
+                       f"({elapsed:.1f} s, {threads} threads) over the GPU cache read back; tokens/s = query "
+                       f"tokens / (layers x time), extrapolated from the sampled layer and sequences")}
+
+
+def run_prefill(args, stream):
+    """Chunked prefill: the cache holds B x ctx tokens (the chunk's K/V
+    included); a step is one pkv_prefill_attention per layer over the last
+    `chunk` tokens of every sequence, as a HIP graph replayed K times."""
+    import torch
+    from paged_kv_cache_62_amd import pkv, synth
+    c = PREFILL_CONFIGS[args.config]
+    print(f"# building prefill workload {args.config}", file=sys.stderr, flush=True)
+    L, hq, hkv, dim, bs, B, ctx, C = (c[k] for k in ("layers", "hq", "hkv", "dim", "bs", "B", "ctx", "chunk"))
+    dev = torch.device("cuda")
+    scale = 1.0 / math.sqrt(dim)
+    nblocks = B * ((ctx + bs - 1) // bs) + 8
+    order = synth.permutation(synth.stream_seed(c["seed"], 1), nblocks)
+    pool = pkv.Pool(L, hkv, dim, bs, nblocks, pkv.PKV_I8, initial_free_order=order)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c["seed"])
+    for s in range(B):
+        slots = torch.from_numpy(pool.allocate(s, ctx)).to(dev)
+        for layer in range(L):
+            k = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+            pool.append_kv(layer, k, v, slots, stream)
+    maxb = (ctx + bs - 1) // bs
+    table, lens = pool.block_table(list(range(B)), maxb)
+    d_table, d_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    qstart = np.arange(B + 1, dtype=np.int32) * C
+    d_qstart = torch.from_numpy(qstart).to(dev)
+    q = [torch.randn(B * C, hq, dim, generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
+    out = torch.empty(B * C, hq, dim, dtype=torch.float32, device=dev)
+
+    def step():
+        for layer in range(L):
+            pool.prefill(layer, q[layer], d_qstart, C, d_table, d_lens, scale, out=out, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    print(f"# warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    avg_dur_s = total_ms / 1e3 / (args.steps * L)
+    # algorithmic work per launch: every (query, head, visible token) pair costs
+    # 2*d flops for q.k and 2*d for p*v
+    pairs = sum(sum(ctx - C + i + 1 for i in range(C)) for _ in range(B)) * hq
+    flops = 4.0 * dim * pairs
+    achieved = flops / avg_dur_s / 1e12
+    res = {
+        "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": B * C * args.steps / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 kv, fp16 matrix-core products / fp32 accumulate",
+        "data": "synthetic (seeded K/V and queries), cache filled before timing",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": B, "query_tokens_per_seq": C,
+                   "context": ctx, "layers_per_step": L, "hip_graph": True},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_kernel (causal paged attention, fp16 matrix cores)",
+                     "avg_launch_us": avg_dur_s * 1e6, "flops_per_launch": flops,
+                     "timing": f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"},
+    }
+    res["_workload"] = _PrefillView(pool, c, q[0], qstart, table, lens, scale)
     return res
 
 

@@ -260,6 +260,30 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
                            float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked prefill attention over one layer ("轻量级推理引擎实战" §一: prefill
+ * processes a prompt's tokens in parallel, then decode adds one at a time).
+ * For sequence s the last q_len = query_start[s+1] - query_start[s] of its
+ * context_lens[s] cached tokens are queries (their K/V already appended with
+ * pkv_append_kv); query i sits at position p = context_lens[s] - q_len + i
+ * and attends causally to positions 0..p:
+ *   out[qs+i][h] = sum_{t<=p} softmax_t(softmax_scale * q[qs+i][h] . K[s,t]) V[s,t]
+ * with qs = query_start[s], K/V as in pkv_decode_attention. A whole-prompt
+ * prefill is q_len = context_len; q_len = 1 is a decode step.
+ *   q: [total][num_q_heads][head_dim] of q_dtype (F32, F16, BF16), rows packed
+ *     sequence after sequence; out: same shape, fp32.
+ *   query_start: [num_seqs+1] int32 (device), query_start[0] = 0, non-decreasing,
+ *     1 <= q_len <= context_lens[s]; max_query_len >= every q_len (sizes the grid).
+ *   block_tables, context_lens: as for pkv_decode_attention (device).
+ * The K/V operands go through fp16 matrix-core products (INT8 codes convert
+ * exactly), probabilities as fp16 hi + lo parts, fp32 accumulation.
+ * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4}, F16 and
+ * INT8 layers (not seal_on_full). */
+pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                 int32_t num_q_heads, const int32_t* query_start, int32_t max_query_len,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, float softmax_scale,
+                                 float* out, void* stream);
+
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as
  * uint16 for an F16 layer); scales_out (host, may be NULL; written for an

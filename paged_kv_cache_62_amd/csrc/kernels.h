@@ -79,6 +79,25 @@ struct DecodeLaunch {
   const void* v_new;
 };
 
+// Chunked prefill: the last q_len = query_start[s+1] - query_start[s] of
+// each sequence's lens[s] cached tokens are queries, attending causally.
+struct PrefillLaunch {
+  LayerView lv;
+  const void* q;              // [total][Hq][d] of q_dtype
+  int q_dtype;
+  int32_t num_q_heads;
+  const int32_t* query_start; // [num_seqs + 1]
+  int32_t max_query_len;
+  const int32_t* tables;
+  int32_t max_blocks;
+  const int32_t* lens;
+  int32_t num_seqs;
+  float softmax_scale;
+  float* out;                 // [total][Hq][d] fp32
+};
+
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+
 // Longest decode partition (tokens) the kernels take.
 constexpr int32_t kMaxPartitionTokens = 4096;
 

@@ -1297,6 +1297,235 @@ hipError_t launch_decode_g(const DecodeLaunch& d, int group, hipStream_t stream)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunked prefill ("轻量级推理引擎实战" §一: prefill handles a prompt's tokens in
+// parallel): each sequence's last q_len cached tokens are queries; query i
+// sits at position p = len - q_len + i and attends to positions 0..p.
+//
+// One wavefront per tile of 16 matrix-core columns = 16/G query tokens x the
+// G query heads of one KV head; four wavefronts (consecutive tiles of one
+// sequence and KV head) per workgroup, independent, sharing the K/V they
+// stream through the caches. Per 16-token unit of context:
+//   S^T[token][col] = K[token][:] . Q^T[:][col]        (fp16 products, fp32 sums;
+//                                                      INT8 K codes -> fp16 exactly)
+//   O^T[dim][col]  += V^T[dim][token] . P^T[token][col]  (P as fp16 hi + lo)
+// Lane (column n16, group gq) holds dims [gq*D/4, (gq+1)*D/4) of its column's
+// query and of its K row n16; matrix-core product c contracts elements
+// [8c, 8c+8) of every lane's range, on both sides. The query is scaled per
+// column by a power of two into fp16 (a lo part too for an fp32 query).
+// Scores are in base 2; each column keeps its own running max and sum.
+// ---------------------------------------------------------------------------
+template <bool I8, int D, int G, int QT>
+__global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
+  constexpr int TQ = 16 / G;                // query tokens per tile
+  constexpr int ESZ = I8 ? 1 : 2;
+  constexpr int NC = D / 4 * ESZ / 16;      // 16-byte chunks per lane per unit, K and V
+  constexpr int NK = D / 32;                // fp16 QK products per unit
+  constexpr int NDT = D / 16;               // 16-dim tiles of the PV product
+  constexpr int RB = D * ESZ;               // bytes per K row
+  constexpr int UB = kUnit * RB;            // bytes of one 16-token sub-tile
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, gq = lane >> 4;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int hq = a.num_q_heads, hkv = a.lv.num_kv_heads, bs = a.lv.block_size;
+  const int lupb = __builtin_ctz(bs / kUnit);
+  const int qs = a.query_start[s];
+  const int ql = min(a.query_start[s + 1] - qs, a.max_query_len);
+  const int len = min(a.lens[s], a.max_blocks * bs);
+  const int j0 = (blockIdx.x * 4 + wave) * TQ;  // first query of this tile
+  if (j0 >= ql || ql > len) return;             // wave-uniform; no barrier below
+
+  // this lane's column: query j0 + n16 / G, head n16 % G
+  const int qi = j0 + n16 / G, h = n16 % G;
+  const bool colv = qi < ql;
+  const int pos = colv ? len - ql + qi : -1;    // last position the column sees
+  const int p_last = len - ql + min(j0 + TQ, ql) - 1;
+  const int nunits = p_last / kUnit + 1;
+
+  // ---- query operand (B of QK): D/4 elements per lane, fp16 hi (+ lo)
+  constexpr int QE = D / 4;
+  float qv[QE];
+  const size_t qrow = ((size_t)(qs + (colv ? qi : 0)) * hq + g * G + h) * D + gq * QE;
+#pragma unroll
+  for (int e = 0; e < QE; ++e) qv[e] = colv ? load_elem<QT>(a.q, qrow + e) : 0.f;
+  float qm = 0.f;
+#pragma unroll
+  for (int e = 0; e < QE; ++e) qm = fmaxf(qm, fabsf(qv[e]));
+  qm = max_over_lane_groups(qm);                // the column's max |q|
+  int qexp;
+  frexpf(qm, &qexp);                            // qm < 2^qexp (0 for a zero column)
+  f16x8 qh[NK], ql8[NK];
+#pragma unroll
+  for (int c = 0; c < NK; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = ldexpf(qv[8 * c + e], 15 - qexp);
+      const _Float16 hi = (_Float16)y;
+      qh[c][e] = hi;
+      ql8[c][e] = (_Float16)(y - (float)hi);
+    }
+  }
+  const float qconst = ldexpf(a.softmax_scale * kLog2e, qexp - 15);
+
+  const int32_t* table = a.tables + (size_t)s * a.max_blocks;
+  const char* kcodes = (const char*)a.lv.k_codes;
+  const char* vcodes = (const char*)a.lv.v_codes;
+  const uint64_t tile_bytes = (uint64_t)bs * RB;
+  // Block-table entries 64 at a time, one per lane (tb0: blocks [b0, b0+64),
+  // tb1: the next 64, requested a batch ahead); units are loaded in order.
+  const int nbl = (p_last + bs) / bs;  // blocks the tile reads
+  auto batch = [&](int first) { return table[min(first + lane, nbl - 1)]; };
+  int b0 = 0;
+  int tb0 = batch(0), tb1 = batch(64);
+  // unit u: its K rows and V sub-tile, and (INT8) its block's scales
+  auto load_unit = [&](int u, uint4 (&kd)[NC], uint4 (&vd)[NC], float& ksc, float& vsc) {
+    const int bi = u >> lupb;
+    if (bi >= b0 + 64) {  // wave-uniform: move to the next batch, request the one after
+      b0 += 64;
+      tb0 = tb1;
+      tb1 = batch(b0 + 64);
+    }
+    const int blk = min(max(__builtin_amdgcn_readlane(tb0, bi - b0), 0), a.lv.num_blocks - 1);
+    const uint64_t sub = ((uint64_t)blk * hkv + g) * tile_bytes + (uint64_t)(u & ((1 << lupb) - 1)) * UB;
+    const char* kp = (const char*)uniform_ptr(kcodes + sub);
+    const char* vp = (const char*)uniform_ptr(vcodes + sub);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kd[c] = *(const uint4*)(kp + n16 * RB + gq * (QE * ESZ) + 16 * c);
+      vd[c] = *(const uint4*)(vp + lane * (QE * ESZ) + 16 * c);
+    }
+    if constexpr (I8) {
+      ksc = a.lv.k_scales[(size_t)blk * hkv + g];
+      vsc = a.lv.v_scales[(size_t)blk * hkv + g];
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 kc[NC], vc[NC], kn[NC], vn[NC];
+  float ksc = 1.f, vsc = 1.f, ksn = 1.f, vsn = 1.f;
+  load_unit(0, kc, vc, ksc, vsc);
+  for (int u = 0; u < nunits; ++u) {
+    if (u + 1 < nunits) load_unit(u + 1, kn, vn, ksn, vsn);  // wave-uniform
+    // K rows -> fp16 operands
+    f16x8 kf[NK];
+    if constexpr (I8) {
+      uint32_t w[4 * NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        w[4 * c] = kc[c].x; w[4 * c + 1] = kc[c].y; w[4 * c + 2] = kc[c].z; w[4 * c + 3] = kc[c].w;
+      }
+#pragma unroll
+      for (int c = 0; c < NK; ++c) {  // 8 codes = 2 words per product
+        const f16x4 x0 = biased_i8x4_to_f16x4(w[2 * c] ^ 0x80808080u);
+        const f16x4 x1 = biased_i8x4_to_f16x4(w[2 * c + 1] ^ 0x80808080u);
+        kf[c] = f16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NK; ++c) kf[c] = __builtin_bit_cast(f16x8, kc[c]);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NK; ++c) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], qh[c], acc, 0, 0, 0);
+      if constexpr (QT == kF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], ql8[c], acc, 0, 0, 0);
+    }
+    const float f = (I8 ? ksc : 1.f) * qconst;
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = u * kUnit + 4 * gq + i;
+      sc[i] = t <= pos ? acc[i] * f : -INFINITY;
+    }
+    // online softmax, per column
+    float um = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    um = max_over_lane_groups(um);
+    const float mn = fmaxf(m, um);
+    const float mref = mn == -INFINITY ? 0.f : mn;  // a column with nothing to see yet
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - mref);
+    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    m = mn;
+    // P (times the V scale) as fp16 hi + lo
+    f16x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = p[i] * (I8 ? vsc : 1.f);
+      const _Float16 hi = (_Float16)pv;
+      ph[i] = hi;
+      pl[i] = (_Float16)(pv - (float)hi);
+    }
+    uint32_t vw[4 * NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      vw[4 * c] = vc[c].x; vw[4 * c + 1] = vc[c].y; vw[4 * c + 2] = vc[c].z; vw[4 * c + 3] = vc[c].w;
+    }
+    const int nvalid = len - u * kUnit;  // rows of the unit inside the context
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f16x4 av;
+      if constexpr (I8) {
+        av = biased_i8x4_to_f16x4(vw[dt]);
+      } else {
+        av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
+        if (nvalid < kUnit) {  // rows past the context may hold any bits
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[j] = 4 * gq + j < nvalid ? av[j] : (_Float16)0.0f;
+        }
+      }
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ph, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pl, o[dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kc[c] = kn[c];
+      vc[c] = vn[c];
+    }
+    ksc = ksn;
+    vsc = vsn;
+  }
+  l = sum_over_lane_groups(l);
+  if (colv) {
+    float* dst = a.out + ((size_t)(qs + qi) * hq + g * G + h) * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[dt][i] * inv;
+  }
+}
+
+template <bool I8, int D, int G>
+hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
+  const int tiles = (p.max_query_len + 16 / G - 1) / (16 / G);
+  const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)p.lv.num_kv_heads, (unsigned)p.num_seqs);
+  switch (p.q_dtype) {
+    case kF32: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF32>), grid, dim3(256), 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF16>), grid, dim3(256), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kBF16>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool I8, int D>
+hipError_t launch_prefill_g(const PrefillLaunch& p, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_prefill_q<I8, D, 1>(p, stream);
+    case 2: return launch_prefill_q<I8, D, 2>(p, stream);
+    case 4: return launch_prefill_q<I8, D, 4>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
@@ -1331,6 +1560,15 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   else
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, d);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
+  if (p.num_seqs <= 0 || p.max_query_len <= 0) return hipSuccess;
+  const int group = p.num_q_heads / p.lv.num_kv_heads;
+  const bool i8 = p.lv.kv_dtype == kI8;
+  if (p.lv.head_dim == 128)
+    return i8 ? launch_prefill_g<true, 128>(p, group, stream) : launch_prefill_g<false, 128>(p, group, stream);
+  return i8 ? launch_prefill_g<true, 64>(p, group, stream) : launch_prefill_g<false, 64>(p, group, stream);
 }
 
 hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int in_dtype,

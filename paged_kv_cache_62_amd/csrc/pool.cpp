@@ -632,6 +632,49 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
                        partition_tokens, flags, out, workspace, workspace_bytes, stream);
 }
 
+pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                 int32_t num_q_heads, const int32_t* query_start, int32_t max_query_len,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, float softmax_scale,
+                                 float* out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "q_dtype must be F32, F16 or BF16");
+  if (num_q_heads < 1 || num_q_heads % c.num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                c.num_kv_heads);
+  if (!pkv::decode_supported(c.head_dim, num_q_heads / c.num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d with %d query heads per KV head", c.head_dim,
+                num_q_heads / c.num_kv_heads);
+  if (pool->tails && pool->tail_index[layer] >= 0)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_prefill_attention: layer %d quantizes on seal", layer);
+  if (num_seqs < 0 || max_query_len < 0 || max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d, max_query_len %d, max_blocks_per_seq %d", num_seqs,
+                max_query_len, max_blocks_per_seq);
+  if (num_seqs > 0 && (!q || !query_start || !block_tables || !context_lens || !out))
+    return fail(PKV_ERR_INVALID_ARG, "NULL q, query_start, block_tables, context_lens or out");
+  pkv::PrefillLaunch p{};
+  p.lv = pool->layer_view(layer);
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.num_q_heads = num_q_heads;
+  p.query_start = query_start;
+  p.max_query_len = max_query_len;
+  p.tables = block_tables;
+  p.max_blocks = max_blocks_per_seq;
+  p.lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.softmax_scale = softmax_scale;
+  p.out = out;
+  hipError_t e = pkv::launch_prefill(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
 pkv_status pkv_read_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
                            void* codes_out, float* scales_out) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");

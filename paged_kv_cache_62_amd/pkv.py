@@ -107,6 +107,8 @@ SIGNATURES = {
     "pkv_sched_step": (C.c_int, [_vp, _vp, _i32, _vp, _vp]),
     "pkv_sched_get_stats": (C.c_int, [_vp, _vp]),
     "pkv_read_tail_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp]),
+    "pkv_prefill_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _i32,
+                                        _f32, _vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
 }
@@ -429,6 +431,24 @@ class Pool:
             workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
         pkv_decode_step(self.h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
                         softmax_scale, out, workspace, partition_tokens, stream, flags)
+        return out
+
+    def prefill(self, layer, q, query_start, max_query_len, block_tables, context_lens, softmax_scale,
+                out=None, stream=None):
+        """Causal attention of each sequence's last q_len cached tokens (q rows packed by
+        sequence, query_start [B+1] int32 on the device) -- pkv_prefill_attention."""
+        import torch
+        for t in (q, query_start, block_tables, context_lens):
+            assert t.is_contiguous()
+        assert query_start.dtype == torch.int32 and block_tables.dtype == torch.int32
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        assert out.is_contiguous() and out.dtype == torch.float32 and out.shape == q.shape
+        _check(lib().pkv_prefill_attention(
+            self.h, layer, _vp(q.data_ptr()), _torch_dtype_code(q), int(q.shape[1]), _vp(query_start.data_ptr()),
+            int(max_query_len), _vp(block_tables.data_ptr()), int(block_tables.shape[1]),
+            _vp(context_lens.data_ptr()), int(context_lens.shape[0]), float(softmax_scale),
+            _vp(out.data_ptr()), _stream_ptr(stream)))
         return out
 
     def read_tail_blocks(self, layer, blocks):
