@@ -33,6 +33,10 @@
 
 #include "kernels.h"
 
+#ifndef PKV_PREFILL_TILES
+#define PKV_PREFILL_TILES 1
+#endif
+
 namespace pkv {
 namespace {
 
@@ -1315,15 +1319,16 @@ hipError_t launch_decode_g(const DecodeLaunch& d, int group, hipStream_t stream)
 // column by a power of two into fp16 (a lo part too for an fp32 query).
 // Scores are in base 2; each column keeps its own running max and sum.
 // ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT>
+template <bool I8, int D, int G, int QT, int NT>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
   constexpr int TQ = 16 / G;                // query tokens per tile
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int NC = D / 4 * ESZ / 16;      // 16-byte chunks per lane per unit, K and V
-  constexpr int NK = D / 32;                // fp16 QK products per unit
+  constexpr int NK = D / 32;                // fp16 QK products per unit and tile
   constexpr int NDT = D / 16;               // 16-dim tiles of the PV product
   constexpr int RB = D * ESZ;               // bytes per K row
   constexpr int UB = kUnit * RB;            // bytes of one 16-token sub-tile
+  constexpr int QE = D / 4;                 // query elements per lane and tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, gq = lane >> 4;
@@ -1333,40 +1338,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
   const int qs = a.query_start[s];
   const int ql = min(a.query_start[s + 1] - qs, a.max_query_len);
   const int len = min(a.lens[s], a.max_blocks * bs);
-  const int j0 = (blockIdx.x * 4 + wave) * TQ;  // first query of this tile
-  if (j0 >= ql || ql > len) return;             // wave-uniform; no barrier below
+  const int j0 = (blockIdx.x * 4 + wave) * NT * TQ;  // first query of this wavefront's tiles
+  if (j0 >= ql || ql > len) return;                  // wave-uniform; no barrier below
 
-  // this lane's column: query j0 + n16 / G, head n16 % G
-  const int qi = j0 + n16 / G, h = n16 % G;
-  const bool colv = qi < ql;
-  const int pos = colv ? len - ql + qi : -1;    // last position the column sees
-  const int p_last = len - ql + min(j0 + TQ, ql) - 1;
+  // the wavefront's NT tiles: lane column n16 of tile t is query j0 + t*TQ + n16/G, head n16 % G
+  const int h = n16 % G;
+  int qi[NT], pos[NT];
+  bool colv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    qi[t] = j0 + t * TQ + n16 / G;
+    colv[t] = qi[t] < ql;
+    pos[t] = colv[t] ? len - ql + qi[t] : -1;  // last position the column sees
+  }
+  const int p_last = len - ql + min(j0 + NT * TQ, ql) - 1;
   const int nunits = p_last / kUnit + 1;
 
-  // ---- query operand (B of QK): D/4 elements per lane, fp16 hi (+ lo)
-  constexpr int QE = D / 4;
-  float qv[QE];
-  const size_t qrow = ((size_t)(qs + (colv ? qi : 0)) * hq + g * G + h) * D + gq * QE;
+  // ---- query operands (B of QK), per tile: D/4 elements per lane, fp16 hi (+ lo)
+  f16x8 qh[NT][NK], ql8[NT][QT == kF32 ? NK : 1];
+  float qconst[NT];
 #pragma unroll
-  for (int e = 0; e < QE; ++e) qv[e] = colv ? load_elem<QT>(a.q, qrow + e) : 0.f;
-  float qm = 0.f;
+  for (int t = 0; t < NT; ++t) {
+    float qv[QE];
+    const size_t qrow = ((size_t)(qs + (colv[t] ? qi[t] : 0)) * hq + g * G + h) * D + gq * QE;
 #pragma unroll
-  for (int e = 0; e < QE; ++e) qm = fmaxf(qm, fabsf(qv[e]));
-  qm = max_over_lane_groups(qm);                // the column's max |q|
-  int qexp;
-  frexpf(qm, &qexp);                            // qm < 2^qexp (0 for a zero column)
-  f16x8 qh[NK], ql8[NK];
+    for (int e = 0; e < QE; ++e) qv[e] = colv[t] ? load_elem<QT>(a.q, qrow + e) : 0.f;
+    float qm = 0.f;
 #pragma unroll
-  for (int c = 0; c < NK; ++c) {
+    for (int e = 0; e < QE; ++e) qm = fmaxf(qm, fabsf(qv[e]));
+    qm = max_over_lane_groups(qm);  // the column's max |q|
+    int qexp;
+    frexpf(qm, &qexp);              // qm < 2^qexp (0 for a zero column)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float y = ldexpf(qv[8 * c + e], 15 - qexp);
-      const _Float16 hi = (_Float16)y;
-      qh[c][e] = hi;
-      ql8[c][e] = (_Float16)(y - (float)hi);
+    for (int c = 0; c < NK; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = ldexpf(qv[8 * c + e], 15 - qexp);
+        const _Float16 hi = (_Float16)y;
+        qh[t][c][e] = hi;
+        if constexpr (QT == kF32) ql8[t][c][e] = (_Float16)(y - (float)hi);
+      }
     }
+    qconst[t] = ldexpf(a.softmax_scale * kLog2e, qexp - 15);
   }
-  const float qconst = ldexpf(a.softmax_scale * kLog2e, qexp - 15);
 
   const int32_t* table = a.tables + (size_t)s * a.max_blocks;
   const char* kcodes = (const char*)a.lv.k_codes;
@@ -1374,7 +1388,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
   const uint64_t tile_bytes = (uint64_t)bs * RB;
   // Block-table entries 64 at a time, one per lane (tb0: blocks [b0, b0+64),
   // tb1: the next 64, requested a batch ahead); units are loaded in order.
-  const int nbl = (p_last + bs) / bs;  // blocks the tile reads
+  const int nbl = (p_last + bs) / bs;  // blocks the tiles read
   auto batch = [&](int first) { return table[min(first + lane, nbl - 1)]; };
   int b0 = 0;
   int tb0 = batch(0), tb1 = batch(64);
@@ -1401,16 +1415,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
     }
   };
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[NDT];
+  float m[NT], l[NT];
+  f32x4 o[NT][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   uint4 kc[NC], vc[NC], kn[NC], vn[NC];
   float ksc = 1.f, vsc = 1.f, ksn = 1.f, vsn = 1.f;
   load_unit(0, kc, vc, ksc, vsc);
   for (int u = 0; u < nunits; ++u) {
     if (u + 1 < nunits) load_unit(u + 1, kn, vn, ksn, vsn);  // wave-uniform
-    // K rows -> fp16 operands
+    // K rows -> fp16 operands, once for all tiles
     f16x8 kf[NK];
     if constexpr (I8) {
       uint32_t w[4 * NC];
@@ -1428,61 +1447,74 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
 #pragma unroll
       for (int c = 0; c < NK; ++c) kf[c] = __builtin_bit_cast(f16x8, kc[c]);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // V sub-tile -> fp16 operands, once for all tiles
+    f16x4 av[NDT];
+    {
+      uint32_t vw[4 * NC];
 #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], qh[c], acc, 0, 0, 0);
-      if constexpr (QT == kF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], ql8[c], acc, 0, 0, 0);
-    }
-    const float f = (I8 ? ksc : 1.f) * qconst;
-    float sc[4];
+      for (int c = 0; c < NC; ++c) {
+        vw[4 * c] = vc[c].x; vw[4 * c + 1] = vc[c].y; vw[4 * c + 2] = vc[c].z; vw[4 * c + 3] = vc[c].w;
+      }
+      const int nvalid = len - u * kUnit;  // rows of the unit inside the context
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = u * kUnit + 4 * gq + i;
-      sc[i] = t <= pos ? acc[i] * f : -INFINITY;
-    }
-    // online softmax, per column
-    float um = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    um = max_over_lane_groups(um);
-    const float mn = fmaxf(m, um);
-    const float mref = mn == -INFINITY ? 0.f : mn;  // a column with nothing to see yet
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
-    float p[4];
+      for (int dt = 0; dt < NDT; ++dt) {
+        if constexpr (I8) {
+          av[dt] = biased_i8x4_to_f16x4(vw[dt]);
+        } else {
+          av[dt] = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
+          if (nvalid < kUnit) {  // rows past the context may hold any bits
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - mref);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    m = mn;
-    // P (times the V scale) as fp16 hi + lo
-    f16x4 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = p[i] * (I8 ? vsc : 1.f);
-      const _Float16 hi = (_Float16)pv;
-      ph[i] = hi;
-      pl[i] = (_Float16)(pv - (float)hi);
-    }
-    uint32_t vw[4 * NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      vw[4 * c] = vc[c].x; vw[4 * c + 1] = vc[c].y; vw[4 * c + 2] = vc[c].z; vw[4 * c + 3] = vc[c].w;
-    }
-    const int nvalid = len - u * kUnit;  // rows of the unit inside the context
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      f16x4 av;
-      if constexpr (I8) {
-        av = biased_i8x4_to_f16x4(vw[dt]);
-      } else {
-        av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
-        if (nvalid < kUnit) {  // rows past the context may hold any bits
-#pragma unroll
-          for (int j = 0; j < 4; ++j) av[j] = 4 * gq + j < nvalid ? av[j] : (_Float16)0.0f;
+            for (int j = 0; j < 4; ++j) av[dt][j] = 4 * gq + j < nvalid ? av[dt][j] : (_Float16)0.0f;
+          }
         }
       }
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ph, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pl, o[dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (u * kUnit > len - ql + min(j0 + (t + 1) * TQ, ql) - 1) continue;  // the tile sees nothing here
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NK; ++c) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], qh[t][c], acc, 0, 0, 0);
+        if constexpr (QT == kF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c], ql8[t][c], acc, 0, 0, 0);
+      }
+      const float f = (I8 ? ksc : 1.f) * qconst[t];
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = u * kUnit + 4 * gq + i;
+        sc[i] = tok <= pos[t] ? acc[i] * f : -INFINITY;
+      }
+      // online softmax, per column
+      float um = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      um = max_over_lane_groups(um);
+      const float mn = fmaxf(m[t], um);
+      const float mref = mn == -INFINITY ? 0.f : mn;  // a column with nothing to see yet
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - mref);
+      if (mn > m[t]) {  // rescale only when some column's max grew (wave-uniform test)
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - mref);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+      }
+      m[t] = mn;
+      l[t] += (p[0] + p[1]) + (p[2] + p[3]);
+      // P (times the V scale) as fp16 hi + lo
+      f16x4 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = p[i] * (I8 ? vsc : 1.f);
+        const _Float16 hi = (_Float16)pv;
+        ph[i] = hi;
+        pl[i] = (_Float16)(pv - (float)hi);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[dt], ph, o[t][dt], 0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[dt], pl, o[t][dt], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -1492,25 +1524,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillLaunch a) {
     ksc = ksn;
     vsc = vsn;
   }
-  l = sum_over_lane_groups(l);
-  if (colv) {
-    float* dst = a.out + ((size_t)(qs + qi) * hq + g * G + h) * D;
-    const float inv = 1.f / l;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int t = 0; t < NT; ++t) {
+    const float lt = sum_over_lane_groups(l[t]);
+    if (colv[t]) {
+      float* dst = a.out + ((size_t)(qs + qi[t]) * hq + g * G + h) * D;
+      const float inv = 1.f / lt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[dt][i] * inv;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
+    }
   }
 }
 
+constexpr int kPrefillTiles = PKV_PREFILL_TILES;  // 16-column tiles per wavefront
+
 template <bool I8, int D, int G>
 hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
+  constexpr int NT = kPrefillTiles;
   const int tiles = (p.max_query_len + 16 / G - 1) / (16 / G);
-  const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)p.lv.num_kv_heads, (unsigned)p.num_seqs);
+  const dim3 grid((unsigned)((tiles + 4 * NT - 1) / (4 * NT)), (unsigned)p.lv.num_kv_heads, (unsigned)p.num_seqs);
   switch (p.q_dtype) {
-    case kF32: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF32>), grid, dim3(256), 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF16>), grid, dim3(256), 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kBF16>), grid, dim3(256), 0, stream, p); break;
+    case kF32: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF32, NT>), grid, dim3(256), 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF16, NT>), grid, dim3(256), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kBF16, NT>), grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
