@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 
 # rocprofv3 FETCH_SIZE + WRITE_SIZE summaries (scaled by a plain-copy reference)
 # per workload; used only while the kernel source still has the hash they record.
-TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md"}
+TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
+                    "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md"}
 
 
 def measured_traffic(config):
@@ -669,6 +670,7 @@ def run_serve(args, stream):
                      "timing": f"HIP events around {reps} replays of a graph of the {L} decode launches"},
     }
     res["_workload"] = _ServeView(pool, [int(x) for x in last["seqs"]], maxb, c, q, scale)
+    res["_workload"].sched = sched  # its requests hold the blocks the baseline reads
     return res
 
 
