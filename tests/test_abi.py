@@ -146,3 +146,15 @@ def test_required_bytes_per_layer_types():
     assert pkv.pkv_pool_required_bytes(cfg) == 0
     with pytest.raises(pkv.PkvError):
         pkv.Pool(2, 2, 64, 16, 8, pkv.PKV_I8, host_only=True, layer_kv_dtypes=[pkv.PKV_F16, 2])
+
+
+def test_graft_entry_build_calls_the_library_build(monkeypatch):
+    """__graft_entry__.build() reaches the package's build function (the stub
+    here stands in for the hipcc run) and then loads the library."""
+    import importlib
+    import paged_kv_cache_62_amd as pkg
+    calls = []
+    monkeypatch.setattr(pkg, "build", lambda *a, **k: calls.append(1))
+    entry = importlib.import_module("__graft_entry__")
+    entry.build()
+    assert calls == [1]
