@@ -3,7 +3,7 @@ FP64 oracle (orc_prefill_attention) over the GPU's own cache read back:
 causal attention of each sequence's last q_len cached tokens, within max-abs
 2e-3 and row max-rel 1e-2. Whole prompts, chunks at an offset, one-token
 chunks, ragged tiles; INT8 and FP16 layers; G 1/2/4; head_dim 64/128;
-block sizes 16/32/64; fp32/bf16/fp16 queries."""
+block sizes 16/32/64; fp32/bf16/fp16 queries; four- and eight-tile workgroups."""
 import numpy as np
 import pytest
 
@@ -87,3 +87,19 @@ def test_prefill_one_token_chunks_equal_decode(gpu):
         out = pool.prefill(layer, q, qstart, 1, torch.from_numpy(res["table"]).to(dev),
                            torch.from_numpy(res["lens"]).to(dev), c.shape.scale)
         H.assert_attention_close(out.cpu().numpy(), res["ref"][layer])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+def test_prefill_many_tiles(gpu, kv):
+    """Enough tiles (4 sequences x 8 KV heads, chunks of 530-600 queries with
+    G = 2) that the launch takes four-tile workgroups on a 256-CU device; the
+    small cases above take eight-tile ones."""
+    lens = [600, 620, 545, 700]
+    c = _case(kv, 16, 8, 128, 16, lens, 64300 + kv)
+    got, ref, ma, mr = _prefill(c, [600, 530, 545, 580], "bf16")
+    print(f"prefill many tiles kv={kv}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+    H.assert_attention_close(got, ref)
+    # P's hi + lo parts carry ~22 bits, so the error sits near 2e-5 here; a
+    # hi part rounded twice (once for the product, once for the lo
+    # subtraction) showed up as ~2.5e-3 on this case
+    assert ma < 2e-4, f"max abs error {ma:.3e}: P split lost precision"
