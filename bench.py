@@ -677,11 +677,45 @@ def run_serve(args, stream):
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak
 
 
-class _PrefillView:
-    """What the prefill CPU baseline reads."""
+class PrefillWorkload:
+    """The chunked-prefill workload PREFILL_CONFIGS[name]: B sequences of ctx
+    cached tokens (seeded bf16 K/V appended through pkv_append_kv, every layer)
+    and, per layer, queries for the last `chunk` tokens of each sequence.
+    `prefill(layer)` is the launch a benchmark step makes per layer."""
 
-    def __init__(self, pool, c, q, qstart, table, lens, scale):
-        self.pool, self.c, self.q, self.qstart, self.table, self.lens, self.scale = pool, c, q, qstart, table, lens, scale
+    def __init__(self, name, stream=None):
+        import torch
+        from paged_kv_cache_62_amd import pkv, synth
+        c = self.c = PREFILL_CONFIGS[name]
+        L, hq, hkv, dim, bs, B, ctx, C = (c[k] for k in ("layers", "hq", "hkv", "dim", "bs", "B", "ctx", "chunk"))
+        self.L, self.hq, self.hkv, self.dim, self.bs, self.B, self.ctx, self.C = L, hq, hkv, dim, bs, B, ctx, C
+        dev = torch.device("cuda")
+        self.stream = stream
+        self.scale = 1.0 / math.sqrt(dim)
+        self.nblocks = B * ((ctx + bs - 1) // bs) + 8
+        order = synth.permutation(synth.stream_seed(c["seed"], 1), self.nblocks)
+        self.pool = pkv.Pool(L, hkv, dim, bs, self.nblocks, pkv.PKV_I8, initial_free_order=order)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(c["seed"])
+        for s in range(B):
+            slots = torch.from_numpy(self.pool.allocate(s, ctx)).to(dev)
+            for layer in range(L):
+                k = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+                v = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
+                self.pool.append_kv(layer, k, v, slots, stream)
+        self.max_blocks = (ctx + bs - 1) // bs
+        self.table, self.lens = self.pool.block_table(list(range(B)), self.max_blocks)
+        self.d_table, self.d_lens = torch.from_numpy(self.table).to(dev), torch.from_numpy(self.lens).to(dev)
+        self.qstart = np.arange(B + 1, dtype=np.int32) * C
+        self.d_qstart = torch.from_numpy(self.qstart).to(dev)
+        self.qs = [torch.randn(B * C, hq, dim, generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
+        self.q = self.qs[0]  # what the CPU baseline reads
+        self.out = torch.empty(B * C, hq, dim, dtype=torch.float32, device=dev)
+
+    def prefill(self, layer):
+        self.pool.prefill(layer, self.qs[layer], self.d_qstart, self.C, self.d_table, self.d_lens, self.scale,
+                          out=self.out, stream=self.stream)
+        return self.out
 
 
 def prefill_cpu_baseline(w, target_s):
@@ -722,34 +756,14 @@ def run_prefill(args, stream):
     included); a step is one pkv_prefill_attention per layer over the last
     `chunk` tokens of every sequence, as a HIP graph replayed K times."""
     import torch
-    from paged_kv_cache_62_amd import pkv, synth
-    c = PREFILL_CONFIGS[args.config]
     print(f"# building prefill workload {args.config}", file=sys.stderr, flush=True)
-    L, hq, hkv, dim, bs, B, ctx, C = (c[k] for k in ("layers", "hq", "hkv", "dim", "bs", "B", "ctx", "chunk"))
-    dev = torch.device("cuda")
-    scale = 1.0 / math.sqrt(dim)
-    nblocks = B * ((ctx + bs - 1) // bs) + 8
-    order = synth.permutation(synth.stream_seed(c["seed"], 1), nblocks)
-    pool = pkv.Pool(L, hkv, dim, bs, nblocks, pkv.PKV_I8, initial_free_order=order)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(c["seed"])
-    for s in range(B):
-        slots = torch.from_numpy(pool.allocate(s, ctx)).to(dev)
-        for layer in range(L):
-            k = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
-            v = torch.randn(ctx, hkv, dim, generator=gen, device=dev).to(torch.bfloat16)
-            pool.append_kv(layer, k, v, slots, stream)
-    maxb = (ctx + bs - 1) // bs
-    table, lens = pool.block_table(list(range(B)), maxb)
-    d_table, d_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
-    qstart = np.arange(B + 1, dtype=np.int32) * C
-    d_qstart = torch.from_numpy(qstart).to(dev)
-    q = [torch.randn(B * C, hq, dim, generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
-    out = torch.empty(B * C, hq, dim, dtype=torch.float32, device=dev)
+    w = PrefillWorkload(args.config, stream)
+    c = w.c
+    L, hq, dim, B, ctx, C = w.L, w.hq, w.dim, w.B, w.ctx, w.C
 
     def step():
         for layer in range(L):
-            pool.prefill(layer, q[layer], d_qstart, C, d_table, d_lens, scale, out=out, stream=stream)
+            w.prefill(layer)
 
     step()
     torch.cuda.synchronize()
@@ -794,7 +808,7 @@ def run_prefill(args, stream):
                      "avg_launch_us": avg_dur_s * 1e6, "flops_per_launch": flops,
                      "timing": f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"},
     }
-    res["_workload"] = _PrefillView(pool, c, q[0], qstart, table, lens, scale)
+    res["_workload"] = w
     return res
 
 

@@ -1,4 +1,4 @@
-"""Parity at the benchmark's full sizes and launch configuration.
+"""Parity at the benchmark's full sizes and launch configuration (decode and chunked prefill).
 
 For every bench workload: build it exactly as bench.py does (seeded fill
 through pkv_append_kv), run one step (host slot/table update, then per layer
@@ -102,6 +102,44 @@ def test_full_size_step(gpu, cfg):
             got = out.cpu().numpy()[sample]
             max_abs, max_rel = H.attention_errors(got, ref)
             print(f"[fullsize] {cfg} layer {l} seqs {sample}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
+                  flush=True)
+            H.assert_attention_close(got, ref)
+        w.pool.close()
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", ["prefill512", "prefill2k"])
+def test_full_size_prefill(gpu, cfg):
+    """The chunked-prefill workloads as bench.py builds and launches them
+    (bench.PrefillWorkload, every layer filled); sampled query rows of two
+    sequences, all heads, in the first and last layer, against the FP64
+    oracle over the GPU's read-back cache. A query at position p is the
+    decode of its row over tokens 0..p (pinned in test_prefill_oracle)."""
+    import torch
+    import bench
+    print(f"[fullsize] building {cfg}", flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        w = bench.PrefillWorkload(cfg, stream)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(11)
+        seqs = sorted(rng.choice(w.B, size=2, replace=False).tolist())
+        picks = sorted({0, 1, w.C // 2, w.C - 2, w.C - 1, *rng.integers(0, w.C, 3).tolist()})
+        rows = [(s, i) for s in seqs for i in picks]
+        shape = H.Shape(layers=w.L, hq=w.hq, hkv=w.hkv, dim=w.dim, bs=w.bs, nblocks=w.nblocks, kv_dtype=orc.I8)
+        blocks = sorted({int(b) for s in seqs for b in w.table[s, :w.max_blocks]})
+        for layer in (0, w.L - 1):
+            out = w.prefill(layer)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()[[w.qstart[s] + i for s, i in rows]]
+            kc, vc, ks, vs = H.gpu_layer_arrays(w.pool, layer, blocks, shape)
+            q = synth.as_f32(w.qs[layer].cpu())[[w.qstart[s] + i for s, i in rows]]
+            lens = np.array([w.lens[s] - w.C + i + 1 for s, i in rows], np.int32)
+            ref = orc.decode_attention(orc.I8, kc, vc, ks, vs, q, w.table[[s for s, _ in rows]], lens, w.scale)
+            max_abs, max_rel = H.attention_errors(got, ref)
+            print(f"[fullsize] {cfg} layer {layer} rows {len(rows)}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
                   flush=True)
             H.assert_attention_close(got, ref)
         w.pool.close()
