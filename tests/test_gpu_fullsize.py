@@ -21,17 +21,17 @@ from tests import harness as H
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["qwen", "llama29", "llama128", "mix16", "mix32", "long_i8", "long_f16"]
+CONFIGS = ["qwen", "qwen_mixed", "llama29", "llama128", "mix16", "mix32", "long_i8", "long_f16"]
 
 
-def _kv_code(w):
+def _kv_code(w, layer):
     from paged_kv_cache_62_amd import pkv
-    return orc.I8 if w.kv_code == pkv.PKV_I8 else orc.F16
+    return orc.I8 if w.layer_kv[layer] == pkv.PKV_I8 else orc.F16
 
 
 def _expected_after_append(w, layer, before_codes, before_scales, blocks, slots, knew, vnew):
     """Oracle: apply this step's tokens to the pre-step blocks."""
-    bs, kvd = w.bs, _kv_code(w)
+    bs, kvd = w.bs, _kv_code(w, layer)
     exp_codes, exp_scales = before_codes.copy(), before_scales.copy()
     bidx = {b: i for i, b in enumerate(blocks)}
     for t, slot in enumerate(slots):  # one token per sequence: each is its own run
@@ -62,7 +62,7 @@ def test_full_size_step(gpu, cfg):
         w.host_prep()  # this step's slots and tables, uploaded
         slots = w.d_slots.cpu().numpy()
         blocks = sorted({int(s) // bs for s in slots})
-        layers_checked = [0, w.L - 1]
+        layers_checked = sorted({0, w.L // 2, w.L - 1})  # both element types of a mixed pool
         before = {l: w.pool.read_blocks(l, blocks) for l in layers_checked}
         w.device_step(list(w.decode_layers(0)))
         torch.cuda.synchronize()
@@ -75,7 +75,7 @@ def test_full_size_step(gpu, cfg):
                 rows = max(int(s) % bs for s in slots if int(s) // bs == b) + 1
                 np.testing.assert_array_equal(got_c[i][:, :, :rows], exp_c[i][:, :, :rows],
                                               err_msg=f"{cfg} layer {l} block {b} codes")
-                if _kv_code(w) == orc.I8:
+                if _kv_code(w, l) == orc.I8:
                     np.testing.assert_array_equal(got_s[i].view(np.uint32), exp_s[i].view(np.uint32),
                                                   err_msg=f"{cfg} layer {l} block {b} scales")
         print(f"[fullsize] {cfg}: append bit-exact on {len(blocks)} blocks x {len(layers_checked)} layers",
@@ -95,10 +95,10 @@ def test_full_size_step(gpu, cfg):
             torch.cuda.synchronize()
             sub_blocks = sorted({int(b) for s in sample for b in table[s, :(int(lens[s]) + bs - 1) // bs]})
             shape = H.Shape(layers=w.L, hq=w.hq, hkv=w.hkv, dim=w.dim, bs=bs, nblocks=w.nblocks,
-                            kv_dtype=_kv_code(w))
+                            kv_dtype=_kv_code(w, l))
             kc, vc, ks, vs = H.gpu_layer_arrays(w.pool, l, sub_blocks, shape)
             q = synth.as_f32(w.q[l].cpu())[sample]
-            ref = orc.decode_attention(_kv_code(w), kc, vc, ks, vs, q, table[sample], lens[sample], w.scale)
+            ref = orc.decode_attention(_kv_code(w, l), kc, vc, ks, vs, q, table[sample], lens[sample], w.scale)
             got = out.cpu().numpy()[sample]
             max_abs, max_rel = H.attention_errors(got, ref)
             print(f"[fullsize] {cfg} layer {l} seqs {sample}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
