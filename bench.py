@@ -172,8 +172,7 @@ class Workload:
         self.partition = partition or c.get("partition", 0)
         self.flags = flags
         # one pkv_decode_step launch per decoded layer instead of append + decode
-        # (not for a seal-on-full cache, which pkv_decode_step does not take)
-        self.fused = fused and not c.get("seal")
+        self.fused = fused
         self.scale = 1.0 / math.sqrt(self.dim)
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
         seed = c["seed"]

@@ -251,6 +251,10 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pk
  *   Precondition: that block is not shared (pkv_seq_append_slots gave the
  *     position, copying a shared block first). A table entry outside the
  *     pool is not written.
+ *   On an INT8 layer of a seal_on_full pool the new row is staged as
+ *     binary16 and, when it fills its block, the block is sealed (codes,
+ *     scales), both exactly as pkv_append_kv does; the decode then reads
+ *     the block as the following pkv_decode_attention would.
  * All other arguments, the workspace and the flags are as for
  * pkv_decode_attention. */
 pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const void* k_new,

@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, co
 // ---------------------------------------------------------------------------
 template <bool I8, int D, int G, int QT, bool APPEND, bool SEAL>
 __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
-  static_assert(!SEAL || (I8 && !APPEND), "seal-on-full: INT8 decode without append");
+  static_assert(!SEAL || I8, "seal-on-full: INT8 layers");
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int RB = D * ESZ;       // bytes per K row
   constexpr int NCH = RB / 64;      // 16-byte chunks per lane per unit (K, and V)
@@ -603,12 +603,19 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
                  (nrem > 0 && (nblk_full & (kWaves - 1)) == wave ? nrem : 0);
   // Seal-on-full cache: a partly filled last block of the sequence is still
   // in FP16 (its staging tiles); the wavefront that holds it reads its units
-  // (its last ntail units) after the loop, from there.
+  // (its last ntail units) after the loop, from there. In a decode step the
+  // last block also takes the new token: if that fills it, it is sealed in
+  // this launch, and the same wavefront takes the whole block after the loop.
   int ntail = 0;
   if constexpr (SEAL) {
     const int r = len & (bs - 1);
     const int nbl = ((len - 1) >> (lupb + 4)) - (u0 >> lupb);  // the last block within the partition
-    if (r > 0 && t1 == len && (nbl & (kWaves - 1)) == wave) ntail = (r + kUnit - 1) / kUnit;
+    // (a partition past the sequence's end, t0 >= len, also has t1 == len
+    // but holds none of its blocks)
+    if (t0 < len && t1 == len && (nbl & (kWaves - 1)) == wave) {
+      if (r > 0) ntail = (r + kUnit - 1) / kUnit;
+      else if (APPEND) ntail = bs / kUnit;
+    }
   }
   const int nu8 = nu - ntail;  // units read through the ring
 
@@ -679,7 +686,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int nb_rel = (pos >> (lupb + 4)) - (u0 >> lupb);  // the new token's block within the partition
   const int i_new = (nb_rel >> 2) << lupb;  // owner: its unit index of that block's first unit
   const int row0 = pos & (bs - 1);          // the new token's row in its block
-  bool owner = APPEND && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
+  bool owner = APPEND && !SEAL && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
   int a_entry = 0;
   constexpr int NPL = D / 64;  // new-row elements per lane: dims lane + 64*k
   float nk[NPL], nv[NPL];
@@ -709,6 +716,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   gather_scales();
 #pragma unroll
   for (int b = 0; b < NB; ++b) issue(b, nu8, kb[b], vb[b]);
+
 
   // ---- the query as the B operand of the QK product (Q^T: dims x columns),
   // built once per workgroup in LDS. Column n16 carries head hc, part pc:
@@ -1068,6 +1076,114 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   };
 
+  // Decode step on a seal-on-full layer, by the owner of the sequence's last
+  // block, before the loop: the block's staged rows and the new token's row (binary16, as
+  // pkv_append_kv stages it) go to wave-private LDS. If the new row leaves
+  // the block partly filled, it is also staged in memory; if it fills the
+  // block, the block is sealed as the append does it (scale = max|x| / 127
+  // per K and V, codes, largest |code|).
+  constexpr int kMaxBs = 64;
+  __shared__ __align__(16) uint16_t sm_tail[SEAL && APPEND ? 2 : 1][SEAL && APPEND ? kMaxBs * D : 8];
+  float seal_sk = 1.f, seal_sv = 1.f;  // scales of a block sealed in this launch
+  const int seal_row = (len - 1) & (bs - 1);  // the new token's row in its block
+  auto seal_step_stage = [&]() {
+    const int blk = min(max(__builtin_amdgcn_readlane(tentry, nu - 1), 0), a.lv.num_blocks - 1);
+    const size_t toff = ((size_t)blk * hkv + g) * bs * D;
+    uint16_t* tk = (uint16_t*)a.lv.tail_k + toff;
+    uint16_t* tv = (uint16_t*)a.lv.tail_v + toff;
+    // rows [0, 16 * ntail) of both tiles are prefixes of the tiles
+    const int nchunk = ntail * kUnit * D * 2 / 16;  // 16-byte chunks per tile
+    for (int c = lane; c < nchunk; c += 64) {
+      ((uint4*)sm_tail[0])[c] = ((const uint4*)tk)[c];
+      ((uint4*)sm_tail[1])[c] = ((const uint4*)tv)[c];
+    }
+    const size_t rowbase = ((size_t)s * hkv + g) * D;
+    for (int dd = lane; dd < D; dd += 64) {
+      const uint16_t hk = __builtin_bit_cast(uint16_t, (_Float16)load_elem<QT>(a.k_new, rowbase + dd));
+      const uint16_t hv = __builtin_bit_cast(uint16_t, (_Float16)load_elem<QT>(a.v_new, rowbase + dd));
+      sm_tail[0][k_tile_offset(seal_row, dd, D)] = hk;
+      sm_tail[1][v_tile_offset(seal_row, dd, D)] = hv;
+      if (seal_row < bs - 1) {
+        tk[k_tile_offset(seal_row, dd, D)] = hk;
+        tv[v_tile_offset(seal_row, dd, D)] = hv;
+      }
+    }
+    if (seal_row < bs - 1) return;
+    // seal: per K and V, the scale from the block's largest |x|
+    float mk = 0.f, mv = 0.f;
+    for (int e = lane; e < bs * D; e += 64) {
+      mk = fmaxf(mk, fabsf(f16_to_f32(sm_tail[0][e])));
+      mv = fmaxf(mv, fabsf(f16_to_f32(sm_tail[1][e])));
+    }
+    seal_sk = scale_of(wave_max(mk));
+    seal_sv = scale_of(wave_max(mv));
+    int8_t* ck = (int8_t*)a.lv.k_codes + toff;
+    int8_t* cv = (int8_t*)a.lv.v_codes + toff;
+    int qk = 0, qv = 0;
+    for (int e = lane; e < bs * D; e += 64) {  // element e of each tile, in its layout
+      const int8_t xk = encode(f16_to_f32(sm_tail[0][e]), seal_sk);
+      const int8_t xv = encode(f16_to_f32(sm_tail[1][e]), seal_sv);
+      qk = max(qk, abs((int)xk));
+      qv = max(qv, abs((int)xv));
+      ck[e] = xk;
+      cv[e] = (int8_t)(xv ^ (int8_t)0x80);  // V codes are stored biased by 128
+    }
+    qk = wave_max_int(qk);
+    qv = wave_max_int(qv);
+    if (lane == 0) {
+      const size_t at = (size_t)blk * hkv + g;
+      a.lv.k_scales[at] = seal_sk;
+      a.lv.v_scales[at] = seal_sv;
+      a.lv.k_qmax[at] = qk;
+      a.lv.v_qmax[at] = qv;
+    }
+  };
+  if constexpr (SEAL && APPEND) {
+    if (ntail > 0) seal_step_stage();  // wave-uniform
+  }
+
+  // Decode step on a seal-on-full layer, after the loop: the last block's
+  // units, staged in LDS before the loop, in the order a decode of the
+  // appended cache takes them: as FP16, or from the codes of a block sealed
+  // in this launch.
+  auto seal_step_decode = [&]() {
+    if (seal_row < bs - 1) {
+      for (int j = 0; j < ntail; ++j) {
+        uint4 kr[NCH16], vr[NCH16];
+#pragma unroll
+        for (int c = 0; c < NCH16; ++c) {
+          kr[c] = *(const uint4*)((const char*)sm_tail[0] + (size_t)(kUnit * j + n16) * D * 2 + 16 * gq + 64 * c);
+          vr[c] = *(const uint4*)((const char*)sm_tail[1] + (size_t)j * kUnit * D * 2 + lane * (16 * NCH16) + 16 * c);
+        }
+        process(std::true_type{}, kr, vr, 1.f, 1.f, unit_of(nu8 + j) * kUnit);
+      }
+      return;
+    }
+    // the sealed block's units as INT8, in the ring's register layout
+    for (int j = 0; j < ntail; ++j) {
+      uint4 kd[NCH], vd[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        uint32_t kw[4], vw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x = 0, y = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int dk = 16 * gq + 64 * c + 4 * w + b;  // K row kUnit * j + n16, this dim
+            const int ve = j * kUnit * D + lane * (16 * NCH) + 16 * c + 4 * w + b;  // V element
+            x |= (uint32_t)(uint8_t)encode(f16_to_f32(sm_tail[0][(kUnit * j + n16) * D + dk]), seal_sk) << (8 * b);
+            y |= (uint32_t)(uint8_t)(encode(f16_to_f32(sm_tail[1][ve]), seal_sv) ^ (int8_t)0x80) << (8 * b);
+          }
+          kw[w] = x;
+          vw[w] = y;
+        }
+        kd[c] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        vd[c] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+      }
+      process(std::false_type{}, kd, vd, seal_sk, seal_sv, unit_of(nu8 + j) * kUnit);
+    }
+  };
   // The scales reach the loop through a register move the compiler cannot
   // see into: it waits once for their loads here, and the loop's readlanes
   // then carry no wait. (Otherwise, where the scales' registers were
@@ -1108,7 +1224,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   }
 
-  if constexpr (APPEND && I8) {  // the new token's block: its scales and largest codes
+  if constexpr (APPEND && I8 && !SEAL) {  // the new token's block: its scales and largest codes
     if (owner && lane == 0) {
       const size_t at = (size_t)a_entry * hkv + g;
       a.lv.k_scales[at] = sk_new;
@@ -1118,7 +1234,9 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   }
 
-  if constexpr (SEAL) {
+  if constexpr (SEAL && APPEND) {
+    if (ntail > 0) seal_step_decode();
+  } else if constexpr (SEAL) {
     if (ntail > 0) {  // wave-uniform: the FP16 tail, after the INT8 units
       const int blk = min(max(__builtin_amdgcn_readlane(tentry, nu - 1), 0), a.lv.num_blocks - 1);
       const size_t tile16 = (size_t)bs * D * 2;
@@ -1295,7 +1413,9 @@ void launch_one(const DecodeLaunch& d, hipStream_t stream) {
   const dim3 grid(d.max_partitions, d.lv.num_kv_heads, d.num_seqs);
   const bool step = d.k_new != nullptr;
   if constexpr (I8) {
-    if (step)
+    if (step && d.lv.seal)
+      hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true, true>), grid, dim3(kThreads), 0, stream, d);
+    else if (step)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true>), grid, dim3(kThreads), 0, stream, d);
     else if (d.lv.seal)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, false, true>), grid, dim3(kThreads), 0, stream, d);

@@ -624,9 +624,6 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
                            float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL k_new or v_new");
-  if (pool && pool->tails && layer >= 0 && layer < pool->cfg.num_layers && pool->tail_index[layer] >= 0)
-    return fail(PKV_ERR_UNSUPPORTED, "pkv_decode_step: layer %d quantizes on seal; use pkv_append_kv + "
-                "pkv_decode_attention", layer);
   return decode_launch(pool, layer, q, dtype, num_q_heads, k_new, v_new, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len, softmax_scale,
                        partition_tokens, flags, out, workspace, workspace_bytes, stream);

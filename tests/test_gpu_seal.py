@@ -143,12 +143,98 @@ def test_seal_on_full_copy_on_write_and_mixed_layers(gpu):
     print(f"seal cow mixed: max_abs={worst[0]:.3e} max_rel={worst[1]:.3e}", flush=True)
 
 
-def test_decode_step_rejects_seal_layers(gpu):
+def _step_pair(sh, seed, lens, steps, forks=(), layer_kv=None, T=0, flags=0):
+    """Two seal-on-full pools built from the same script; each step appends one
+    token to every sequence, on one pool by pkv_append_kv + pkv_decode_attention,
+    on the other by pkv_decode_step. Outputs must be identical bits at every
+    step, and both caches (codes, scales, staged rows) identical at the end."""
     import torch
-    pool = pkv.Pool(1, 2, 64, 16, 8, pkv.PKV_I8, seal_on_full=True)
-    pool.allocate(0, 3)
-    q = torch.zeros(1, 2, 64, device="cuda")
-    with pytest.raises(pkv.PkvError) as e:
-        pool.decode_step(0, q, q[:, :2], q[:, :2], torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
-                         torch.full((1,), 3, dtype=torch.int32, device="cuda"), 3, 0.125)
-    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+    dev = torch.device("cuda")
+    pools = [pkv.Pool(sh.layers, sh.hkv, sh.dim, sh.bs, sh.nblocks, pkv.PKV_I8,
+                      initial_free_order=H.free_order(sh, seed), layer_kv_dtypes=layer_kv, seal_on_full=True)
+             for _ in range(2)]
+    sig = H.sigmas(sh, seed)
+    op = 0
+    for s, n in enumerate(lens):
+        slots = [p.allocate(s, n) for p in pools]
+        np.testing.assert_array_equal(slots[0], slots[1])
+        d_slots = torch.from_numpy(np.ascontiguousarray(slots[0], dtype=np.int64)).to(dev)
+        for layer in range(sh.layers):
+            k, v = H.kv_values(sh, seed, op, layer, len(slots[0]), sig)
+            for p in pools:
+                p.append_kv(layer, k.to(dev), v.to(dev), d_slots)
+        op += 1
+    seqs = list(range(len(lens)))
+    for p_, c_ in forks:
+        for p in pools:
+            p.fork(p_, c_)
+        seqs.append(c_)
+    worst = 0.0
+    for step in range(steps):
+        slots = [p.append_slots(seqs, [1] * len(seqs)) for p in pools]
+        np.testing.assert_array_equal(slots[0], slots[1])
+        d_slots = torch.from_numpy(np.ascontiguousarray(slots[0], dtype=np.int64)).to(dev)
+        maxb = max((int(pools[0].length(s)) + sh.bs - 1) // sh.bs for s in seqs)
+        table, lens_now = pools[0].block_table(seqs, maxb)
+        t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens_now).to(dev)
+        q = H.q_values(sh, seed + step, len(seqs)).to(dev)
+        for layer in range(sh.layers):
+            k, v = H.kv_values(sh, seed, op, layer, len(seqs), sig)
+            k, v = k.to(dev).to(q.dtype), v.to(dev).to(q.dtype)
+            pools[0].append_kv(layer, k, v, d_slots)
+            ref = pools[0].decode(layer, q, t_table, t_lens, int(lens_now.max()), sh.scale, partition_tokens=T,
+                                  flags=flags)
+            got = pools[1].decode_step(layer, q, k, v, t_table, t_lens, int(lens_now.max()), sh.scale,
+                                       partition_tokens=T, flags=flags)
+            torch.cuda.synchronize()
+            a_, b_ = ref.cpu().numpy(), got.cpu().numpy()
+            np.testing.assert_array_equal(b_.view(np.uint32), a_.view(np.uint32),
+                                          err_msg=f"step {step} layer {layer}: decode step differs")
+        op += 1
+    maxb = max((int(pools[0].length(s)) + sh.bs - 1) // sh.bs for s in seqs)
+    table, lens_now = pools[0].block_table(seqs, maxb)
+    rows = {}  # rows in use per block (the pool's memory is not cleared: only these are defined)
+    for s in range(len(seqs)):
+        n = int(lens_now[s])
+        for j in range((n + sh.bs - 1) // sh.bs):
+            b = int(table[s, j])
+            rows[b] = max(rows.get(b, 0), min(sh.bs, n - j * sh.bs))
+    blocks = sorted(rows)
+    for layer in range(sh.layers):
+        i8 = (layer_kv or [pkv.PKV_I8] * sh.layers)[layer] == pkv.PKV_I8
+        ca, sa_ = pools[0].read_blocks(layer, blocks)
+        cb, sb_ = pools[1].read_blocks(layer, blocks)
+        ta, tb = (pools[0].read_tail_blocks(layer, blocks), pools[1].read_tail_blocks(layer, blocks)) if i8 else (None, None)
+        for i, b in enumerate(blocks):
+            r = rows[b]
+            if not i8:  # binary16 rows
+                np.testing.assert_array_equal(cb[i][:, :, :r], ca[i][:, :, :r], err_msg=f"layer {layer} block {b}")
+            elif r == sh.bs:  # sealed: codes and scales
+                np.testing.assert_array_equal(cb[i], ca[i], err_msg=f"layer {layer} block {b} codes")
+                np.testing.assert_array_equal(sb_[i].view(np.uint32), sa_[i].view(np.uint32),
+                                              err_msg=f"layer {layer} block {b} scales")
+            else:  # partly filled: the staged rows
+                np.testing.assert_array_equal(tb[i, :, :, :r], ta[i, :, :, :r],
+                                              err_msg=f"layer {layer} block {b} staged rows")
+    for p in pools:
+        p.close()
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("group", [1, 2, 4])
+def test_decode_step_seal_matches_append_then_decode(gpu, bs, group):
+    """pkv_decode_step on seal-on-full layers: blocks staged, filled and sealed
+    across the steps, identical to pkv_append_kv + pkv_decode_attention."""
+    sh = H.Shape(layers=2, hq=2 * group, hkv=2, dim=128, bs=bs, nblocks=80, kv_dtype=orc.I8, in_dtype="bf16",
+                 q_dtype="bf16", free_order_seed=8, sigma_kv="per_head", outlier_p=0.01)
+    _step_pair(sh, 63400 + bs + group, [1, bs - 2, 2 * bs, 5 * bs + 3, 300], steps=bs + 3)
+
+
+@pytest.mark.parametrize("T", [16, 64, 0])
+def test_decode_step_seal_partitions_forks_mixed(gpu, T):
+    """Forked sequences (copy-on-write of staged rows), head_dim 64, fp32
+    rows, FP16 first and last layers beside sealed INT8 layers."""
+    sh = H.Shape(layers=4, hq=4, hkv=2, dim=64, bs=16, nblocks=96, kv_dtype=orc.I8, in_dtype="f32",
+                 q_dtype="f32", free_order_seed=9, sigma_kv="per_head")
+    _step_pair(sh, 63500 + T, [1, 15, 16, 200, 37], steps=20, forks=[(3, 5), (3, 6), (4, 7)], T=T,
+               layer_kv=[pkv.PKV_F16, pkv.PKV_I8, pkv.PKV_I8, pkv.PKV_F16])
