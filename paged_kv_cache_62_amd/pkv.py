@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 
@@ -353,9 +354,12 @@ class Pool:
             cfg.device_arena = _vp(self.arena.data_ptr())
             cfg.arena_bytes = nbytes
         self.h = pkv_pool_create(cfg)
+        self._scheds = weakref.WeakSet()  # schedulers over this pool: closed before it
 
     def close(self):
         if getattr(self, "h", None):
+            for sched in list(getattr(self, "_scheds", ())):
+                sched.close()  # it frees its running sequences' blocks through the pool
             pkv_pool_destroy(self.h)
             self.h = None
 
@@ -480,6 +484,7 @@ class Scheduler:
         h = _vp()
         _check(lib().pkv_sched_create(pool.h, C.byref(cfg), C.byref(h)))
         self.h = h
+        pool._scheds.add(self)
 
     def close(self):
         if getattr(self, "h", None):

@@ -29,16 +29,15 @@ def _kv_code(w, layer):
     return orc.I8 if w.layer_kv[layer] == pkv.PKV_I8 else orc.F16
 
 
-def _expected_after_append(w, layer, before_codes, before_scales, blocks, slots, knew, vnew):
-    """Oracle: apply this step's tokens to the pre-step blocks."""
-    bs, kvd = w.bs, _kv_code(w, layer)
+def _expected_after_append(bs, hkv, kvd, before_codes, before_scales, blocks, slots, knew, vnew):
+    """Oracle: apply this step's tokens (one per sequence) to the pre-step blocks."""
     exp_codes, exp_scales = before_codes.copy(), before_scales.copy()
     bidx = {b: i for i, b in enumerate(blocks)}
     for t, slot in enumerate(slots):  # one token per sequence: each is its own run
         b, row = int(slot) // bs, int(slot) % bs
         i = bidx[b]
         for kv, x in ((0, knew), (1, vnew)):
-            for h in range(w.hkv):
+            for h in range(hkv):
                 if kvd == orc.I8:
                     codes, sc = orc.quant_append(exp_codes[i, kv, h], float(exp_scales[i, kv, h]), row,
                                                  x[t:t + 1, h, :])
@@ -69,7 +68,8 @@ def test_full_size_step(gpu, cfg):
         for l in layers_checked:
             knew = synth.as_f32(w.knew[l].cpu())
             vnew = synth.as_f32(w.vnew[l].cpu())
-            exp_c, exp_s = _expected_after_append(w, l, before[l][0], before[l][1], blocks, slots, knew, vnew)
+            exp_c, exp_s = _expected_after_append(bs, w.hkv, _kv_code(w, l), before[l][0], before[l][1], blocks, slots,
+                                                  knew, vnew)
             got_c, got_s = w.pool.read_blocks(l, blocks)
             for i, b in enumerate(blocks):
                 rows = max(int(s) % bs for s in slots if int(s) // bs == b) + 1
@@ -140,6 +140,175 @@ def test_full_size_prefill(gpu, cfg):
             ref = orc.decode_attention(orc.I8, kc, vc, ks, vs, q, w.table[[s for s, _ in rows]], lens, w.scale)
             max_abs, max_rel = H.attention_errors(got, ref)
             print(f"[fullsize] {cfg} layer {layer} rows {len(rows)}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
+                  flush=True)
+            H.assert_attention_close(got, ref)
+        w.pool.close()
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_full_size_seal_steps(gpu):
+    """The seal-on-full workload (Qwen3-TTS talker, 28 layers, 4 x 8000, INT8
+    quantized when a block fills) as bench.py builds and launches it: two
+    pkv_decode_step steps. The first writes row 15 of each sequence's last
+    block and so seals it; the second starts a fresh block, whose row stays
+    binary16. Per step and checked layer: sealed blocks' codes and scales
+    bit-exact with the oracle's quantize_block over the pre-step binary16
+    rows plus the new row; staged rows bit-exact; the decode-step output of
+    the last layer and a plain decode of the first and middle layers within
+    tolerance of the FP64 oracle over the GPU's read-back cache (INT8 for full
+    blocks, binary16 for the partly filled one)."""
+    import torch
+    import bench
+    from oracle import seal
+    print("[fullsize] building qwen_seal", flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        w = bench.Workload("qwen_seal", steps_total=4)
+        torch.cuda.synchronize()
+        bs = w.bs
+        layers_checked = sorted({0, w.L // 2, w.L - 1})
+        sealed_seen = staged_seen = 0
+        for step in range(2):
+            w.host_prep()
+            slots = w.d_slots.cpu().numpy()
+            blocks = sorted({int(s) // bs for s in slots})
+            before = {l: w.pool.read_tail_blocks(l, blocks) for l in layers_checked}
+            w.device_step()
+            torch.cuda.synchronize()
+            last_out = w.out.cpu().numpy()
+            table, lens = w.pool.block_table(w.seqs, w.max_blocks)
+            for l in layers_checked:
+                knew = synth.as_f32(w.knew[l].cpu())
+                vnew = synth.as_f32(w.vnew[l].cpu())
+                codes, scales = w.pool.read_blocks(l, blocks)
+                tails = w.pool.read_tail_blocks(l, blocks)
+                for t, slot in enumerate(slots):
+                    b, r = int(slot) // bs, int(slot) % bs
+                    i = blocks.index(b)
+                    for kv, x in ((0, knew), (1, vnew)):
+                        rows16 = before[l][i, kv].copy()  # [Hkv][bs][d] binary16 bits
+                        rows16[:, r, :] = seal.f16_bits(x[t])
+                        if r == bs - 1:
+                            for h in range(w.hkv):
+                                xq = rows16[h].view(np.float16).astype(np.float32)
+                                eq, es = seal.quantize_block(xq)
+                                np.testing.assert_array_equal(codes[i, kv, h], eq,
+                                                              err_msg=f"step {step} layer {l} block {b} codes")
+                                assert np.float32(scales[i, kv, h]).view(np.uint32) == np.float32(es).view(
+                                    np.uint32), f"step {step} layer {l} block {b} scale"
+                            sealed_seen += 1
+                        else:
+                            np.testing.assert_array_equal(tails[i, kv, :, :r + 1], rows16[:, :r + 1],
+                                                          err_msg=f"step {step} layer {l} block {b} rows")
+                            staged_seen += 1
+                # attention over the cache as the kernels read it
+                nblk = (lens + bs - 1) // bs
+                used = sorted({int(table[s, j]) for s in range(w.B) for j in range(nblk[s])})
+                c_all, s_all = w.pool.read_blocks(l, used)
+                t_all = w.pool.read_tail_blocks(l, used)
+                kvals = np.zeros((w.nblocks, w.hkv, bs, w.dim))
+                vvals = np.zeros_like(kvals)
+                last_blk = {int(table[s, nblk[s] - 1]): int(lens[s]) - (nblk[s] - 1) * bs for s in range(w.B)}
+                for i, b in enumerate(used):
+                    r = last_blk.get(b, bs)
+                    if r == bs:
+                        kvals[b] = c_all[i, 0] * s_all[i, 0].astype(np.float64)[:, None, None]
+                        vvals[b] = c_all[i, 1] * s_all[i, 1].astype(np.float64)[:, None, None]
+                    else:
+                        kvals[b, :, :r] = t_all[i, 0, :, :r].view(np.float16).astype(np.float64)
+                        vvals[b, :, :r] = t_all[i, 1, :, :r].view(np.float16).astype(np.float64)
+                q = synth.as_f32(w.q[l].cpu())
+                ref = orc.decode_attention(orc.VALUES, kvals, vvals, None, None, q, table, lens, w.scale)
+                if l == w.L - 1:
+                    got = last_out
+                else:
+                    d_table = torch.from_numpy(table).cuda()
+                    d_lens = torch.from_numpy(lens).cuda()
+                    out = torch.empty(w.B, w.hq, w.dim, dtype=torch.float32, device="cuda")
+                    w.pool.decode(l, w.q[l], d_table, d_lens, w.max_ctx, w.scale, out=out, workspace=w.ws,
+                                  partition_tokens=w.partition, flags=w.flags)
+                    torch.cuda.synchronize()
+                    got = out.cpu().numpy()
+                max_abs, max_rel = H.attention_errors(got, ref)
+                print(f"[fullsize] qwen_seal step {step} layer {l}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
+                      flush=True)
+                H.assert_attention_close(got, ref)
+        assert sealed_seen > 0 and staged_seen > 0
+        w.pool.close()
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", ["serve16", "serve32"])
+def test_full_size_serving_step(gpu, cfg):
+    """The serving workload as bench.py runs it (1024 queued requests over a
+    shared 200-token prompt, batch up to 128, 32 layers, INT8, pkv_sched
+    planning every step, copy-on-write of the shared prompt's last block):
+    after 100 steps, the next step that admits nobody is checked. Its
+    appended rows are bit-exact with the oracle's quantizer applied to the
+    blocks read back before it (after the plan's copies); the last layer's
+    decode-step output and a plain decode of the first layer, for sampled
+    sequences, are within tolerance of the FP64 oracle over the GPU's cache."""
+    import torch
+    import bench
+    print(f"[fullsize] building {cfg}", flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        w = bench.ServeWorkload(cfg, stream)
+        for _ in range(100):
+            w.step()
+        for _ in range(100):
+            p = w.plan()
+            if p["prefill_slots"].size == 0 and len(p["seqs"]) > 0:
+                break
+            w.launch(p)
+        else:
+            pytest.fail("no step without admissions")
+        torch.cuda.synchronize()  # the plan's copy-on-write copies are done
+        n, bs = len(p["seqs"]), w.bs
+        slots = p["slots"]
+        blocks = sorted({int(x) // bs for x in slots})
+        layers_checked = [0, w.L - 1]
+        before = {l: w.pool.read_blocks(l, blocks) for l in layers_checked}
+        w.launch(p)
+        torch.cuda.synchronize()
+        last_out = w.out[:n].cpu().numpy()
+        knew = synth.as_f32(w.knew[:n].cpu())
+        vnew = synth.as_f32(w.vnew[:n].cpu())
+        for l in layers_checked:
+            exp_c, exp_s = _expected_after_append(bs, w.hkv, orc.I8, before[l][0], before[l][1], blocks, slots,
+                                                  knew, vnew)
+            got_c, got_s = w.pool.read_blocks(l, blocks)
+            for i, b in enumerate(blocks):
+                rows = max(int(x) % bs for x in slots if int(x) // bs == b) + 1
+                np.testing.assert_array_equal(got_c[i][:, :, :rows], exp_c[i][:, :, :rows],
+                                              err_msg=f"{cfg} layer {l} block {b} codes")
+                np.testing.assert_array_equal(got_s[i].view(np.uint32), exp_s[i].view(np.uint32),
+                                              err_msg=f"{cfg} layer {l} block {b} scales")
+        print(f"[fullsize] {cfg}: batch {n}, append bit-exact on {len(blocks)} blocks x {len(layers_checked)} layers",
+              flush=True)
+        rng = np.random.default_rng(5)
+        sample = sorted(rng.choice(n, size=min(3, n), replace=False).tolist())
+        table, lens = p["block_tables"], p["context_lens"]
+        sub_blocks = sorted({int(b) for s in sample for b in table[s, :(int(lens[s]) + bs - 1) // bs]})
+        shape = H.Shape(layers=w.L, hq=w.hq, hkv=w.hkv, dim=w.dim, bs=bs, nblocks=w.nblocks, kv_dtype=orc.I8)
+        q = synth.as_f32(w.q[:n].cpu())[sample]
+        for l in layers_checked:
+            if l == w.L - 1:
+                got = last_out[sample]
+            else:
+                out = torch.empty(n, w.hq, w.dim, dtype=torch.float32, device="cuda")
+                w.pool.decode(l, w.q[:n], w.table(n), w.d_lens[:n], p["max_context_len"], w.scale, out=out,
+                              workspace=w.ws)
+                torch.cuda.synchronize()
+                got = out.cpu().numpy()[sample]
+            kc, vc, ks, vs = H.gpu_layer_arrays(w.pool, l, sub_blocks, shape)
+            ref = orc.decode_attention(orc.I8, kc, vc, ks, vs, q, table[sample], lens[sample], w.scale)
+            max_abs, max_rel = H.attention_errors(got, ref)
+            print(f"[fullsize] {cfg} layer {l} seqs {sample}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}",
                   flush=True)
             H.assert_attention_close(got, ref)
         w.pool.close()

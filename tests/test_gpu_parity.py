@@ -27,6 +27,32 @@ def test_tiny_config(gpu, kv, T, flags):
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+def test_workspace_shared_across_merge_placements(gpu, kv):
+    """One workspace for calls that mix merge placements and partition sizes
+    (so each call uses a different part of it): every call matches the
+    oracle, and the arrival counters are back at zero after each call, as the
+    next call needs them."""
+    import torch
+    case = H.tiny_case(kv)
+    res = H.run_decode_case(case, partition_tokens=16)
+    pool, table, lens, q = res["pool"], res["table"], res["lens"], res["q"]
+    sh = case.shape
+    dev = pool.arena.device
+    t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    max_ctx = int(lens.max())
+    nb = max(pool.workspace_bytes(len(lens), sh.hq, max_ctx, T) for T in (16, 64))
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    for T, flags in [(16, 2), (64, 1), (16, 1), (64, 2), (16, 2), (64, 0), (16, 2)]:
+        for layer in range(sh.layers):
+            out = pool.decode(layer, q.to(dev), t_table, t_lens, max_ctx, sh.scale, workspace=ws,
+                              partition_tokens=T, flags=flags)
+            torch.cuda.synchronize()
+            counters = ws[:4 * len(lens) * sh.hkv].view(torch.int32)
+            assert int(torch.count_nonzero(counters)) == 0, f"T={T} flags={flags}: counters not reset"
+            H.assert_attention_close(out.cpu().numpy(), res["ref"][layer])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("in_dtype,q_dtype", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16")])
 def test_input_dtypes(gpu, kv, in_dtype, q_dtype):
     res = H.run_decode_case(H.tiny_case(kv, in_dtype=in_dtype, q_dtype=q_dtype), partition_tokens=64)

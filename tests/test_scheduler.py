@@ -202,3 +202,18 @@ def test_submit_errors():
     s.step()
     with pytest.raises(pkv.PkvError):
         s.step(eos=[7])                            # not in the previous batch
+
+
+def test_pool_close_closes_its_schedulers_first():
+    """A scheduler frees its running sequences through the pool when closed,
+    so closing the pool closes the schedulers over it first; a scheduler
+    closed that way is inert afterwards."""
+    from paged_kv_cache_62_amd import pkv
+    p = pkv.Pool(2, 2, 64, 16, 64, pkv.PKV_I8, host_only=True)
+    s = pkv.Scheduler(p, 4, 256)
+    s.submit(1, 20, 10)
+    assert len(s.step()["seqs"]) == 1
+    assert p.stats()["used_blocks"] == 2
+    p.close()
+    assert s.h is None
+    s.close()  # no-op
