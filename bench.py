@@ -374,7 +374,7 @@ def main():
     if args.warmup is None:
         args.warmup = 100 if serve else 2 if prefill else 50
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     known = sorted(CONFIGS) + sorted(SERVE_CONFIGS) + sorted(PREFILL_CONFIGS)
     if args.config not in known:

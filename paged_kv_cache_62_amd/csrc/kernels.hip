@@ -1077,8 +1077,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   };
 
   // Decode step on a seal-on-full layer, by the owner of the sequence's last
-  // block, before the loop: the block's staged rows and the new token's row (binary16, as
-  // pkv_append_kv stages it) go to wave-private LDS. If the new row leaves
+  // block, after the loop (its streaming starts with everyone else's; staged
+  // before the loop, it started several microseconds late): the block's
+  // staged rows and the new token's row (binary16, as pkv_append_kv stages
+  // it) go to wave-private LDS. If the new row leaves
   // the block partly filled, it is also staged in memory; if it fills the
   // block, the block is sealed as the append does it (scale = max|x| / 127
   // per K and V, codes, largest |code|).
@@ -1091,16 +1093,38 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     const size_t toff = ((size_t)blk * hkv + g) * bs * D;
     uint16_t* tk = (uint16_t*)a.lv.tail_k + toff;
     uint16_t* tv = (uint16_t*)a.lv.tail_v + toff;
-    // rows [0, 16 * ntail) of both tiles are prefixes of the tiles
-    const int nchunk = ntail * kUnit * D * 2 / 16;  // 16-byte chunks per tile
-    for (int c = lane; c < nchunk; c += 64) {
-      ((uint4*)sm_tail[0])[c] = ((const uint4*)tk)[c];
-      ((uint4*)sm_tail[1])[c] = ((const uint4*)tv)[c];
-    }
+    // the new row first, then rows [0, 16 * ntail) of both tiles (prefixes
+    // of the tiles), four 16-byte chunks per lane and tile in flight at once
     const size_t rowbase = ((size_t)s * hkv + g) * D;
-    for (int dd = lane; dd < D; dd += 64) {
-      const uint16_t hk = __builtin_bit_cast(uint16_t, (_Float16)load_elem<QT>(a.k_new, rowbase + dd));
-      const uint16_t hv = __builtin_bit_cast(uint16_t, (_Float16)load_elem<QT>(a.v_new, rowbase + dd));
+    float xk[NPL], xv[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      xk[k] = load_elem<QT>(a.k_new, rowbase + lane + 64 * k);
+      xv[k] = load_elem<QT>(a.v_new, rowbase + lane + 64 * k);
+    }
+    const int nchunk = ntail * kUnit * D * 2 / 16;  // 16-byte chunks per tile
+    for (int c0 = 0; c0 < nchunk; c0 += 4 * 64) {
+      uint4 ck[4], cv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = min(c0 + 64 * u + lane, nchunk - 1);
+        ck[u] = ((const uint4*)tk)[c];
+        cv[u] = ((const uint4*)tv)[c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u + lane;
+        if (c < nchunk) {
+          ((uint4*)sm_tail[0])[c] = ck[u];
+          ((uint4*)sm_tail[1])[c] = cv[u];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int dd = lane + 64 * k;
+      const uint16_t hk = __builtin_bit_cast(uint16_t, (_Float16)xk[k]);
+      const uint16_t hv = __builtin_bit_cast(uint16_t, (_Float16)xv[k]);
       sm_tail[0][k_tile_offset(seal_row, dd, D)] = hk;
       sm_tail[1][v_tile_offset(seal_row, dd, D)] = hv;
       if (seal_row < bs - 1) {
@@ -1138,12 +1162,8 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
       a.lv.v_qmax[at] = qv;
     }
   };
-  if constexpr (SEAL && APPEND) {
-    if (ntail > 0) seal_step_stage();  // wave-uniform
-  }
-
   // Decode step on a seal-on-full layer, after the loop: the last block's
-  // units, staged in LDS before the loop, in the order a decode of the
+  // units, staged in LDS just before, in the order a decode of the
   // appended cache takes them: as FP16, or from the codes of a block sealed
   // in this launch.
   auto seal_step_decode = [&]() {
@@ -1235,7 +1255,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   }
 
   if constexpr (SEAL && APPEND) {
-    if (ntail > 0) seal_step_decode();
+    if (ntail > 0) {  // wave-uniform
+      seal_step_stage();
+      seal_step_decode();
+    }
   } else if constexpr (SEAL) {
     if (ntail > 0) {  // wave-uniform: the FP16 tail, after the INT8 units
       const int blk = min(max(__builtin_amdgcn_readlane(tentry, nu - 1), 0), a.lv.num_blocks - 1);

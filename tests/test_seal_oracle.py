@@ -4,7 +4,7 @@ the mathematics fix, independently of its own code. CPU only.
 "轻量级推理引擎实战：KV Cache 量化与连续批处理的底层优化" §三: the quantizer takes FP16
 data (modelled as f32), one scale per (block, head) = max|x|/127 (1.0 for an
 all-zero head), codes round(x/scale) clamped to [-127, 127]; third design
-note: quantize off the hot path, which this build reads as "once a block is
+note: quantize off the hot path, read here as "once a block is
 full" (until then its rows are FP16)."""
 import numpy as np
 import pytest
