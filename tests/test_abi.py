@@ -91,7 +91,9 @@ def test_device_calls_on_host_only_pool_are_unsupported():
     ((28, 8, 128, 16, 2048, "I8"), 4, 8044, 0, (1024, 8, 1)),      # Qwen3-TTS talker
     ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 0, (512, 9, 0)),    # Llama-2-7B, 29 x 4096
     ((32, 32, 128, 16, 8192, "F16"), 128, 1068, 0, (2048, 1, 0)),  # Llama-2-7B, 128 x 1024
-    ((32, 8, 128, 16, 15000, "I8"), 128, 1270, 0, (512, 3, 0)),    # continuous-batching mix
+    ((32, 8, 128, 16, 15000, "I8"), 128, 1270, 0, (2048, 1, 0)),  # continuous-batching mix
+    ((32, 8, 128, 16, 15000, "I8"), 32, 1024, 0, (1024, 1, 1)),    # 256 (seq, KV head) pairs: one partition
+    ((32, 8, 128, 16, 15000, "I8"), 31, 1024, 0, (512, 2, 1)),     # 248 pairs: split, every CU has work
     ((2, 8, 128, 64, 4200, "I8"), 8, 32800, 0, (1024, 33, 0)),     # long context
     ((1, 2, 64, 16, 64, "I8"), 4, 600, 0, (128, 5, 1)),            # tiny
     ((1, 2, 64, 16, 64, "I8"), 4, 600, 1, (128, 5, 0)),
