@@ -1402,34 +1402,96 @@ void decode_kernel_f16(const DecodeLaunch a) {
 // H3 as its own launch: merge the partitions of each (sequence, query head):
 //   M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p
 // where o_p is the partition's normalised output and m_p its base-2 maximum.
+// The partials are a few KB per row, so the merge is bound by memory latency:
+// one 256-thread workgroup per row takes the partitions CHUNK (16, 32 or 64,
+// the least that covers max_partitions) at a time, with every load of a
+// chunk in flight at once. Wavefront 0 loads the chunk's m and l (lane =
+// partition) and puts the weights in LDS; thread t
+// loads dim t % D of partitions t / D, t / D + S, ... (S = 256 / D slices).
+// The first chunk's loads leave before the sequence length is known (they
+// stay inside the row's max_partitions slots; partitions past the sequence's
+// get weight 0). The slices' sums are added through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const DecodeLaunch a) {
+constexpr int kMergeThreads = 256;
+
+template <int D, int CHUNK>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeLaunch a) {
+  static_assert(CHUNK <= 64, "one partition per lane of wavefront 0");
+  constexpr int S = kMergeThreads / D;
+  constexpr int NO = CHUNK / S;  // o values per thread and chunk
   const int hq = a.num_q_heads;
   const int s = blockIdx.x / hq;
   const int h = blockIdx.x % hq;
-  const int T = a.partition_tokens;
-  const int len = min(a.lens[s], min(a.max_blocks * a.lv.block_size, a.max_partitions * T));
-  const int nparts = (len + T - 1) / T;
-  if (nparts <= 1) return;
-  const size_t pmax = a.max_partitions;
+  const int pmax = a.max_partitions;
   const size_t nrow = (size_t)a.num_seqs * hq * pmax;
   const float* ws_m = a.ws;
   const float* ws_l = a.ws + nrow;
   const float* ws_o = a.ws + 2 * nrow;
   const size_t base = ((size_t)s * hq + h) * pmax;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_m[base + p]);
-  float L = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(ws_m[base + p] - M) * ws_l[base + p];
-    L += w;
-    O = fmaf(w, ws_o[(base + p) * D + threadIdx.x], O);
+  const int t = threadIdx.x;
+  const int dd = t % D;
+  const int slice = t / D;
+  const int T = a.partition_tokens;
+  const int len = min(a.lens[s], min(a.max_blocks * a.lv.block_size, pmax * T));
+  const int nparts = (len + T - 1) / T;
+
+  __shared__ float sm_w[CHUNK];
+  __shared__ float sm_mn;
+  float M = -INFINITY, L = 0.f, O = 0.f;  // L: wavefront 0 only
+  for (int c0 = 0; c0 < pmax; c0 += CHUNK) {
+    float ov[NO];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) ov[k] = ws_o[(base + min(c0 + slice + k * S, pmax - 1)) * D + dd];
+    float mv = -INFINITY, lv = 0.f;
+    if (t < CHUNK) {
+      const int p = min(c0 + t, pmax - 1);
+      mv = ws_m[base + p];
+      lv = ws_l[base + p];
+    }
+    if (nparts <= 1) return;  // (uniform) one partition: the decode kernel wrote the output
+    if (c0 >= nparts) break;  // (uniform) nothing more to merge
+    if (t < 64) {  // wavefront 0
+      const bool live = t < CHUNK && c0 + t < nparts;
+      const float Mn = fmaxf(M, wave_max(live ? mv : -INFINITY));
+      const float w = live ? __builtin_amdgcn_exp2f(mv - Mn) * lv : 0.f;
+      float ws = w;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
+      L = L * __builtin_amdgcn_exp2f(M - Mn) + ws;  // M = -inf on the first chunk: 0
+      if (t < CHUNK) sm_w[t] = w;
+      if (t == 0) sm_mn = Mn;
+    }
+    __syncthreads();
+    const float Mn = sm_mn;
+    O *= __builtin_amdgcn_exp2f(M - Mn);
+#pragma unroll
+    for (int k = 0; k < NO; ++k)  // slots past nparts may hold anything from earlier calls
+      O = fmaf(sm_w[slice + k * S], c0 + slice + k * S < nparts ? ov[k] : 0.f, O);
+    M = Mn;
+    __syncthreads();  // sm_w and sm_mn are rewritten by the next chunk
   }
-  a.out[((size_t)s * hq + h) * D + threadIdx.x] = O / L;
+  __shared__ float sm_o[S][D];
+  __shared__ float sm_l;
+  sm_o[slice][dd] = O;
+  if (t == 0) sm_l = L;
+  __syncthreads();
+  if (slice != 0) return;
+  float Ot = 0.f;
+#pragma unroll
+  for (int k = 0; k < S; ++k) Ot += sm_o[k][dd];
+  a.out[((size_t)s * hq + h) * D + dd] = Ot / sm_l;
 }
 
+
+template <int D>
+void launch_merge(const DecodeLaunch& d, int chunk, dim3 grid, hipStream_t stream) {
+  if (chunk == 16)
+    hipLaunchKernelGGL((merge_kernel<D, 16>), grid, dim3(kMergeThreads), 0, stream, d);
+  else if (chunk == 32)
+    hipLaunchKernelGGL((merge_kernel<D, 32>), grid, dim3(kMergeThreads), 0, stream, d);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, 64>), grid, dim3(kMergeThreads), 0, stream, d);
+}
 
 template <bool I8, int D, int G, int QT>
 void launch_one(const DecodeLaunch& d, hipStream_t stream) {
@@ -1919,10 +1981,11 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     e = i8 ? launch_decode_g<true, 64>(d, group, stream) : launch_decode_g<false, 64>(d, group, stream);
   if (e != hipSuccess || d.max_partitions <= 1 || d.fused_merge) return e;
   const dim3 grid((unsigned)(d.num_seqs * d.num_q_heads));
+  const int chunk = d.max_partitions <= 16 ? 16 : d.max_partitions <= 32 ? 32 : 64;
   if (d.lv.head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, d);
+    launch_merge<128>(d, chunk, grid, stream);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, d);
+    launch_merge<64>(d, chunk, grid, stream);
   return hipGetLastError();
 }
 
