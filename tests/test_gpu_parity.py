@@ -52,6 +52,25 @@ def test_workspace_shared_across_merge_placements(gpu, kv):
             H.assert_attention_close(out.cpu().numpy(), res["ref"][layer])
 
 
+@pytest.mark.parametrize("dim", [64, 128])
+@pytest.mark.parametrize("T", [256, 128, 64, 16])
+@pytest.mark.parametrize("flags", [1, 2])
+def test_merge_over_partition_counts(gpu, dim, T, flags):
+    """Contexts of 3000, 1 and 700 tokens split into 12, 24, 47 or 188
+    partitions: every chunk size of the merge launch (16, 32, 64 partitions,
+    and several chunks of 64) and of the in-launch merge, at both head
+    dims."""
+    lens = [3000, 1, 700]
+    bs = 16
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=dim, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + 3,
+                 kv_dtype=orc.I8, in_dtype="bf16", q_dtype="bf16", free_order_seed=5, sigma_kv="per_head")
+    case = H.Case(sh, 62300 + dim + T, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=list(range(len(lens))))
+    res = H.run_decode_case(case, partition_tokens=T, flags=flags, compare_cache=False)
+    _report(f"merge d={dim} T={T} flags={flags}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("in_dtype,q_dtype", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16")])
 def test_input_dtypes(gpu, kv, in_dtype, q_dtype):
