@@ -473,6 +473,21 @@ def run(args, stream):
     e1.record()
     torch.cuda.synchronize()
     avg_dur_s = e0.elapsed_time(e1) / 1e3 / (reps * len(layers))
+    # H1 alone: the step's appends as pkv_append_kv launches (one per decoded
+    # layer), timed the same way; storing the last tokens again leaves the
+    # cache unchanged.
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga, stream=stream):
+        for layer in layers:
+            w.pool.append_kv(layer, w.knew[layer], w.vnew[layer], w.d_slots)
+    ga.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        ga.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) * 1e3 / (reps * len(layers))
     _, lens_now = w.pool.block_table(w.seqs, w.max_blocks)
     bytes_launch = float(np.mean([w.kv_read_bytes(lens_now, l) for l in layers]))  # per launch, averaged
     achieved = bytes_launch / avg_dur_s / 1e9
@@ -501,7 +516,8 @@ def run(args, stream):
                             "last workgroup" if plan[2] else "separate launch",
                    "hip_graph": not args.no_graph,
                    "launches_per_layer": 1 if w.fused else 2,
-                   "kv_read_GBps_whole_step": kv_gbs_step},
+                   "kv_read_GBps_whole_step": kv_gbs_step,
+                   "append_kernel_us": append_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
                      "kernel": ("decode_kernel, decode step (new token's append + split-context decode + merge)"
