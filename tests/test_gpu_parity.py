@@ -183,6 +183,25 @@ def test_decode_step_shapes(gpu, kv, shape_i):
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("T", [0, 32])
+def test_decode_step_grid_beyond_one_round(gpu, kv, T):
+    """120 sequences x 8 KV heads (960 workgroups at one partition, 4 x more
+    at 32-token partitions): grids larger than the device holds at once, where
+    the INT8 step runs its two-deep variant. Identical to append + decode over
+    three steps (the new tokens open, continue and fill blocks), cache
+    bit-exact with the oracle."""
+    rng = np.random.default_rng(62450)
+    lens = [int(x) for x in rng.integers(1, 120, size=120)]
+    bs = 16
+    sh = H.Shape(layers=1, hq=16, hkv=8, dim=128, bs=bs, nblocks=sum((n + 3) // bs + 1 for n in lens) + 8,
+                 kv_dtype=kv, in_dtype="bf16", q_dtype="bf16", free_order_seed=4, sigma_kv="per_head")
+    case = H.Case(sh, 62450, [("allocate", s, n) for s, n in enumerate(lens)], decode_seqs=list(range(len(lens))))
+    res = H.run_step_case(case, partition_tokens=T, steps=3)
+    _report(f"step big grid kv={kv} T={T}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 def test_decode_step_after_copy_on_write(gpu, kv):
     """The step writes into blocks that the preceding append_slots copied from a
     shared prefix (and into a freshly opened block after a freed sequence)."""
