@@ -493,6 +493,15 @@ def run(args, stream):
     achieved = bytes_launch / avg_dur_s / 1e9
     kv_gbs_step = float(np.sum(step_bytes)) / (total_ms / 1e3) / 1e9
     plan = w.pool.decode_plan(w.B, w.max_ctx, w.partition, w.flags)
+    # what a launch moves besides the K/V it reads: q, the fp32 output, the
+    # table entries and lengths it reads, the partition partials (written,
+    # then read by the merge) and, for a decode step, the new K/V rows read
+    qbytes = w.q[layers[0]].element_size()
+    used_blocks = int(sum((int(n) + w.bs - 1) // w.bs for n in lens_now))
+    nparts = sum((int(n) + plan[0] - 1) // plan[0] for n in lens_now)
+    other_bytes = (w.B * w.hq * w.dim * (qbytes + 4) + 4 * used_blocks + 4 * w.B +
+                   (2 * nparts * w.hq * (w.dim + 2) * 4 if plan[1] > 1 else 0) +
+                   (2 * w.B * w.hkv * w.dim * qbytes if w.fused else 0))
     res = {
         "metric": "decode attn tokens/sec and KV-read HBM GB/s (% of MI355X peak), 1 GPU",
         "value": tokens / (total_ms / 1e3),
@@ -523,6 +532,7 @@ def run(args, stream):
                      "kernel": ("decode_kernel, decode step (new token's append + split-context decode + merge)"
                                 if w.fused else "decode_kernel (split-context decode incl. partition merge)"),
                      "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
+                     "other_bytes_per_launch": other_bytes,
                      "timing": f"HIP events around {reps} replays of a graph of the {len(layers)} decode launches"},
     }
     res["_workload"] = w
