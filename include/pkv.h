@@ -82,8 +82,9 @@ typedef struct {
                             sequence's partly filled last block, and is quantized once,
                             all rows together, by the append that writes its last row
                             (see pkv_append_kv). Decode reads the FP16 rows of a
-                            sequence's partly filled last block and INT8 elsewhere.
-                            pkv_decode_step does not support it. 0 = quantize on append. */
+                            sequence's partly filled last block and INT8 elsewhere;
+                            pkv_decode_step stages and seals the same way.
+                            0 = quantize on append. */
 } pkv_pool_config;
 
 typedef struct {
