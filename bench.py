@@ -35,7 +35,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # rocprofv3 FETCH_SIZE + WRITE_SIZE summaries (scaled by a plain-copy reference)
 # per workload; used only while the kernel source still has the hash they record.
 TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
-                    "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md"}
+                    "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md",
+                    "mix16": "profiles/decode_kernel_mix_bs16_int8.md",
+                    "long_i8": "profiles/decode_kernel_long_context_int8.md"}
 
 
 def measured_traffic(config):
