@@ -328,6 +328,18 @@ class Workload:
         return range(self.L) if not self.rotate else [step_i % self.L]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w: Workload, target_s: float):
     """The FP64 oracle on a bounded sample: layers in order until ~target_s of
     CPU time, over the GPU's cache read back after the timed steps."""
@@ -338,6 +350,7 @@ def cpu_baseline(w: Workload, target_s: float):
     threads = max(1, min(16, os.cpu_count() or 1))
     done, elapsed = 0, 0.0
     layers = range(w.L) if not w.rotate else [0]
+    last = None
     for layer in layers:
         kvd = orc.I8 if w.pool.layer_kv_dtypes[layer] == w.pkv.PKV_I8 else orc.F16
         dt = np.int8 if kvd == orc.I8 else np.uint16
@@ -355,12 +368,18 @@ def cpu_baseline(w: Workload, target_s: float):
         orc.decode_attention(kvd, kc, vc, ks, vs, q, table, lens, w.scale, threads=threads)
         elapsed += time.perf_counter() - t0
         done += 1
+        last = (kvd, kc, vc, ks, vs, q)
         if elapsed >= target_s:
             break
     t_layer = elapsed / done
     layers_per_step = 1 if w.rotate else w.L
     value = w.B / (t_layer * layers_per_step)
+    # the same oracle on one thread, the last sampled layer once
+    t0 = time.perf_counter()
+    orc.decode_attention(*last[:6], table, lens, w.scale, threads=1)
+    t_one = time.perf_counter() - t0
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "value_1thread": w.B / (t_one * layers_per_step), "cpu_model": cpu_model(),
             "sample": (f"FP64 oracle decode of {done} of {layers_per_step} layer(s) per step "
                        f"({t_layer * 1e3:.1f} ms per layer, {threads} threads) over the GPU cache "
                        f"read back after the timed steps; tokens/s = B / (layers x time per layer), "
@@ -808,6 +827,7 @@ def prefill_cpu_baseline(w, target_s):
         if elapsed >= target_s:
             break
     return {"value": done_q / (elapsed * c["layers"]), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"FP64 prefill oracle on layer 0 for {done_q} of {int(w.qstart[-1])} query tokens "
                        f"({elapsed:.1f} s, {threads} threads) over the GPU cache read back; tokens/s = query "
                        f"tokens / (layers x time), extrapolated from the sampled layer and sequences")}
