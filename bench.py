@@ -40,19 +40,28 @@ TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "long_i8": "profiles/decode_kernel_long_context_int8.md"}
 
 
+def kernels_code_hash():
+    """sha256 of kernels.hip with comments and whitespace removed: it changes
+    when the kernels' code does, not when their comments do."""
+    import hashlib
+    import re
+    src = open(os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+
+
 def measured_traffic(config):
     """HBM bytes per decode launch from the committed counter summary, or
-    None when there is none or the kernels changed since it was taken."""
-    import hashlib
+    None when there is none or the kernels' code changed since it was taken."""
     import re
     path = TRAFFIC_PROFILES.get(config)
     if path is None or not os.path.exists(os.path.join(ROOT, path)):
         return None
     text = open(os.path.join(ROOT, path), encoding="utf-8").read()
     t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    h = re.search(r"kernels_hip_sha256: ([0-9a-f]{64})", text)
-    src = os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip")
-    if not t or not h or hashlib.sha256(open(src, "rb").read()).hexdigest() != h.group(1):
+    h = re.search(r"kernels_code_sha256: ([0-9a-f]{64})", text)
+    if not t or not h or kernels_code_hash() != h.group(1):
         return None
     return int(t.group(1))
 

@@ -11,6 +11,12 @@
 //  H3 merge:   log-sum-exp merge of the partitions, done by the last
 //              workgroup of each (sequence, KV head) to arrive, or by a
 //              separate launch.
+//  Decode step: H1 of each sequence's new token folded into H2 (one launch
+//              per layer); the INT8 step has a second variant for grids the
+//              device cannot hold at once.
+//  Prefill:    causal attention of each sequence's newest tokens over its
+//              context ("轻量级推理引擎实战" §一), on the same matrix-core
+//              contractions with the context staged once per workgroup in LDS.
 //
 // Both contractions of H2 run on the matrix cores, 16 tokens at a time:
 //   S^T[token][col] = K[token][:] . Q^T[:][col]      (A = K rows from HBM)
