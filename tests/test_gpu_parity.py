@@ -156,6 +156,26 @@ def test_partition_size_invariance(gpu, kv):
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_largest_partition(gpu, kv, bs):
+    """4096-token partitions (the largest): each wavefront of a full partition
+    takes 64 units, one per lane of its bookkeeping. Contexts of 9000 and 4096
+    tokens (partitions 4096 + 4096 + 808, and exactly one); decode, then
+    two decode steps against append + decode."""
+    lens = [9000, 4096, 5]
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + 2) // bs + 1 for n in lens) + 4,
+                 kv_dtype=kv, in_dtype="bf16", q_dtype="bf16", free_order_seed=8, sigma_kv="per_head")
+    case = H.Case(sh, 62500 + bs, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=list(range(len(lens))))
+    res = H.run_decode_case(case, partition_tokens=4096, compare_cache=False)
+    _report(f"largest partition kv={kv} bs={bs}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+    res = H.run_step_case(case, partition_tokens=4096, steps=2)
+    _report(f"largest partition step kv={kv} bs={bs}", res)
+    H.assert_attention_close(res["gpu"], res["ref"])
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("T", [16, 64, 0])
 @pytest.mark.parametrize("flags", [1, 2])
 def test_decode_step_tiny(gpu, kv, T, flags):
