@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md",
                     "mix16": "profiles/decode_kernel_mix_bs16_int8.md",
-                    "long_i8": "profiles/decode_kernel_long_context_int8.md"}
+                    "long_i8": "profiles/decode_kernel_long_context_int8.md",
+                    "prefill512": "profiles/prefill_kernel_qwen3_tts_chunk512_int8.md"}
 
 
 def kernels_code_hash():
@@ -894,7 +895,7 @@ def run_prefill(args, stream):
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": B, "query_tokens_per_seq": C,
                    "context": ctx, "layers_per_step": L, "hip_graph": True},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": measured_traffic(args.config),
                      "kernel": "prefill_kernel (causal paged attention, fp16 matrix cores)",
                      "avg_launch_us": avg_dur_s * 1e6, "flops_per_launch": flops,
                      "timing": f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"},
