@@ -1091,7 +1091,8 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // block, the block is sealed as the append does it (scale = max|x| / 127
   // per K and V, codes, largest |code|).
   constexpr int kMaxBs = 64;
-  __shared__ __align__(16) uint16_t sm_tail[SEAL && APPEND ? 2 : 1][SEAL && APPEND ? kMaxBs * D : 8];
+  // (two rows in every variant: the seal-on-full code below is compiled, never run, in the others)
+  __shared__ __align__(16) uint16_t sm_tail[2][SEAL && APPEND ? kMaxBs * D : 8];
   float seal_sk = 1.f, seal_sv = 1.f;  // scales of a block sealed in this launch
   const int seal_row = (len - 1) & (bs - 1);  // the new token's row in its block
   auto seal_step_stage = [&]() {
