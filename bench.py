@@ -41,12 +41,14 @@ TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "prefill512": "profiles/prefill_kernel_qwen3_tts_chunk512_int8.md"}
 
 
-def kernels_code_hash():
-    """sha256 of kernels.hip with comments and whitespace removed: it changes
-    when the kernels' code does, not when their comments do."""
+def kernels_code_hash(path=None):
+    """sha256 of kernels.hip (or `path`) with comments and whitespace
+    removed: it changes when the kernels' code does, not when their
+    comments do."""
     import hashlib
     import re
-    src = open(os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip"), encoding="utf-8").read()
+    path = path or os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip")
+    src = open(path, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
