@@ -408,20 +408,30 @@ void orc_cache_destroy(void* p) { delete (OrcCache*)p; }
 // in bf16/fp16 are widened exactly by the caller). slots[i] = block*bs + row.
 // Consecutive tokens that fall in the same block form one append into that
 // block, starting at row slots[first] % bs; their rows must be consecutive.
+// A slot outside [0, nblocks*bs), a same-block neighbour whose row is not
+// the next one, or a block that comes back after another block's tokens is
+// rejected before anything is written.
 int orc_cache_append(void* p, int32_t layer, const float* k, const float* v,
                      const int64_t* slots, int32_t n) {
   auto* c = (OrcCache*)p;
   const int64_t bs = c->bs;
+  std::vector<char> done(c->nblocks, 0);  // blocks whose run has ended
+  for (int32_t i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= (int64_t)c->nblocks * bs) return ORC_INVALID;
+    const int64_t blk = slots[i] / bs;
+    if (i > 0 && blk == slots[i - 1] / bs) {
+      if (slots[i] != slots[i - 1] + 1) return ORC_INVALID;
+    } else {
+      if (done[blk]) return ORC_INVALID;
+      if (i > 0) done[slots[i - 1] / bs] = 1;
+    }
+  }
   for (int32_t i = 0; i < n;) {
     const int64_t blk = slots[i] / bs;
     const int32_t row0 = (int32_t)(slots[i] % bs);
     int32_t j = i + 1;
-    while (j < n && slots[j] / bs == blk) {
-      if (slots[j] != slots[j - 1] + 1) return ORC_INVALID;
-      ++j;
-    }
+    while (j < n && slots[j] / bs == blk) ++j;
     const int32_t rows = j - i;
-    if (blk < 0 || blk >= c->nblocks) return ORC_INVALID;
     for (int kv = 0; kv < 2; ++kv) {
       const float* src = kv == 0 ? k : v;
       for (int32_t hd = 0; hd < c->heads; ++hd) {

@@ -348,3 +348,119 @@ def test_permutation_is_a_permutation():
     p = synth.permutation(123, 1000)
     assert sorted(p.tolist()) == list(range(1000))
     assert not np.array_equal(p, np.arange(1000))
+
+
+# ---------------------------------------------------------------- cache replay
+# The oracle's cache model replays the library's append and copy-on-write
+# calls. Its own parts: grouping a call's consecutive tokens that land in one
+# block into one append (reading 7 of the quantizer: one max over the run),
+# per-block dispatch of a run that crosses a block boundary, rejection of
+# slots that break the adjacency precondition, and the copy of a shared
+# block. Each is checked against quant_append (pinned above) composed by hand.
+
+def _hand_quant(tile, scale, fill, rows):
+    return orc.quant_append(tile, scale, fill, rows)
+
+
+def test_cache_append_takes_a_run_as_one_append(oracle_lib):
+    """A run of four tokens into a block that holds three rows, its max
+    growing inside the run: the block equals ONE quant_append of the four
+    rows (one m_new over the run), which here differs from four one-row
+    appends (each growth would re-encode the earlier rows again)."""
+    rng = np.random.default_rng(62011)
+    heads, dim, bs, N = 2, 8, 16, 4
+    c = orc.Cache(1, heads, dim, bs, N, orc.I8)
+    x0 = (0.5 * rng.standard_normal((3, heads, dim))).astype(np.float32)
+    run = rng.standard_normal((4, heads, dim)).astype(np.float32)
+    run[1] *= 3.0
+    run[3] *= 7.0
+    assert c.append(0, x0, -x0, np.arange(32, 35)) == orc.OK
+    assert c.append(0, run, 2.0 * run, np.arange(35, 39)) == orc.OK
+    codes, scales = c.read_block(0, 2)
+    differs = False
+    for kv, (a, b) in enumerate(((x0, run), (-x0, 2.0 * run))):
+        for h in range(heads):
+            t, s = _hand_quant(np.zeros((bs, dim), np.int8), 1.0, 0, a[:, h])
+            t, s = _hand_quant(t, s, 3, b[:, h])
+            np.testing.assert_array_equal(codes[kv, h, :7], t[:7])
+            assert np.float32(scales[kv, h]).view(np.uint32) == np.float32(s).view(np.uint32)
+            u, su = _hand_quant(np.zeros((bs, dim), np.int8), 1.0, 0, a[:, h])
+            for r in range(4):
+                u, su = _hand_quant(u, su, 3 + r, b[r:r + 1, h])
+            differs |= not np.array_equal(u[:7], t[:7]) or su != s
+    assert differs, "the run was not a case where grouping matters"
+
+
+@pytest.mark.parametrize("kv_dtype", [orc.I8, orc.F16])
+def test_cache_append_run_crossing_a_block_boundary(oracle_lib, kv_dtype):
+    """Slots 14, 15 of block 1 then 0, 1 of block 3 in one call: two appends,
+    the first onto the block's 14 rows, the second a fresh block whose scale
+    comes from its own two rows only."""
+    rng = np.random.default_rng(62012)
+    heads, dim, bs, N = 2, 8, 16, 5
+    c = orc.Cache(1, heads, dim, bs, N, kv_dtype)
+    pre = rng.standard_normal((14, heads, dim)).astype(np.float32)
+    x = rng.standard_normal((4, heads, dim)).astype(np.float32)
+    x[2:] *= 0.25  # block 3's own max is small: a scale from all four rows would be wrong
+    assert c.append(0, pre, pre, np.arange(16, 30)) == orc.OK
+    assert c.append(0, x, x, np.array([30, 31, 48, 49])) == orc.OK
+    c1, s1 = c.read_block(0, 1)
+    c3, s3 = c.read_block(0, 3)
+    for h in range(heads):
+        if kv_dtype == orc.I8:
+            t, s = _hand_quant(np.zeros((bs, dim), np.int8), 1.0, 0, pre[:, h])
+            t, s = _hand_quant(t, s, 14, x[:2, h])
+            u, su = _hand_quant(np.zeros((bs, dim), np.int8), 1.0, 0, x[2:, h])
+            for kv in range(2):
+                np.testing.assert_array_equal(c1[kv, h], t)
+                np.testing.assert_array_equal(c3[kv, h, :2], u[:2])
+                assert s1[kv, h] == np.float32(s) and s3[kv, h] == np.float32(su)
+            assert su == float(np.float32(np.abs(x[2:, h]).max()) / np.float32(127.0))
+        else:
+            for kv in range(2):
+                np.testing.assert_array_equal(c1[kv, h, :14], orc.f32_to_f16_bits(pre[:, h]).reshape(14, dim))
+                np.testing.assert_array_equal(c1[kv, h, 14:], orc.f32_to_f16_bits(x[:2, h]).reshape(2, dim))
+                np.testing.assert_array_equal(c3[kv, h, :2], orc.f32_to_f16_bits(x[2:, h]).reshape(2, dim))
+
+
+def test_cache_append_rejects_slots_that_break_the_run_rule(oracle_lib):
+    """Tokens of one block must be adjacent with consecutive rows; slots
+    outside the cache are rejected too. Nothing is written by a rejected
+    call."""
+    heads, dim, bs, N = 1, 8, 16, 3
+    for slots in ([32, 34], [33, 32], [32, 32], [-1, 0], [N * bs, N * bs + 1], [32, 16, 33]):
+        x = np.ones((len(slots), heads, dim), np.float32)
+        c = orc.Cache(1, heads, dim, bs, N, orc.I8)
+        assert c.append(0, x, x, np.array(slots)) == orc.INVALID, slots
+        for b in range(N):
+            codes, scales = c.read_block(0, b)
+            assert not codes.any() and (scales == 1.0).all(), (slots, b)
+    x = np.ones((2, heads, dim), np.float32)
+    c = orc.Cache(1, heads, dim, bs, N, orc.I8)
+    assert c.append(0, x, x, np.array([15, 16])) == orc.OK  # consecutive slots, two blocks
+
+
+def test_cache_copy_block_copies_rows_and_scales(oracle_lib):
+    """Copy-on-write: rows [0, rows) and the scale of every (layer, K|V,
+    head) go to the new block; its other rows and the source stay as they
+    were."""
+    rng = np.random.default_rng(62013)
+    L, heads, dim, bs, N = 2, 2, 8, 16, 4
+    c = orc.Cache(L, heads, dim, bs, N, orc.I8)
+    for layer in range(L):
+        a = rng.standard_normal((bs, heads, dim)).astype(np.float32)
+        b = (5.0 * rng.standard_normal((bs, heads, dim))).astype(np.float32)
+        assert c.append(layer, a, -a, np.arange(0, bs)) == orc.OK           # block 0: the source
+        assert c.append(layer, b, 2.0 * b, np.arange(2 * bs, 3 * bs)) == orc.OK  # block 2: overwritten
+    src = [c.read_block(layer, 0) for layer in range(L)]
+    old = [c.read_block(layer, 2) for layer in range(L)]
+    c.copy_block(0, 2, 5)
+    for layer in range(L):
+        dc, ds = c.read_block(layer, 2)
+        sc, ss = c.read_block(layer, 0)
+        np.testing.assert_array_equal(dc[:, :, :5], src[layer][0][:, :, :5])
+        np.testing.assert_array_equal(dc[:, :, 5:], old[layer][0][:, :, 5:])
+        np.testing.assert_array_equal(ds.view(np.uint32), src[layer][1].view(np.uint32))
+        np.testing.assert_array_equal(sc, src[layer][0])
+        np.testing.assert_array_equal(ss, src[layer][1])
+        assert not np.array_equal(src[layer][1], old[layer][1])  # the scales really changed

@@ -29,6 +29,64 @@ def pair(nblocks, bs, max_batch, max_model_len, reserve=1, order_seed=None):
     return pool, lib_s, ora
 
 
+class _LibSide:
+    """The library's scheduler over a host-only pool."""
+
+    def __init__(self, nblocks, bs, max_batch, max_model_len, reserve):
+        self.pool = pkv.Pool(1, 2, 64, bs, nblocks, pkv.PKV_I8, host_only=True)
+        self.s = pkv.Scheduler(self.pool, max_batch, max_model_len, reserve)
+
+    def allocate(self, seq, n):
+        self.pool.allocate(seq, n)
+
+    def submit(self, rid, prompt, max_new, prefix_seq=-1):
+        self.s.submit(rid, prompt, max_new, prefix_seq)
+
+    def step(self, eos=()):
+        return self.s.step(eos)
+
+    def stats(self):
+        return self.s.stats()
+
+    def pool_stats(self):
+        st = self.pool.stats()
+        return {k: st[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "cow_copies")}
+
+
+class _OracleSide:
+    """The oracle scheduler (oracle/scheduler.py) over the oracle's allocator
+    model, behind the same calls."""
+
+    def __init__(self, nblocks, bs, max_batch, max_model_len, reserve):
+        self.alloc = orc.Allocator(nblocks, bs)
+        self.s = osch.Scheduler(self.alloc, max_batch, max_model_len, reserve)
+
+    def allocate(self, seq, n):
+        assert self.alloc.allocate(seq, n)[0] == orc.OK
+
+    def submit(self, rid, prompt, max_new, prefix_seq=-1):
+        plen = 0
+        if prefix_seq >= 0:
+            st, _, lens = self.alloc.table([prefix_seq], self.alloc.num_blocks)
+            assert st == orc.OK
+            plen = int(lens[0])
+        self.s.submit(rid, prompt, max_new, prefix_seq, plen)
+
+    def step(self, eos=()):
+        return self.s.step(eos)
+
+    def stats(self):
+        return self.s.stats()
+
+    def pool_stats(self):
+        st = self.alloc.stats()
+        return {"free_blocks": st["free"], "used_blocks": st["used"], "shared_blocks": st["shared"],
+                "cow_copies": st["cow"]}
+
+
+SIDES = {"library": _LibSide, "oracle": _OracleSide}
+
+
 def same_plan(a, b, step):
     for k in KEYS:
         np.testing.assert_array_equal(a[k], b[k], err_msg=f"{k} differs at step {step}")
@@ -87,11 +145,12 @@ def test_random_scripts_match_the_oracle(seed):
         prev = a
 
 
-def test_b_finishes_c_joins_a_continues():
+@pytest.mark.parametrize("side", sorted(SIDES))
+def test_b_finishes_c_joins_a_continues(side):
     """"无 vLLM 环境下的 Paged-KV 与连续批处理调度" §3.1: with no room for C while A and
     B run, B's EOS frees its blocks and C is admitted in that very step,
     while A keeps decoding without a break."""
-    pool, s, _ = pair(nblocks=8, bs=16, max_batch=4, max_model_len=128, reserve=1)
+    s = SIDES[side](nblocks=8, bs=16, max_batch=4, max_model_len=128, reserve=1)
     s.submit(0, 40, 60)   # A: long (3 blocks, 4 with its tokens)
     s.submit(1, 30, 60)   # B: short text, ends by EOS
     s.submit(2, 40, 60)   # C: 3 blocks + 1 reserve: does not fit beside A and B
@@ -108,8 +167,11 @@ def test_b_finishes_c_joins_a_continues():
     assert s.stats()["finished_eos"] == 1
 
 
-def test_length_limit_ends_with_kind_3_and_frees_at_once():
-    pool, s, _ = pair(nblocks=16, bs=16, max_batch=2, max_model_len=20, reserve=0)
+@pytest.mark.parametrize("side", sorted(SIDES))
+def test_length_limit_ends_with_kind_3_and_frees_at_once(side):
+    """"无 vLLM 环境下的 Paged-KV 与连续批处理调度" §3.1: the length limit ends a
+    request (event kind 3) and its blocks are reclaimed at once."""
+    s = SIDES[side](nblocks=16, bs=16, max_batch=2, max_model_len=20, reserve=0)
     s.submit(0, 15, 100)     # stops at max_model_len = 20 tokens
     s.submit(1, 10, 3)       # stops after 3 decoded tokens
     lens = []
@@ -120,14 +182,15 @@ def test_length_limit_ends_with_kind_3_and_frees_at_once():
     assert [d.get(0) for d in lens[:5]] == [16, 17, 18, 19, 20] and 0 not in lens[5]
     st = s.stats()
     assert st["finished_max_length"] == 2 and st["running"] == 0
-    assert pool.stats()["used_blocks"] == 0      # reclaimed at once
+    assert s.pool_stats()["used_blocks"] == 0    # reclaimed at once
     assert st["generated"] == 5 + 3
 
 
-def test_no_free_block_waits_and_pauses_admission():
+@pytest.mark.parametrize("side", sorted(SIDES))
+def test_no_free_block_waits_and_pauses_admission(side):
     """"连续批处理与KV缓存" §4.2: a request whose next token needs a block while
     the queue is empty waits; §4.4: new requests pause until blocks return."""
-    pool, s, _ = pair(nblocks=4, bs=16, max_batch=4, max_model_len=200, reserve=0)
+    s = SIDES[side](nblocks=4, bs=16, max_batch=4, max_model_len=200, reserve=0)
     s.submit(0, 32, 30)    # 2 full blocks: its next token needs a third
     s.submit(1, 20, 40)    # 2 blocks, room for 12 more tokens
     p = s.step()
@@ -140,12 +203,13 @@ def test_no_free_block_waits_and_pauses_admission():
     assert (1, pkv.PKV_EV_EOS) in p["events"] and 0 in p["seqs"].tolist()
 
 
-def test_everyone_waiting_preempts_the_youngest():
+@pytest.mark.parametrize("side", sorted(SIDES))
+def test_everyone_waiting_preempts_the_youngest(side):
     """Two requests each filling one block of a two-block pool: neither can
     take its next token. The youngest gives its block back and returns to the
     queue front; the other goes on, finishes, and the first is admitted again
     (with its tokens so far as its prompt) and finishes too."""
-    pool, s, _ = pair(nblocks=2, bs=16, max_batch=2, max_model_len=100, reserve=0)
+    s = SIDES[side](nblocks=2, bs=16, max_batch=2, max_model_len=100, reserve=0)
     s.submit(0, 16, 16)
     s.submit(1, 16, 16)
     p = s.step()
@@ -159,7 +223,7 @@ def test_everyone_waiting_preempts_the_youngest():
         if len(finished) == 2:
             break
     assert finished == {0, 1}
-    assert s.stats()["generated"] == 32 and pool.stats()["used_blocks"] == 0
+    assert s.stats()["generated"] == 32 and s.pool_stats()["used_blocks"] == 0
 
 
 def test_request_larger_than_the_pool_is_rejected():
@@ -169,17 +233,18 @@ def test_request_larger_than_the_pool_is_rejected():
     s.submit(1, 16, 16)
 
 
-def test_shared_system_prompt_blocks():
+@pytest.mark.parametrize("side", sorted(SIDES))
+def test_shared_system_prompt_blocks(side):
     """"vLLM核心概念" §3.6: a ~200-token system prompt shared by all requests.
     At bs 16 it is 12 full blocks + 1 partial: each request adds its own
     blocks, and its first write copies the partial block (copy-on-write)."""
-    pool, s, _ = pair(nblocks=400, bs=16, max_batch=8, max_model_len=1024, reserve=1)
-    pool.allocate(999, 200)
+    s = SIDES[side](nblocks=400, bs=16, max_batch=8, max_model_len=1024, reserve=1)
+    s.allocate(999, 200)
     for r in range(8):
         s.submit(r, 200 + 50, 100, prefix_seq=999)
     p = s.step()
     assert list(p["prefill_first"]) == [200] * 8 and list(p["prefill_tokens"]) == [50] * 8
-    ps = pool.stats()
+    ps = s.pool_stats()
     assert ps["cow_copies"] == 8
     # 13 prefix blocks; each request: the copied partial block + ceil(251/16) - 13 more
     assert ps["used_blocks"] == 13 + 8 * (1 + (251 + 15) // 16 - 13)
