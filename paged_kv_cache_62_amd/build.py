@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = [os.path.join(CSRC, "pool.cpp"), os.path.join(CSRC, "sched.cpp"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("pool.cpp", "sched.cpp", "plan.cpp", "kernels.hip")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 HIPCC_FLAGS = [

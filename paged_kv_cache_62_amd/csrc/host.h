@@ -14,4 +14,7 @@ void set_last_error(const char* msg);
 // Tokens per block of a pool.
 int32_t pool_block_size(const pkv_pool* pool);
 
+// Blocks in a pool's free queue (O(1)).
+int64_t pool_free_blocks(const pkv_pool* pool);
+
 }  // namespace pkv

@@ -104,6 +104,10 @@ constexpr int32_t kMaxPartitionTokens = 4096;
 // True if the kernels cover this head_dim / group size.
 bool decode_supported(int head_dim, int group);
 
+// Compute units of the current HIP device (a partitioned GPU exposes fewer;
+// 256 if the device cannot be asked), queried once per device.
+int device_compute_units();
+
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 
 // Workspace: counters first (256-byte aligned), then the partials.

@@ -1,0 +1,45 @@
+// plan.cpp -- host-side sizes and device facts the decode launches are
+// planned with (workspace layout, supported shapes, compute units). Shared
+// by the host library (pool.cpp) and the kernel launchers (kernels.hip);
+// host code only.
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+int device_compute_units() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool decode_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
+}
+
+size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+}
+
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_partitions) {
+  if (max_partitions <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
+  return decode_counter_bytes(num_seqs, num_kv_heads) + rows * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+}  // namespace pkv

@@ -65,8 +65,10 @@ struct pkv_pool {
   std::vector<int32_t> ring;
   int64_t head = 0, count = 0;
   std::vector<int32_t> refcount;
+  int64_t shared = 0;                   // blocks with reference count > 1
   std::unordered_map<int64_t, Seq> seqs;
   int64_t cow_total = 0;
+  int32_t cus = 256;                    // compute units of the pool's device (planning)
   // device side
   int device = -1;
   char* arena = nullptr;
@@ -95,6 +97,17 @@ struct pkv_pool {
   void push_back(int32_t b) {
     ring[(head + count) % cfg.num_blocks] = b;
     ++count;
+  }
+  // The k-th block the next pops will return (k < count), without popping.
+  int32_t peek(int64_t k) const { return ring[(head + k) % cfg.num_blocks]; }
+  void add_ref(int32_t b) {
+    if (++refcount[b] == 2) ++shared;
+  }
+  // One reference less; a block reaching zero goes to the back of the queue.
+  void drop_ref(int32_t b) {
+    const int32_t r = --refcount[b];
+    if (r == 1) --shared;
+    if (r == 0) push_back(b);
   }
   pkv::LayerView layer_view(int32_t layer) const {
     pkv::LayerView lv{};
@@ -169,9 +182,46 @@ int64_t nblocks_for(int64_t len, int64_t bs) { return (len + bs - 1) / bs; }
 
 }  // namespace
 
+// Copy-on-write of one block into another, on `stream`: whole (block, head)
+// tiles of every layer and K/V, one 2-D copy per run of layers of one element
+// type (one row per (layer, K|V) slice); the FP16 staging tiles of a
+// seal-on-full pool the same way; then the scales and largest codes, one row
+// per (layer, K|V, scale|qmax).
+static hipError_t copy_block_async(pkv_pool* pool, int32_t old, int32_t fresh, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  const int32_t L = pool->cfg.num_layers;
+  for (int32_t l0 = 0; l0 < L && e == hipSuccess;) {
+    int32_t l1 = l0 + 1;
+    while (l1 < L && pool->ldt[l1] == pool->ldt[l0]) ++l1;
+    const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * elem_bytes(pool->ldt[l0]);
+    char* base = pool->arena + pool->layer_off[l0];
+    e = hipMemcpy2DAsync(base + (size_t)fresh * tile_bytes, pool->slice_bytes(l0),
+                         base + (size_t)old * tile_bytes, pool->slice_bytes(l0), tile_bytes,
+                         2 * (size_t)(l1 - l0), hipMemcpyDeviceToDevice, st);
+    l0 = l1;
+  }
+  if (e == hipSuccess && pool->tails) {  // staged FP16 rows: one slice per (INT8 layer, K|V)
+    int32_t n_i8 = 0;
+    for (int32_t l = 0; l < L; ++l) n_i8 += pool->tail_index[l] >= 0;
+    const size_t t16 = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * 2;
+    e = hipMemcpy2DAsync(pool->tails + (size_t)fresh * t16, pool->tail_slice,
+                         pool->tails + (size_t)old * t16, pool->tail_slice, t16, 2 * (size_t)n_i8,
+                         hipMemcpyDeviceToDevice, st);
+  }
+  if (e == hipSuccess && pool->scales) {
+    const size_t sc_row = (size_t)pool->cfg.num_kv_heads * sizeof(float);
+    const size_t sc_pitch = (size_t)pool->cfg.num_blocks * sc_row;
+    e = hipMemcpy2DAsync((char*)pool->scales + (size_t)fresh * sc_row, sc_pitch,
+                         (char*)pool->scales + (size_t)old * sc_row, sc_pitch, sc_row,
+                         4 * (size_t)L, hipMemcpyDeviceToDevice, st);
+  }
+  return e;
+}
+
 namespace pkv {
 void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
 int32_t pool_block_size(const pkv_pool* pool) { return pool->cfg.block_size; }
+int64_t pool_free_blocks(const pkv_pool* pool) { return pool->count; }
 }  // namespace pkv
 
 extern "C" {
@@ -224,6 +274,7 @@ pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
   if (!cfg->host_only) {
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
+    p->cus = pkv::device_compute_units();
     if (cfg->device_arena) {
       p->arena = (char*)cfg->device_arena;
     } else {
@@ -292,6 +343,11 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
       return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seqs[i]);
     ss[i] = &it->second;
   }
+  // The call's pops, in order, are the queue's first `need` entries: plan
+  // the copy-on-write targets (tracking reference counts that earlier
+  // sequences of this call release by copying) and count the blocks.
+  struct Cow { int32_t old, fresh; };
+  std::vector<Cow> cows;
   int64_t need = 0;
   std::unordered_map<int32_t, int32_t> released;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -300,7 +356,11 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
     const int64_t have = (int64_t)s.blocks.size();
     if (s.len % bs != 0) {  // first new token lands in the partly filled last block
       const int32_t b = s.blocks[have - 1];
-      if (pool->refcount[b] - released[b] > 1) { ++need; ++released[b]; }
+      if (pool->refcount[b] - released[b] > 1) {
+        if (need < pool->count) cows.push_back({b, pool->peek(need)});
+        ++need;
+        ++released[b];
+      }
     }
     need += nblocks_for(s.len + n_new[i], bs) - have;
   }
@@ -308,7 +368,14 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
     return fail(PKV_ERR_NO_FREE_BLOCK, "append needs %lld blocks, %lld free", (long long)need,
                 (long long)pool->count);
 
-  const hipStream_t st = (hipStream_t)stream;
+  // The copies go out before anything changes: if one cannot be enqueued the
+  // call fails with the pool as it was (the targets are still free blocks).
+  if (pool->arena)
+    for (const Cow& c : cows) {
+      const hipError_t e = copy_block_async(pool, c.old, c.fresh, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "copy-on-write copy");
+    }
+
   int64_t o = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     Seq& s = *ss[i];
@@ -316,45 +383,11 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_s
     if (s.len % bs != 0) {
       const int64_t j = (int64_t)s.blocks.size() - 1;
       const int32_t old = s.blocks[j];
-      if (pool->refcount[old] > 1) {
+      if (pool->refcount[old] > 1) {  // a planned copy: pops come in the planned order
         const int32_t fresh = pool->pop_front();
-        pool->refcount[old] -= 1;
+        pool->drop_ref(old);  // stays referenced (it was shared)
         s.blocks[j] = fresh;
         pool->cow_total += 1;
-        if (pool->arena) {
-          // whole (block, head) tiles of every layer and K/V: one 2-D copy per
-          // run of layers of one element type (one row per (layer, K|V)
-          // slice); then the scales and largest codes the same way, one row
-          // per (layer, K|V, scale|qmax)
-          hipError_t e = hipSuccess;
-          const int32_t L = pool->cfg.num_layers;
-          for (int32_t l0 = 0; l0 < L && e == hipSuccess;) {
-            int32_t l1 = l0 + 1;
-            while (l1 < L && pool->ldt[l1] == pool->ldt[l0]) ++l1;
-            const size_t tile_bytes = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * elem_bytes(pool->ldt[l0]);
-            char* base = pool->arena + pool->layer_off[l0];
-            e = hipMemcpy2DAsync(base + (size_t)fresh * tile_bytes, pool->slice_bytes(l0),
-                                 base + (size_t)old * tile_bytes, pool->slice_bytes(l0), tile_bytes,
-                                 2 * (size_t)(l1 - l0), hipMemcpyDeviceToDevice, st);
-            l0 = l1;
-          }
-          if (e == hipSuccess && pool->tails) {  // staged FP16 rows: one slice per (INT8 layer, K|V)
-            int32_t n_i8 = 0;
-            for (int32_t l = 0; l < L; ++l) n_i8 += pool->tail_index[l] >= 0;
-            const size_t t16 = (size_t)pool->cfg.num_kv_heads * pool->tile_elems * 2;
-            e = hipMemcpy2DAsync(pool->tails + (size_t)fresh * t16, pool->tail_slice,
-                                 pool->tails + (size_t)old * t16, pool->tail_slice, t16, 2 * (size_t)n_i8,
-                                 hipMemcpyDeviceToDevice, st);
-          }
-          if (e == hipSuccess && pool->scales) {
-            const size_t sc_row = (size_t)pool->cfg.num_kv_heads * sizeof(float);
-            const size_t sc_pitch = (size_t)pool->cfg.num_blocks * sc_row;
-            e = hipMemcpy2DAsync((char*)pool->scales + (size_t)fresh * sc_row, sc_pitch,
-                                 (char*)pool->scales + (size_t)old * sc_row, sc_pitch, sc_row,
-                                 4 * (size_t)L, hipMemcpyDeviceToDevice, st);
-          }
-          if (e != hipSuccess) return hip_fail(e, "copy-on-write copy");
-        }
       }
     }
     for (int64_t t = s.len; t < s.len + n_new[i]; ++t) {
@@ -373,7 +406,7 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child) {
   if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown parent %lld", (long long)parent);
   if (pool->seqs.count(child)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld already exists", (long long)child);
   Seq c = it->second;
-  for (int32_t b : c.blocks) pool->refcount[b] += 1;
+  for (int32_t b : c.blocks) pool->add_ref(b);
   pool->seqs.emplace(child, std::move(c));
   return ok();
 }
@@ -382,8 +415,7 @@ pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return ok();
-  for (int32_t b : it->second.blocks)
-    if (--pool->refcount[b] == 0) pool->push_back(b);
+  for (int32_t b : it->second.blocks) pool->drop_ref(b);
   pool->seqs.erase(it);
   return ok();
 }
@@ -422,11 +454,10 @@ pkv_status pkv_seq_length(const pkv_pool* pool, int64_t seq, int64_t* len_out) {
 
 pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
   if (!pool || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
-  int64_t used = 0, shared = 0;
-  for (int32_t r : pool->refcount) { used += r > 0; shared += r > 1; }
+  // every block is either in the free queue or referenced (conservation)
   out->free_blocks = pool->count;
-  out->used_blocks = used;
-  out->shared_blocks = shared;
+  out->used_blocks = pool->cfg.num_blocks - pool->count;
+  out->shared_blocks = pool->shared;
   out->cow_copies = pool->cow_total;
   out->num_seqs = (int64_t)pool->seqs.size();
   out->total_blocks = pool->cfg.num_blocks;
@@ -459,23 +490,24 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const voi
   return ok();
 }
 
-// Compute units of the device the kernels are built for, and how many decode
-// workgroups fit on the device at once (three per compute unit).
-constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kResidentWorkgroups = 3 * kComputeUnits;
+// Decode workgroups the device holds at once: three per compute unit (the
+// compute units of the pool's device, asked at creation; 256 for a host-only
+// pool).
+static int64_t resident_workgroups(const pkv_pool* pool) { return 3LL * pool->cus; }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t max_context_len) {
   const pkv_pool_config& c = pool->cfg;
   const int64_t pairs = (int64_t)num_seqs * c.num_kv_heads;
+  const int64_t cus = pool->cus;
   // Every compute unit has a (sequence, KV head) and contexts are short: one
   // partition per sequence, nothing to merge. Splitting would add the
   // partials' stores, the merge and more workgroup start-ups; measured with
   // INT8 GQA 32/8 decode steps (one partition vs the best split): 32 x 1024
   // tokens 17.5 vs 22.0 us, 64 x 1024 28.5 vs 37.5 us, 96 x 2000 74.6 vs
   // 81.9 us, 128 sequences of 200..1270 tokens 30.7 vs 38.9 us.
-  if (pairs >= kComputeUnits && max_context_len <= 2048) {
+  if (pairs >= cus && max_context_len <= 2048) {
     int32_t T = c.block_size;
     while (T < max_context_len) T *= 2;
     return T;
@@ -489,11 +521,11 @@ static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t ma
   while (T < 2048 && (int64_t)T * 2 * token_bytes <= 262144) T *= 2;
   // With several rounds of workgroups the longest one sets the tail: longer
   // partitions than 512 tokens only for long contexts.
-  if (T > 512 && pairs * ceil_div(max_context_len, T) > kResidentWorkgroups &&
+  if (T > 512 && pairs * ceil_div(max_context_len, T) > resident_workgroups(pool) &&
       max_context_len < 8 * T)
     T = 512;
   // At least one workgroup per compute unit.
-  while (T > 128 && pairs * ceil_div(max_context_len, T) < kComputeUnits) T /= 2;
+  while (T > 128 && pairs * ceil_div(max_context_len, T) < cus) T /= 2;
   if (T < c.block_size) T = c.block_size;
   return T;
 }
@@ -504,7 +536,7 @@ static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t ma
 static int32_t plan_fused_merge(const pkv_pool* pool, int32_t num_seqs, int32_t P, int32_t flags) {
   if (flags & PKV_DECODE_FUSED_MERGE) return 1;
   if (flags & PKV_DECODE_SEPARATE_MERGE) return 0;
-  return (int64_t)num_seqs * pool->cfg.num_kv_heads * P <= kResidentWorkgroups ? 1 : 0;
+  return (int64_t)num_seqs * pool->cfg.num_kv_heads * P <= resident_workgroups(pool) ? 1 : 0;
 }
 
 static bool valid_flags(int32_t flags) {

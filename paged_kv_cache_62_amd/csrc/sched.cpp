@@ -67,11 +67,7 @@ struct pkv_sched {
 
 namespace {
 
-int64_t free_blocks(const pkv_sched* s) {
-  pkv_stats ps{};
-  pkv_pool_stats(s->pool, &ps);
-  return ps.free_blocks;
-}
+int64_t free_blocks(const pkv_sched* s) { return pkv::pool_free_blocks(s->pool); }
 
 // New blocks the prompt of r takes at admission: its logical blocks minus
 // the full blocks of a shared prefix (a partly filled prefix block is copied

@@ -15,7 +15,9 @@ import weakref
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# The in-tree build; PKV_LIB names another build of the same C ABI (the
+# host-only sanitizer build the CPU tests make).
+LIB_PATH = os.environ.get("PKV_LIB") or os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1

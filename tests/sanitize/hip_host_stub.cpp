@@ -1,0 +1,80 @@
+// hip_host_stub.cpp -- host-memory stand-ins for the HIP runtime calls and
+// kernel launchers that the host library (pool.cpp, sched.cpp, plan.cpp)
+// makes, so that it can be built with g++ under AddressSanitizer and
+// UndefinedBehaviorSanitizer and exercised on a machine with no GPU.
+//
+// TEST INFRASTRUCTURE ONLY: linked into the sanitizer build that
+// tests/test_sanitizers.py makes, never into libpkv.so.
+//
+// "Device" memory is host memory: hipMalloc is calloc and the copies are
+// memcpy, so every copy-on-write copy is bounds-checked by ASan. The kernel
+// launchers do nothing and report hipErrorNotSupported. A host switch makes
+// hipMemcpy2DAsync fail after a given number of calls, to drive the
+// library's error paths from the host.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../paged_kv_cache_62_amd/csrc/kernels.h"
+
+namespace {
+int g_copies_left = -1;  // < 0: never fail
+}
+
+extern "C" {
+
+// After this call, n more hipMemcpy2DAsync calls succeed and every further
+// one fails; n < 0 turns failures off.
+void pkv_stub_fail_copies_after(int n) { g_copies_left = n; }
+
+hipError_t hipGetDevice(int* device) {
+  *device = 0;
+  return hipSuccess;
+}
+
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+  *value = 256;
+  return hipSuccess;
+}
+
+hipError_t hipMalloc(void** ptr, size_t size) {
+  *ptr = std::calloc(size ? size : 1, 1);
+  return *ptr ? hipSuccess : hipErrorOutOfMemory;
+}
+
+hipError_t hipFree(void* ptr) {
+  std::free(ptr);
+  return hipSuccess;
+}
+
+hipError_t hipMemcpy(void* dst, const void* src, size_t bytes, hipMemcpyKind) {
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                            size_t height, hipMemcpyKind, hipStream_t) {
+  if (g_copies_left == 0) return hipErrorInvalidValue;
+  if (g_copies_left > 0) --g_copies_left;
+  for (size_t r = 0; r < height; ++r)
+    std::memcpy((char*)dst + r * dpitch, (const char*)src + r * spitch, width);
+  return hipSuccess;
+}
+
+hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
+
+const char* hipGetErrorString(hipError_t) { return "stub HIP runtime"; }
+
+}  // extern "C"
+
+namespace pkv {
+
+hipError_t launch_append(const LayerView&, const void*, const void*, int, const int64_t*, int32_t, hipStream_t) {
+  return hipErrorNotSupported;
+}
+hipError_t launch_decode(const DecodeLaunch&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prefill(const PrefillLaunch&, hipStream_t) { return hipErrorNotSupported; }
+
+}  // namespace pkv
