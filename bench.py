@@ -87,6 +87,10 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (reference for HBM byte counters)")
+    ap.add_argument("--extra", default="auto",
+                    help="comma-separated decode workloads also timed in this run and reported under "
+                         "'extra_workloads' (no CPU baseline); 'auto' = llama29,llama128 after the default "
+                         "qwen workload, 'none' = no others")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     return ap.parse_args()
@@ -195,9 +199,9 @@ class Workload:
             self.suffix = mix_suffix_lengths(seed, self.B)
             lens0 = 200 + self.suffix
         else:
-            # the first timed step (after `warmup` steps) decodes at ctx
+            # the first step after `warmup` appends decodes at ctx
             lens0 = np.full(self.B, c["ctx"] - 1 - warmup, dtype=np.int64)
-        appends = steps_total  # one new slot per sequence per step (shared by all layers)
+        appends = steps_total  # host_prep() calls: one new slot per sequence each (shared by all layers)
         need = int(sum((int(n) + appends + self.bs - 1) // self.bs for n in lens0)) + 8
         nblocks = c["nblocks"] if c["nblocks"] is not None else need
         if need > nblocks:
@@ -437,7 +441,38 @@ def main():
         res["cpu_baseline"] = base(res.pop("_workload"), args.cpu_seconds)
     else:
         res.pop("_workload")
+    extra = extra_workloads(args)
+    if extra:
+        res["extra_workloads"] = {}
+        for name in extra:
+            # the previous workload's pool is released before the next is built
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**{**vars(args), "config": name, "partition": 0})
+            with torch.cuda.stream(stream):
+                r = run(sub, stream)
+            r.pop("_workload")
+            res["extra_workloads"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup",
+                                                              "dtype", "config", "roofline")}
+            print(f"# {name}: {r['value']:.1f} tokens/s, frac {r['roofline']['frac']:.3f}",
+                  file=sys.stderr, flush=True)
+            del r
     print(json.dumps(res), flush=True)
+
+
+def extra_workloads(args):
+    """Decode workloads timed after the main one in the same run: by default
+    the two Llama-2-7B shapes ("vLLM核心概念" §3.1 and §3.5) after the default
+    Qwen3-TTS-talker workload, so one run measures both shapes the target names."""
+    if args.extra == "none":
+        return []
+    if args.extra == "auto":
+        return ["llama29", "llama128"] if args.config == "qwen" else []
+    names = [x for x in args.extra.split(",") if x]
+    bad = [x for x in names if x not in CONFIGS]
+    if bad:
+        sys.exit(f"--extra: unknown decode workloads {bad}; choose from {sorted(CONFIGS)}")
+    return names
 
 
 def run(args, stream):
@@ -445,8 +480,13 @@ def run(args, stream):
     from paged_kv_cache_62_amd import pkv
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
     merge_flags = {"auto": 0, "fused": pkv.PKV_DECODE_FUSED_MERGE, "separate": pkv.PKV_DECODE_SEPARATE_MERGE}
-    w = Workload(args.config, args.warmup + args.steps, args.partition, flags=merge_flags[args.merge],
-                 fused=not args.unfused, warmup=args.warmup)
+    # Every host_prep() appends one token per sequence: the one before graph
+    # capture, the warm-up steps and the timed steps. The workload sizes its
+    # lengths and max_context_len for exactly that many, so the first timed
+    # step decodes at the configured context and no step exceeds the capacity.
+    pre = args.warmup + (0 if args.no_graph else 1)
+    w = Workload(args.config, pre + args.steps, args.partition, flags=merge_flags[args.merge],
+                 fused=not args.unfused, warmup=pre)
     graphs = {}
     if not args.no_graph:
         # The device work of a step, captured once as a HIP graph per layer
@@ -463,6 +503,8 @@ def run(args, stream):
     def run_step():
         i = w.step_i
         lens = w.host_prep()
+        if int(lens.max()) > w.max_ctx:  # the decode calls' contract: len <= max_context_len
+            raise RuntimeError(f"step {i}: length {int(lens.max())} exceeds max_context_len {w.max_ctx}")
         key = tuple(w.decode_layers(i))
         if graphs:
             graphs[key].replay()

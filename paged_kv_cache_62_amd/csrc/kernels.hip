@@ -37,7 +37,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -598,8 +597,12 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   }
 
   // Lengths beyond what the table or the grid covers are clamped, so a bad
-  // length cannot send a load outside the cache or the workspace.
+  // length cannot send a load outside the cache or the workspace. A decode
+  // step whose length was clamped appends nothing: its new token (position
+  // raw_len - 1) lies outside what this launch covers, and writing it at
+  // len - 1 would overwrite a cached row.
   const int len = min(raw_len, min(maxb * bs, a.max_partitions * T));
+  const bool step_fits = APPEND && raw_len == len;  // wave-uniform (one length per sequence)
   const int t1 = min(len, t0 + T);  // t0 >= len (nothing to do): nu = 0 below
   const int nparts = (len + T - 1) / T;
   const int u1 = (t1 + kUnit - 1) / kUnit;
@@ -620,7 +623,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     // but holds none of its blocks)
     if (t0 < len && t1 == len && (nbl & (kWaves - 1)) == wave) {
       if (r > 0) ntail = (r + kUnit - 1) / kUnit;
-      else if (APPEND) ntail = bs / kUnit;
+      else if (step_fits) ntail = bs / kUnit;
     }
   }
   const int nu8 = nu - ntail;  // units read through the ring
@@ -692,7 +695,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   const int nb_rel = (pos >> (lupb + 4)) - (u0 >> lupb);  // the new token's block within the partition
   const int i_new = (nb_rel >> 2) << lupb;  // owner: its unit index of that block's first unit
   const int row0 = pos & (bs - 1);          // the new token's row in its block
-  bool owner = APPEND && !SEAL && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
+  bool owner = step_fits && !SEAL && pos >= t0 && pos < t1 && (nb_rel & (kWaves - 1)) == wave;  // wave-uniform
   int a_entry = 0;
   constexpr int NPL = D / 64;  // new-row elements per lane: dims lane + 64*k
   float nk[NPL], nv[NPL];
@@ -1262,12 +1265,13 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   }
 
   if constexpr (SEAL && APPEND) {
-    if (ntail > 0) {  // wave-uniform
+    if (ntail > 0 && step_fits) {  // wave-uniform
       seal_step_stage();
       seal_step_decode();
     }
-  } else if constexpr (SEAL) {
-    if (ntail > 0) {  // wave-uniform: the FP16 tail, after the INT8 units
+  }
+  if constexpr (SEAL) {
+    if (ntail > 0 && !step_fits) {  // wave-uniform: the FP16 tail, after the INT8 units
       const int blk = min(max(__builtin_amdgcn_readlane(tentry, nu - 1), 0), a.lv.num_blocks - 1);
       const size_t tile16 = (size_t)bs * D * 2;
       const char* tk = (const char*)a.lv.tail_k + ((size_t)blk * hkv + g) * tile16;
@@ -1503,20 +1507,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeLaunch
 }
 
 
-// Compute units of the current device (a partitioned GPU exposes fewer),
-// asked once per device.
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 template <int D>
 void launch_merge(const DecodeLaunch& d, int chunk, dim3 grid, hipStream_t stream) {
   if (chunk == 16)
@@ -1534,7 +1524,7 @@ void launch_one(const DecodeLaunch& d, hipStream_t stream) {
   if constexpr (I8) {
     if (step && d.lv.seal)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true, true>), grid, dim3(kThreads), 0, stream, d);
-    else if (step && (int64_t)grid.x * grid.y * grid.z > 3LL * device_cus())  // more than one round
+    else if (step && (int64_t)grid.x * grid.y * grid.z > 3LL * device_compute_units())  // more than one round
       hipLaunchKernelGGL((decode_step_kernel_i8_many<D, G, QT>), grid, dim3(kThreads), 0, stream, d);
     else if (step)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true>), grid, dim3(kThreads), 0, stream, d);
@@ -1960,7 +1950,7 @@ template <bool I8, int D, int G>
 hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
   const int64_t tiles = (p.max_query_len + 16 / G - 1) / (16 / G);
   const int64_t wg4 = (tiles + 3) / 4 * p.lv.num_kv_heads * p.num_seqs;
-  return wg4 <= 2 * (int64_t)device_cus() ? launch_prefill_w<I8, D, G, 8>(p, stream)
+  return wg4 <= 2 * (int64_t)device_compute_units() ? launch_prefill_w<I8, D, G, 8>(p, stream)
                                           : launch_prefill_w<I8, D, G, 4>(p, stream);
 }
 
@@ -1974,24 +1964,7 @@ hipError_t launch_prefill_g(const PrefillLaunch& p, int group, hipStream_t strea
   }
 }
 
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
-
-bool decode_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
-}
-
-size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
-}
-
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t max_partitions) {
-  if (max_partitions <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
-  return decode_counter_bytes(num_seqs, num_kv_heads) + rows * (2 + (size_t)head_dim) * sizeof(float);
-}
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   const int group = d.num_q_heads / d.lv.num_kv_heads;

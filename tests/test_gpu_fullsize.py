@@ -7,8 +7,11 @@ max_context_len), and check
   * the step's append bit for bit: the touched blocks read back before the
     step, pushed through the oracle's quantizer / binary16 rounding with the
     step's K/V, must equal the blocks read back after it;
-  * decode outputs of sampled sequences (all their query heads) against the
-    FP64 oracle over the GPU's read-back cache, in the first and last layer.
+  * the step's own output (pkv_decode_step of the last decoded layer, the
+    launch the benchmark times) for sampled sequences, all query heads,
+    against the FP64 oracle over the GPU's read-back cache after the step;
+  * plain decode outputs of sampled sequences (all their query heads) against
+    the FP64 oracle over the GPU's read-back cache, in the first and last layer.
 """
 import gc
 
@@ -65,6 +68,9 @@ def test_full_size_step(gpu, cfg):
         before = {l: w.pool.read_blocks(l, blocks) for l in layers_checked}
         w.device_step(list(w.decode_layers(0)))
         torch.cuda.synchronize()
+        # what bench.py times: the step's last decoded layer, as pkv_decode_step left it in w.out
+        step_layer = list(w.decode_layers(0))[-1]
+        step_out = w.out.cpu().numpy().copy()
         for l in layers_checked:
             knew = synth.as_f32(w.knew[l].cpu())
             vnew = synth.as_f32(w.vnew[l].cpu())
@@ -87,6 +93,20 @@ def test_full_size_step(gpu, cfg):
         table, lens = w.pool.block_table(w.seqs, w.max_blocks)
         d_table = torch.from_numpy(table).cuda()
         d_lens = torch.from_numpy(lens).cuda()
+
+        # the decode step's own output (append + decode + merge in one launch)
+        # against the FP64 oracle over the cache it left behind
+        sub_blocks = sorted({int(b) for s in sample for b in table[s, :(int(lens[s]) + bs - 1) // bs]})
+        shape = H.Shape(layers=w.L, hq=w.hq, hkv=w.hkv, dim=w.dim, bs=bs, nblocks=w.nblocks,
+                        kv_dtype=_kv_code(w, step_layer))
+        kc, vc, ks, vs = H.gpu_layer_arrays(w.pool, step_layer, sub_blocks, shape)
+        q = synth.as_f32(w.q[step_layer].cpu())[sample]
+        ref = orc.decode_attention(_kv_code(w, step_layer), kc, vc, ks, vs, q, table[sample], lens[sample], w.scale)
+        got = step_out[sample]
+        max_abs, max_rel = H.attention_errors(got, ref)
+        print(f"[fullsize] {cfg} decode-step output, layer {step_layer} seqs {sample}: "
+              f"max_abs={max_abs:.3e} max_rel={max_rel:.3e}", flush=True)
+        H.assert_attention_close(got, ref)
         dlayers = [l for l in layers_checked if l in set(w.decode_layers(0)) | set(w.decode_layers(1))]
         for l in dlayers:
             out = torch.empty(w.B, w.hq, w.dim, dtype=torch.float32, device="cuda")
