@@ -127,7 +127,9 @@ pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t n_tokens, int64
  * (all layers, K and V, codes and scales) into it, enqueued on `stream`
  * (copy-on-write, "vLLM核心概念" §3.2). slots_out (host, sum(n_new) entries,
  * may be NULL) receives the slots in the same order. All-or-nothing:
- * PKV_ERR_NO_FREE_BLOCK if the queue cannot serve the whole call. */
+ * PKV_ERR_NO_FREE_BLOCK if the queue cannot serve the whole call, or
+ * PKV_ERR_DEVICE if a copy cannot be enqueued (the copies are enqueued
+ * before anything changes). */
 pkv_status pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                                 const int32_t* n_new, int64_t* slots_out, void* stream);
 
@@ -264,6 +266,26 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                            float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launch, with the library's own scratch in place of a
+ * caller's workspace; it calls no allocator. The scratch is one device array
+ * of 16 MiB per GPU the library runs on (found and zero-filled when the
+ * first pool is created on that device, held until the process ends); every
+ * call leaves its arrival counters at zero again. All calls on one GPU share
+ * it: calls that may overlap in time on one GPU (other streams, other
+ * threads) race and must not be made.
+ *   Arguments as pkv_decode_step, without workspace and workspace_bytes.
+ *   PKV_ERR_INVALID_ARG (nothing launched) when these sizes need more than
+ *   16 MiB of workspace (pkv_decode_workspace_bytes); PKV_ERR_DEVICE if the
+ *   scratch of the pool's device was not set up. */
+pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                                   const void* v_new, pkv_dtype dtype, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                   float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
+                                   void* stream);
 
 /* Chunked prefill attention over one layer ("轻量级推理引擎实战" §一: prefill
  * processes a prompt's tokens in parallel, then decode adds one at a time).

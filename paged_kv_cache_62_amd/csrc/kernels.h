@@ -115,4 +115,13 @@ size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t max_partitions);
 
+// The library's own decode workspace for callers that cannot allocate: a
+// device array of kScratchBytes on every GPU the library runs on, zero-filled
+// once. scratch_setup() finds its address on the current device (once per
+// device; call it with that device current); scratch_ptr() returns it, or
+// null before set-up. Calls that use it on one GPU share it.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+hipError_t scratch_setup();
+void* scratch_ptr(int device);
+
 }  // namespace pkv

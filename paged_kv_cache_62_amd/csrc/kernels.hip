@@ -37,6 +37,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1965,6 +1966,40 @@ hipError_t launch_prefill_g(const PrefillLaunch& p, int group, hipStream_t strea
 }
 
 }  // namespace
+
+// Decode workspace owned by the library (arrival counters, then partition
+// partials, as in a caller's workspace), for pkv_decode_step_noalloc. In host
+// code `scratch` names a host-side stand-in, not device memory: host code
+// uses only the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch[64];  // per device: the array's device address, once found
+}  // namespace
+
+hipError_t scratch_setup() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return hipSuccess;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  // the arrival counters must start at zero (every call leaves them so)
+  e = hipMemset(ptr, 0, kScratchBytes);
+  if (e != hipSuccess) return e;
+  g_scratch[dev] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
+}
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   const int group = d.num_q_heads / d.lv.num_kv_heads;

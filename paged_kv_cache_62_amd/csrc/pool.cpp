@@ -275,6 +275,9 @@ pkv_status pkv_pool_create(const pkv_pool_config* cfg, pkv_pool** out) {
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
     p->cus = pkv::device_compute_units();
+    // the library's decode scratch on this device (pkv_decode_step_noalloc)
+    e = pkv::scratch_setup();
+    if (e != hipSuccess) { delete p; return hip_fail(e, "decode scratch set-up"); }
     if (cfg->device_arena) {
       p->arena = (char*)cfg->device_arena;
     } else {
@@ -663,6 +666,38 @@ pkv_status pkv_decode_step(pkv_pool* pool, int32_t layer, const void* q, const v
   return decode_launch(pool, layer, q, dtype, num_q_heads, k_new, v_new, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len, softmax_scale,
                        partition_tokens, flags, out, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                                   const void* v_new, pkv_dtype dtype, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                   float softmax_scale, int32_t partition_tokens, int32_t flags, float* out,
+                                   void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  if (num_q_heads < 1 || max_context_len < 1 || num_seqs < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d, max_context_len %d, num_seqs %d", num_q_heads,
+                max_context_len, num_seqs);
+  if (num_seqs == 0) return ok();
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % pool->cfg.block_size != 0) ||
+      partition_tokens > pkv::kMaxPartitionTokens)
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d is not a multiple of block_size %d in [0, %d]",
+                partition_tokens, pool->cfg.block_size, pkv::kMaxPartitionTokens);
+  const int32_t T = partition_tokens > 0 ? partition_tokens : auto_partition(pool, num_seqs, max_context_len);
+  const int32_t P = (max_context_len + T - 1) / T;
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, pool->cfg.num_kv_heads,
+                                                  pool->cfg.head_dim, P);
+  if (need > pkv::kScratchBytes)
+    return fail(PKV_ERR_INVALID_ARG,
+                "pkv_decode_step_noalloc: these sizes need %zu bytes of workspace, the library's scratch holds %zu",
+                need, pkv::kScratchBytes);
+  void* ws = pkv::scratch_ptr(pool->device);
+  if (!ws) return fail(PKV_ERR_DEVICE, "decode scratch of device %d is not set up", pool->device);
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL k_new or v_new");
+  return decode_launch(pool, layer, q, dtype, num_q_heads, k_new, v_new, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, softmax_scale, partition_tokens, flags, out,
+                       ws, pkv::kScratchBytes, stream);
 }
 
 pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,

@@ -103,6 +103,8 @@ SIGNATURES = {
                                        _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_decode_step": (C.c_int, [_vp, _i32, _vp, _vp, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
                                   _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_decode_step_noalloc": (C.c_int, [_vp, _i32, _vp, _vp, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
+                                          _f32, _i32, _i32, _vp, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "pkv_sched_create": (C.c_int, [_vp, _vp, _vp]),
     "pkv_sched_destroy": (None, [_vp]),
@@ -302,6 +304,22 @@ def pkv_decode_step(h, layer, q, k_new, v_new, block_tables, context_lens, max_c
         ws_ptr, ws_bytes, _stream_ptr(stream)))
 
 
+def pkv_decode_step_noalloc(h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                            softmax_scale, out, partition_tokens=0, stream=None, flags=0) -> None:
+    """pkv_decode_step with the library's own scratch as the workspace (it
+    allocates nothing); arguments as pkv_decode_step without the workspace."""
+    for t in (q, k_new, v_new, block_tables, context_lens, out):
+        assert t.is_contiguous()
+    assert k_new.dtype == q.dtype and v_new.dtype == q.dtype and out.dtype.itemsize == 4
+    B, hq, _ = q.shape
+    assert k_new.shape[0] == B and v_new.shape == k_new.shape
+    _check(lib().pkv_decode_step_noalloc(
+        h, layer, _vp(q.data_ptr()), _vp(k_new.data_ptr()), _vp(v_new.data_ptr()), _torch_dtype_code(q), hq,
+        _vp(block_tables.data_ptr()), int(block_tables.shape[1]), _vp(context_lens.data_ptr()), B,
+        int(max_context_len), float(softmax_scale), int(partition_tokens), int(flags), _vp(out.data_ptr()),
+        _stream_ptr(stream)))
+
+
 def pkv_read_blocks(h, layer: int, blocks, num_kv_heads: int, block_size: int, head_dim: int,
                     kv_dtype: int):
     """Host copy of blocks in canonical order: codes [n][2][Hkv][bs][d], scales [n][2][Hkv]."""
@@ -437,6 +455,13 @@ class Pool:
             workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=q.device)
         pkv_decode_step(self.h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
                         softmax_scale, out, workspace, partition_tokens, stream, flags)
+        return out
+
+    def decode_step_noalloc(self, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                            softmax_scale, out, partition_tokens=0, stream=None, flags=0):
+        """pkv_decode_step on the library's own scratch: no workspace, nothing allocated."""
+        pkv_decode_step_noalloc(self.h, layer, q, k_new, v_new, block_tables, context_lens, max_context_len,
+                                softmax_scale, out, partition_tokens, stream, flags)
         return out
 
     def prefill(self, layer, q, query_start, max_query_len, block_tables, context_lens, softmax_scale,

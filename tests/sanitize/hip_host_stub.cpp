@@ -76,5 +76,7 @@ hipError_t launch_append(const LayerView&, const void*, const void*, int, const 
 }
 hipError_t launch_decode(const DecodeLaunch&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill(const PrefillLaunch&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t scratch_setup() { return hipSuccess; }
+void* scratch_ptr(int) { return nullptr; }
 
 }  // namespace pkv
