@@ -41,17 +41,24 @@ TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "prefill512": "profiles/prefill_kernel_qwen3_tts_chunk512_int8.md"}
 
 
-def kernels_code_hash(path=None):
-    """sha256 of kernels.hip (or `path`) with comments and whitespace
-    removed: it changes when the kernels' code does, not when their
-    comments do."""
+KERNEL_SOURCES = ("device.h", "append.hip", "decode.hip", "prefill.hip")
+
+
+def code_hash(text):
+    """sha256 of source text with comments and whitespace removed: it changes
+    when the code does, not when its comments do."""
     import hashlib
     import re
-    path = path or os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", "kernels.hip")
-    src = open(path, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
+def kernels_code_hash():
+    """code_hash of the kernel sources (device.h, append.hip, decode.hip,
+    prefill.hip, concatenated in that order)."""
+    return code_hash("\n".join(open(os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", name),
+                                    encoding="utf-8").read() for name in KERNEL_SOURCES))
 
 
 def measured_traffic(config):

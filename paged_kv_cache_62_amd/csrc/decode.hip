@@ -1,8 +1,5 @@
-// kernels.hip -- gfx950 kernels of libpkv.
+// decode.hip -- decode kernels of libpkv for gfx950.
 //
-//  H1 append:  store new tokens' K/V at their slots; binary16 rounding, or the
-//              per-(block, KV head) symmetric INT8 quantizer of
-//              "轻量级推理引擎实战：KV Cache 量化与连续批处理的底层优化" §三.
 //  H2 decode:  split-context decode attention ("vLLM核心概念" §3.1: the new
 //              query against every cached key/value; §3.2: logical token t in
 //              block table[t / bs], row t % bs). One workgroup per (sequence,
@@ -14,9 +11,6 @@
 //  Decode step: H1 of each sequence's new token folded into H2 (one launch
 //              per layer); the INT8 step has a second variant for grids the
 //              device cannot hold at once.
-//  Prefill:    causal attention of each sequence's newest tokens over its
-//              context ("轻量级推理引擎实战" §一), on the same matrix-core
-//              contractions with the context staged once per workgroup in LDS.
 //
 // Both contractions of H2 run on the matrix cores, 16 tokens at a time:
 //   S^T[token][col] = K[token][:] . Q^T[:][col]      (A = K rows from HBM)
@@ -35,495 +29,12 @@
 // Scores are in base 2 (softmax_scale * log2 e folded in) so exp2 is one
 // instruction.
 
-#include <hip/hip_runtime.h>
+#include "device.h"
 
 #include <mutex>
-#include <type_traits>
-#include <utility>
-
-#include "kernels.h"
-
 
 namespace pkv {
 namespace {
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order: a
-// loop whose index is a compile-time constant in every body, so that arrays
-// indexed by it stay in registers.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
-
-constexpr int kWaves = 4;             // wavefronts per decode workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kUnit = 16;             // tokens per unit of work (one MFMA tile of tokens)
-constexpr int kRsrcWord3 = 0x00020000; // buffer descriptor word 3 for untyped dword loads (gfx9 family)
-// sched_barrier mask: ALU, VALU, SALU and MFMA instructions may be scheduled
-// across the barrier; memory instructions may not.
-constexpr int kSchedAluOnly = 0x000F;
-constexpr int kSlack = 4;              // the running max may trail the true maximum by this much (log2)
-// The longest partition is 4 wavefronts x 64 units of 16 tokens, so one lane
-// per unit holds a wavefront's bookkeeping.
-static_assert(kMaxPartitionTokens == kWaves * 64 * kUnit, "partition bound");
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ float f16_to_f32(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-template <int DT>
-__device__ __forceinline__ float load_elem(const void* p, size_t i) {
-  if constexpr (DT == kF32) return ((const float*)p)[i];
-  else if constexpr (DT == kF16) return f16_to_f32(((const uint16_t*)p)[i]);
-  else return bf16_to_f32(((const uint16_t*)p)[i]);
-}
-
-// DPP moves inside a row of 16 lanes; lanes that would read outside the row
-// read 0 (bound_ctrl).
-constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141; // lane i <- 7-i within 8
-constexpr int kMirror = 0x140;     // lane i <- 15-i within 16
-constexpr int kRowShl4 = 0x104;    // lane i <- i+4
-constexpr int kRowShl8 = 0x108;    // lane i <- i+8
-constexpr int kRowShr8 = 0x118;    // lane i <- i-8
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
-}
-
-// Maximum over all 64 lanes, returned wave-uniform.
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f<kQuadXor1>(x));
-  x = fmaxf(x, dpp_f<kQuadXor2>(x));
-  x = fmaxf(x, dpp_f<kHalfMirror>(x));
-  x = fmaxf(x, dpp_f<kMirror>(x));
-  const int b = __builtin_bit_cast(int, x);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-// Combine the four 16-lane rows holding the same column: lane l with lanes
-// l^16, l^32, l^48 (the swaps exchange whole rows between two registers).
-__device__ __forceinline__ float max_over_lane_groups(float x) {
-  const int b = __builtin_bit_cast(int, x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  x = fmaxf(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
-  const int c = __builtin_bit_cast(int, x);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
-}
-__device__ __forceinline__ float sum_over_lane_groups(float x) {
-  const int b = __builtin_bit_cast(int, x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  x = __builtin_bit_cast(float, (int)r16[0]) + __builtin_bit_cast(float, (int)r16[1]);
-  const int c = __builtin_bit_cast(int, x);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return __builtin_bit_cast(float, (int)r32[0]) + __builtin_bit_cast(float, (int)r32[1]);
-}
-
-__device__ __forceinline__ int wave_max_int(int x) {
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
-  return x;
-}
-
-// A float that is wave-uniform by construction, moved to a scalar register.
-__device__ __forceinline__ float uniform_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-
-// A pointer the compiler can treat as wave-uniform (it is, by construction,
-// wherever this is used): buffer descriptors must live in scalar registers,
-// and a value it cannot prove uniform costs a loop over the lanes per load.
-__device__ __forceinline__ void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (void*)(((uint64_t)hi << 32) | lo);
-}
-
-// INT8 V codes are stored biased (code + 128, i.e. code ^ 0x80). Four of them
-// -> four fp16 codes, exactly: each byte becomes the low mantissa byte of
-// 1024.0 (0x6400), giving 1152 + code, and 1152 is subtracted. (Leaving the
-// 1152 in and removing 1152 * sum(P) after the product would save the two
-// subtractions, but the fp32 accumulators would then carry ~1152/|code|
-// times the signal and its rounding error.)
-__device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
-  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
-  return f16x4{a[0], a[1], b[0], b[1]};
-}
-
-// x0, x1 as binary16 pairs hi + lo: hi is x rounded toward zero (one
-// conversion instruction, which the compiler cannot fuse with anything, so
-// every use sees the same hi) and lo = x - hi rounded to nearest; hi + lo
-// carries about 22 significant bits.
-__device__ __forceinline__ void split_f16x2(float x0, float x1, f16x2& hi, f16x2& lo) {
-  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  lo = f16x2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
-}
-
-// ---------------------------------------------------------------------------
-// H1 (binary16 cache): one thread per (token, head, K|V, 8-element chunk);
-// each value rounded to binary16, ties to even.
-// ---------------------------------------------------------------------------
-// Chunk ch (8 elements) of token i's row of head h, K (kv 0) or V (kv 1),
-// into row `row` of block blk.
-template <int IN>
-__device__ __forceinline__ void append_f16_chunk(const LayerView& lv, int kv, int h, int64_t blk, int row,
-                                                 const void* src, int64_t i, int ch) {
-  const int D = lv.head_dim;
-  const int hkv = lv.num_kv_heads;
-  const size_t sbase = ((size_t)i * hkv + h) * D + ch * 8;
-  uint16_t hv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    hv[e] = __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, sbase + e));
-  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
-                   ((size_t)blk * hkv + h) * lv.block_size * D;
-  if (kv == 0) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)hv[2 * e] | ((uint32_t)hv[2 * e + 1] << 16);
-    *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[v_tile_offset(row, ch * 8 + e, D)] = hv[e];
-  }
-}
-
-template <int IN>
-__global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, const void* k,
-                                                         const void* v, const int64_t* slots,
-                                                         int32_t n) {
-  const int hkv = lv.num_kv_heads;
-  const int chunks = lv.head_dim / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n * hkv * 2 * chunks) return;
-  const int ch = (int)(idx % chunks);
-  int64_t rest = idx / chunks;
-  const int h = (int)(rest % hkv);
-  rest /= hkv;
-  const int kv = (int)(rest & 1);
-  const int64_t i = rest >> 1;
-  const int64_t slot = slots[i];
-  const int64_t blk = slot / lv.block_size;
-  const int row = (int)(slot % lv.block_size);
-  if (slot < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  append_f16_chunk<IN>(lv, kv, h, blk, row, kv ? v : k, i, ch);
-}
-
-// ---------------------------------------------------------------------------
-// H1 (int8 cache): one wavefront per (run, head, K|V), where a run is the
-// maximal group of consecutive tokens that land in one block. Only the
-// wavefront of a run's first token works, so every (block, head, K|V) tile
-// has a single writer and no atomics are needed.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float scale_of(float max_abs) {
-  return max_abs > 1e-6f ? max_abs / 127.0f : 1.0f;
-}
-__device__ __forceinline__ int8_t encode(float x, float scale) {
-  const float y = x / scale;  // IEEE binary32 division (correctly rounded)
-  const float rr = fminf(fmaxf(rintf(y), -127.0f), 127.0f);  // rintf: ties to even
-  return (int8_t)(int)rr;
-}
-// Re-encode the bytes of a word of codes selected by `mask` from scale s_old
-// to s_new (the bytes are stored XOR bias4).
-__device__ __forceinline__ uint32_t requant_word(uint32_t w, uint32_t mask, float s_old, float s_new,
-                                                 uint32_t bias4) {
-  uint32_t x = w ^ bias4;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (mask & (0xFFu << (8 * b))) {
-      const int code = (int)(int8_t)(x >> (8 * b));
-      const uint32_t q = (uint32_t)(uint8_t)encode((float)code * s_old, s_new);
-      x = (x & ~(0xFFu << (8 * b))) | (q << (8 * b));
-    }
-  }
-  return x ^ bias4;
-}
-
-// One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
-// head h, K (kv 0) or V (kv 1), at rows row0 .. row0+nr-1 of block blk:
-// grow-only scale, old rows re-encoded when it grows (P5 section 3 plus the
-// rule for partly filled blocks). issue() sends every load without waiting
-// (the block's old codes, rows < row0, 16 bytes per load; its scale; up to
-// kPre new values per lane), so a wavefront can have the K and the V append
-// in flight together; finish() does the rest and returns the new scale.
-// Old rows of a K tile are its first row0*D bytes; those of a V tile lie in
-// its first ceil(row0/16) 16-token sub-tiles, where each byte's token is
-// decoded from its offset.
-template <int IN>
-struct I8Append {
-  static constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
-  static constexpr int kPre = 2;        // new values held per lane (one row of d <= 128)
-  const LayerView* lv;
-  int kv, h, row0, nr;
-  int64_t i;
-  const void* src;
-  int8_t* tile;
-  float* sp;
-  int32_t* qp;
-  int old_bytes;
-  uint4 oc[kMaxChunks];
-  float s_old;
-  float pre[kPre];
-
-  __device__ __forceinline__ void issue(const LayerView& lv_, int kv_, int h_, int64_t blk, int row0_, int nr_,
-                                        const void* src_, int64_t i_) {
-    lv = &lv_; kv = kv_; h = h_; row0 = row0_; nr = nr_; src = src_; i = i_;
-    const int lane = threadIdx.x & 63;
-    const int hkv = lv_.num_kv_heads, D = lv_.head_dim, ld = __builtin_ctz(D);
-    tile = (int8_t*)(kv ? lv_.v_codes : lv_.k_codes) + ((size_t)blk * hkv + h) * lv_.block_size * D;
-    sp = (kv ? lv_.v_scales : lv_.k_scales) + (size_t)blk * hkv + h;
-    qp = (kv ? lv_.v_qmax : lv_.k_qmax) + (size_t)blk * hkv + h;
-    old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
-#pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) {
-      const int c = lane + 64 * k;
-      oc[k] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    s_old = row0 > 0 ? *sp : 1.f;
-    if (nr * D <= 64 * kPre) {
-#pragma unroll
-      for (int k = 0; k < kPre; ++k) {
-        const int e = lane + 64 * k;
-        pre[k] = e < nr * D ? load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))) : 0.f;
-      }
-    }
-  }
-
-  __device__ __forceinline__ float finish() {
-    const int lane = threadIdx.x & 63;
-    const int hkv = lv->num_kv_heads, D = lv->head_dim, ld = __builtin_ctz(D);
-    const uint32_t bias4 = kv ? 0x80808080u : 0u;  // V codes are stored biased by 128 (code ^ 0x80)
-    auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
-    // Bytes of chunk k that hold rows < row0, as a mask over each of its four
-    // words (the same for all four). A K chunk lies in one row. A V chunk
-    // lies in one lane's slice of a 16-token sub-tile (d/4 >= 16 bytes):
-    // tokens base + byte % 4 with base = 16*sub + 4*tg.
-    auto word_mask = [&](int k) -> uint32_t {
-      const int c = lane + 64 * k;
-      if (c * 16 >= old_bytes) return 0u;
-      if (!kv) return ~0u;
-      const int byte = c * 16;
-      const int sub = byte >> (ld + 4);                     // 16-token sub-tile
-      const int L = (byte & ((16 << ld) - 1)) >> (ld - 2);  // lane slice tg*16 + dm
-      const int n = min(max(row0 - (sub * 16 + (L >> 4) * 4), 0), 4);  // valid tokens of the word
-      return n == 4 ? ~0u : (1u << (8 * n)) - 1u;
-    };
-    auto new_value = [&](int e) {
-      return load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1)));
-    };
-    const bool held = nr * D <= 64 * kPre;
-    int qm = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) {
-      const uint32_t wm = word_mask(k);
-      const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = (ws[w] ^ bias4) & wm;  // signed codes; other rows read as 0
-#pragma unroll
-        for (int b = 0; b < 4; ++b) qm = max(qm, abs((int)(int8_t)(x >> (8 * b))));
-      }
-    }
-    float mx = 0.f;
-    if (held) {
-#pragma unroll
-      for (int k = 0; k < kPre; ++k) mx = fmaxf(mx, fabsf(pre[k]));
-    } else {
-      for (int e = lane; e < nr * D; e += 64) mx = fmaxf(mx, fabsf(new_value(e)));
-    }
-    mx = wave_max(mx);
-
-    float sc;
-    int qold = 0;  // largest |code| of the old rows once this append is done
-    if (row0 == 0) {
-      sc = scale_of(mx);
-    } else {
-      qm = wave_max_int(qm);
-      const float m_old = (float)qm * s_old;
-      if (mx <= m_old) {
-        sc = s_old;
-        qold = qm;
-      } else {
-        // the max grew: re-encode the old codes from their dequantised values,
-        // in the registers they were read into, and store whole chunks back
-        // (bytes of rows >= row0 are written back unchanged)
-        sc = scale_of(mx);
-#pragma unroll
-        for (int k = 0; k < kMaxChunks; ++k) {
-          const int c = lane + 64 * k;
-          if (c * 16 < old_bytes) {
-            const uint32_t wm = word_mask(k);
-            uint32_t ws[4] = {oc[k].x ^ bias4, oc[k].y ^ bias4, oc[k].z ^ bias4, oc[k].w ^ bias4};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-#pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                if (wm & (0xFFu << (8 * b))) {
-                  const int code = (int)(int8_t)(ws[w] >> (8 * b));
-                  const int8_t qn = encode((float)code * s_old, sc);
-                  qold = max(qold, abs((int)qn));
-                  ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | ((uint32_t)(uint8_t)qn << (8 * b));
-                }
-              }
-            }
-            *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
-          }
-        }
-        qold = wave_max_int(qold);
-      }
-    }
-    int qnew = 0;  // largest |code| of the new rows
-    if (held) {
-#pragma unroll
-      for (int k = 0; k < kPre; ++k) {
-        const int e = lane + 64 * k;
-        if (e < nr * D) {
-          const int8_t q = encode(pre[k], sc);
-          qnew = max(qnew, abs((int)q));
-          tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(q ^ (int8_t)bias4);
-        }
-      }
-    } else {
-      for (int e = lane; e < nr * D; e += 64) {
-        const int8_t q = encode(new_value(e), sc);
-        qnew = max(qnew, abs((int)q));
-        tile[off(row0 + (e >> ld), e & (D - 1))] = (int8_t)(q ^ (int8_t)bias4);
-      }
-    }
-    qnew = wave_max_int(qnew);
-    if (lane == 0) {
-      *sp = sc;
-      *qp = max(qold, qnew);
-    }
-    return sc;  // the same in every lane
-  }
-};
-
-template <int IN>
-__global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, const void* k,
-                                                        const void* v, const int64_t* slots,
-                                                        int32_t n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hkv = lv.num_kv_heads;
-  if (wid >= (int64_t)n * hkv * 2) return;
-  const int h = (int)(wid % hkv);
-  const int kv = (int)((wid / hkv) & 1);
-  const int64_t i = wid / hkv / 2;
-  const int bs = lv.block_size;
-  const int lbs = __builtin_ctz(bs);  // block sizes are powers of two
-
-  // The slots of tokens i .. i+63, one per lane, and of token i-1: the run
-  // starting at i is the leading lanes whose slot lies in the same block.
-  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
-  const int64_t blk = slot0 >> lbs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
-  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
-  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
-  const int row0 = (int)(slot0 & (bs - 1));
-  const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
-  I8Append<IN> ap;
-  ap.issue(lv, kv, h, blk, row0, nr, kv ? v : k, i);
-  (void)ap.finish();
-}
-
-// ---------------------------------------------------------------------------
-// H1 for a seal-on-full INT8 layer (lazy quantization, "轻量级推理引擎实战"
-// §三, third design note): one wavefront per (run, head, K|V), runs found as
-// above. A run that leaves its block partly filled is stored as binary16
-// rows in the block's FP16 staging tile. The run that writes the block's last
-// row quantizes the whole block -- its staged rows and the run's own, all as
-// binary16 values -- with the section's quantize_block: one scale max|x|/127
-// (1.0 for an all-zero head), codes round(x / scale) to even, clamped to
-// [-127, 127]; it stores the codes, the scale and the largest |code|.
-// ---------------------------------------------------------------------------
-template <int IN>
-__global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, const void* k,
-                                                          const void* v, const int64_t* slots,
-                                                          int32_t n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hkv = lv.num_kv_heads;
-  if (wid >= (int64_t)n * hkv * 2) return;
-  const int h = (int)(wid % hkv);
-  const int kv = (int)((wid / hkv) & 1);
-  const int64_t i = wid / hkv / 2;
-  const int bs = lv.block_size;
-  const int lbs = __builtin_ctz(bs);
-  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
-  const int64_t blk = slot0 >> lbs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
-  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
-  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
-  const int row0 = (int)(slot0 & (bs - 1));
-  const int nr = min(run, bs - row0);
-
-  const int D = lv.head_dim, ld = __builtin_ctz(D);
-  const void* src = kv ? v : k;
-  uint16_t* t16 = (uint16_t*)(kv ? lv.tail_v : lv.tail_k) + ((size_t)blk * hkv + h) * bs * D;
-  auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
-  // element e of the run (row e >> ld, dim e % D) as binary16 bits
-  auto run_bits = [&](int e) {
-    return __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))));
-  };
-  if (row0 + nr < bs) {  // the block stays partly filled: stage the rows
-    for (int e = lane; e < nr * D; e += 64) t16[off(row0 + (e >> ld), e & (D - 1))] = run_bits(e);
-    return;
-  }
-  // the block is complete: its bs rows as binary16 values, staged or new
-  auto value = [&](int e) {  // element e of the block (row e >> ld)
-    const int t = e >> ld, dd = e & (D - 1);
-    return f16_to_f32(t < row0 ? t16[off(t, dd)] : run_bits(((t - row0) << ld) | dd));
-  };
-  float mx = 0.f;
-  for (int e = lane; e < bs * D; e += 64) mx = fmaxf(mx, fabsf(value(e)));
-  mx = wave_max(mx);
-  const float sc = scale_of(mx);
-  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
-  const int8_t bias = kv ? (int8_t)0x80 : 0;  // V codes are stored biased by 128
-  int qm = 0;
-  for (int e = lane; e < bs * D; e += 64) {
-    const int8_t q = encode(value(e), sc);
-    qm = max(qm, abs((int)q));
-    tile[off(e >> ld, e & (D - 1))] = (int8_t)(q ^ bias);
-  }
-  qm = wave_max_int(qm);
-  if (lane == 0) {
-    (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
-    (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // H2: split-context decode on the matrix cores.
@@ -1562,409 +1073,6 @@ hipError_t launch_decode_g(const DecodeLaunch& d, int group, hipStream_t stream)
   }
 }
 
-// ---------------------------------------------------------------------------
-// Chunked prefill ("轻量级推理引擎实战" §一: prefill handles a prompt's tokens in
-// parallel): each sequence's last q_len cached tokens are queries; query i
-// sits at position p = len - q_len + i and attends to positions 0..p.
-//
-// A tile is 16 matrix-core columns = 16/G query tokens x the G query heads of
-// one KV head. A workgroup takes NW (4 or 8) consecutive tiles of one
-// sequence and KV head, one per wavefront, and streams that head's context
-// through them in steps of two 16-token units (A, B). Its wavefronts read the
-// same units, so the workgroup loads each once: every thread requests 16-byte pieces of a
-// step into registers three steps ahead and writes them into a three-slot LDS
-// ring as binary16 (INT8 codes convert exactly; the block scales stay factors
-// of the scores and of P). Per step and wavefront:
-//   S^T[token][col] = K[token][:] . Q^T[:][col]   per unit (fp16 products, fp32 sums)
-//   O^T[dim][col]  += V^T[dim][k] . P^T[k][col]   over the step's 32 tokens, P as
-//                                                 fp16 hi + lo parts
-// Lane (column n16, group gq) holds dims [gq*D/4, (gq+1)*D/4) of its column's
-// query and of K row n16; QK product c contracts elements [8c, 8c+8) of every
-// lane's range, on both sides. The scores leave QK with lane (n16, gq) holding
-// tokens 4gq..4gq+3 of each unit, so the PV products take contraction index
-// 8gq + j as token 4gq + j of unit A (j < 4) or 4gq + j - 4 of unit B: P^T
-// needs no data movement, and the LDS ring keeps each lane's four V rows of A
-// and of B side by side per dim tile. The query is scaled per column by a
-// power of two into fp16 (a lo part too for an fp32 query). Scores are in
-// base 2; each column keeps a running max that may trail the true maximum by
-// up to kSlack and is raised (the accumulators rescaled) only when a score
-// exceeds it by more.
-//
-// The loop is software-pipelined: a wavefront issues the QK products of step
-// st + 1 before the softmax of step st, so its vector ALU work overlaps the
-// matrix-core queue; the ring holds step st (V), st + 1 (K) and st + 2 (being
-// written).
-//
-// Workgroups are numbered so that the tiles of one (sequence, KV head) pair
-// run on one XCD, whose L2 then serves the pair's context to all of them
-// (consecutive workgroup ids go to the eight XCDs in turn), and so that on each
-// XCD the tiles with the longest context start first.
-// ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void prefill_kernel(const PrefillLaunch a) {
-  constexpr int NT = 64 * NW;               // threads
-  constexpr int TQ = 16 / G;                // query tokens per tile
-  constexpr int ESZ = I8 ? 1 : 2;           // bytes per cached element
-  constexpr int NK = D / 32;                // 16-byte binary16 pieces of a K row per lane
-  constexpr int NDT = D / 16;               // 16-dim tiles of the PV product
-  constexpr int QE = D / 4;                 // query, K and V elements per lane
-  constexpr int GB = kUnit * D * ESZ;       // cache bytes of a unit's K (or V)
-  constexpr int NCH = 2 * GB / 16;          // 16-byte cache pieces per unit, K and V together
-  constexpr int SP = 2 * NCH;               // pieces per step
-  constexpr int CPS = (SP + NT - 1) / NT;   // pieces per thread per step
-  constexpr int PE = 16 / ESZ;              // elements per piece
-  constexpr int RP = 2 * D + 16;            // LDS pitch of a binary16 K row (padded against bank conflicts)
-  constexpr int VP = 16 * NDT + 16;         // LDS pitch of a lane's V operands
-  constexpr int KS = kUnit * RP;            // LDS bytes of a unit's K rows
-  constexpr int SS = 2 * KS + 64 * VP;      // LDS bytes of a step: K rows of A, of B, then V
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n16 = lane & 15, gq = lane >> 4;
-  const int hq = a.num_q_heads, hkv = a.lv.num_kv_heads, bs = a.lv.block_size;
-
-  // workgroup -> (pair, tile group); XCD x runs ids x, x + 8, ... and takes
-  // the x-th contiguous stretch of pair-major, longest-first order
-  const int ngroups = ((a.max_query_len + TQ - 1) / TQ + NW - 1) / NW;
-  const int nwg = gridDim.x, xcd = blockIdx.x & 7, base = nwg >> 3, rem = nwg & 7;
-  const int jo = xcd * base + min(xcd, rem) + (blockIdx.x >> 3);
-  const int pair = jo / ngroups, grp = ngroups - 1 - jo % ngroups;
-  const int g = pair % hkv, s = pair / hkv;
-
-  const int lupb = __builtin_ctz(bs / kUnit);
-  const int qs = a.query_start[s];
-  const int ql = min(a.query_start[s + 1] - qs, a.max_query_len);
-  const int len = min(a.lens[s], a.max_blocks * bs);
-  const int jw = grp * NW * TQ;        // first query of the workgroup's tiles
-  if (jw >= ql || ql > len) return;    // the whole workgroup (no barrier passed yet)
-  const int j0 = jw + wave * TQ;       // this wavefront's tile (may lie past the chunk)
-
-  // lane column n16: query j0 + n16 / G, head n16 % G. A column past the
-  // chunk computes over the whole context (its query is zero) and is not
-  // written.
-  const int qi = j0 + n16 / G, h = n16 % G;
-  const bool colv = qi < ql;
-  const int pos = colv ? len - ql + qi : len - 1;  // last position the column sees
-  const int pmin = len - ql + j0;                  // the tile's first query position
-  const int p_wave = j0 < ql ? len - ql + min(j0 + TQ, ql) - 1 : -1;  // last position the tile sees
-  const int nunits = (len - ql + min(jw + NW * TQ, ql) - 1) / kUnit + 1;  // units the workgroup reads
-  const int nsteps = (nunits + 1) / 2;
-  const int vlim = min(len, nunits * kUnit);       // rows from here on are not staged or not cached
-
-  // ---- query operand (B of QK): D/4 elements per lane, fp16 hi (+ lo)
-  f16x8 qh[NK], ql8[QT == kF32 ? NK : 1];
-  float qconst;
-  {
-    float qv[QE];
-    const size_t qrow = ((size_t)(qs + (colv ? qi : 0)) * hq + g * G + h) * D + gq * QE;
-#pragma unroll
-    for (int e = 0; e < QE; ++e) qv[e] = colv ? load_elem<QT>(a.q, qrow + e) : 0.f;
-    float qm = 0.f;
-#pragma unroll
-    for (int e = 0; e < QE; ++e) qm = fmaxf(qm, fabsf(qv[e]));
-    qm = max_over_lane_groups(qm);  // the column's max |q|
-    int qexp;
-    frexpf(qm, &qexp);              // qm < 2^qexp (0 for a zero column)
-#pragma unroll
-    for (int c = 0; c < NK; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = ldexpf(qv[8 * c + e], 15 - qexp);
-        const _Float16 hi = (_Float16)y;
-        qh[c][e] = hi;
-        if constexpr (QT == kF32) ql8[c][e] = (_Float16)(y - (float)hi);
-      }
-    }
-    qconst = ldexpf(a.softmax_scale * kLog2e, qexp - 15);  // > 0
-  }
-
-  // ---- the unit stream. Every request issues the same vector loads (steps
-  // past the end reload the last unit), so that the waits for a step's data
-  // count precisely and leave the later requests in flight: block-table
-  // entries of step x are loaded right after the pieces of step x - 3, and
-  // step x's pieces (and INT8 scales) three steps before it is staged.
-  const int32_t* table = a.tables + (size_t)s * a.max_blocks;
-  const char* kcodes = (const char*)a.lv.k_codes;
-  const char* vcodes = (const char*)a.lv.v_codes;
-  const uint64_t tile_bytes = (uint64_t)bs * D * ESZ;
-  auto table_entry = [&](int x) {  // lane j = 0, 1: the block of unit 2x + j
-    const int u = min(2 * x + (lane & 1), nunits - 1);
-    return table[u >> lupb];
-  };
-  auto piece = [&](int c, int& V, int& o) {  // unit and byte of this thread's piece c of a step
-    if constexpr (NCH % NT == 0) {  // a thread's pieces of one unit: the unit index is static
-      V = NT * c / NCH;
-      o = 16 * ((NT * c) % NCH + (int)threadIdx.x);
-    } else {
-      const int q = min((int)threadIdx.x + NT * c, SP - 1);
-      V = q / NCH;
-      o = 16 * (q % NCH);
-    }
-  };
-  int tq[3];                 // table entries of the next requests, by step % 3
-  i32x4 ring[3][CPS];        // requested steps' pieces, by step % 3
-  float rsc[3];              // and their scales: lane 0/1 K scale of unit A/B, lane 2/3 V scale
-  auto request = [&](int st, auto r) {  // wave-uniform st; r = st % 3
-    const int ba = min(max(__builtin_amdgcn_readlane(tq[r], 0), 0), a.lv.num_blocks - 1);
-    const int bb = min(max(__builtin_amdgcn_readlane(tq[r], 1), 0), a.lv.num_blocks - 1);
-#pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      int V, o;  // piece NT * c + threadIdx.x of the step: unit V, byte o of its K (o < GB) or V
-      piece(c, V, o);
-      const int u = min(2 * st + V, nunits - 1);
-      const uint64_t sub =
-          ((uint64_t)(V == 0 ? ba : bb) * hkv + g) * tile_bytes + (uint64_t)(u & ((1 << lupb) - 1)) * GB;
-      ring[r][c] = *(const i32x4*)(o < GB ? kcodes + sub + o : vcodes + sub + (o - GB));
-    }
-    if constexpr (I8) {
-      const float* sp = (lane & 2) ? a.lv.v_scales : a.lv.k_scales;
-      rsc[r] = sp[(size_t)((lane & 1) ? bb : ba) * hkv + g];
-    }
-    tq[r] = table_entry(st + 3);
-  };
-  __shared__ __align__(16) unsigned char lds[3][SS];
-  float sks[3][2], svs[3][2];  // scales of the steps in the LDS slots
-  auto stage = [&](int st, auto slot) {  // the requested step st -> LDS slot st % 3, as binary16
-    static_for<2>([&](auto V) {
-      sks[slot][V] = 1.f;
-      svs[slot][V] = 1.f;
-      if constexpr (I8) {
-        if (2 * st + V < nunits) {
-          sks[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), V));
-          svs[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), 2 + V));
-        }
-      }
-    });
-#pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      if (SP % NT != 0 && (int)threadIdx.x + NT * c >= SP) continue;
-      int V, o;
-      piece(c, V, o);
-      if (2 * st + V >= nunits) continue;  // the last step of an odd count has no unit B
-      {
-        const bool isk = o < GB;
-        const int e = (isk ? o : o - GB) / ESZ;  // first element of the piece within K (V)
-        const i32x4 w = ring[slot][c];
-        f16x4 x[PE / 4];
-        if constexpr (I8) {  // 16 codes -> 16 binary16 values (K signed, V stored biased)
-          const uint32_t flip = isk ? 0x80808080u : 0u;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) x[k] = biased_i8x4_to_f16x4((uint32_t)w[k] ^ flip);
-        } else {
-          x[0] = __builtin_bit_cast(f16x4, make_uint2(w[0], w[1]));
-          x[1] = __builtin_bit_cast(f16x4, make_uint2(w[2], w[3]));
-        }
-        unsigned char* sl = lds[slot];
-        if (isk) {  // K row e / D, elements e % D ..
-          unsigned char* dst = sl + V * KS + (e / D) * RP + 2 * (e % D);
-#pragma unroll
-          for (int k = 0; k < PE / 8; ++k)
-            *(f16x8*)(dst + 16 * k) = f16x8{x[2 * k][0], x[2 * k][1], x[2 * k][2], x[2 * k][3],
-                                            x[2 * k + 1][0], x[2 * k + 1][1], x[2 * k + 1][2], x[2 * k + 1][3]};
-        } else {  // lane e / QE's V elements: four per dim tile, unit A's then unit B's
-          unsigned char* dst = sl + 2 * KS + (e / QE) * VP + 4 * (e % QE) + 8 * V;
-#pragma unroll
-          for (int k = 0; k < PE / 4; ++k) *(f16x4*)(dst + 16 * k) = x[k];
-        }
-      }
-    }
-  };
-
-  float m = -INFINITY, l = 0.f;
-  // P enters the PV product as p * vscale * 2^(14 - kSlack - ev), ev the
-  // largest binary exponent of any V scale so far (uniform): the fp16 hi and
-  // lo parts stay below 2^14 and clear of fp16 subnormals however small the
-  // scales. The accumulators are rescaled exactly when ev grows and scaled
-  // back by 2^(ev + kSlack - 14) at the end. A binary16 cache has no scale:
-  // ev stays 0.
-  int ev = I8 ? -1000 : 0;
-  f32x4 o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // S^T of step st (LDS slot), both units
-  auto qk = [&](int st, auto slot, f32x4& sa, f32x4& sb) {
-    const unsigned char* sl = lds[slot];
-    f16x8 ka[NK], kb[NK];
-#pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      ka[c] = *(const f16x8*)&sl[n16 * RP + gq * (2 * QE) + 16 * c];
-      kb[c] = *(const f16x8*)&sl[KS + n16 * RP + gq * (2 * QE) + 16 * c];
-    }
-    sa = f32x4{0.f, 0.f, 0.f, 0.f};
-    sb = sa;
-#pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qh[c], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], qh[c], sb, 0, 0, 0);
-      if constexpr (QT == kF32) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], ql8[c], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], ql8[c], sb, 0, 0, 0);
-      }
-    }
-  };
-
-  // softmax of step st from its scores, then O += V^T P^T
-  auto softmax_pv = [&](int st, auto slot, f32x4 sa, f32x4 sb) {
-    const int t0 = st * 2 * kUnit;  // the step's first token
-    const unsigned char* vl = &lds[slot][2 * KS + lane * VP];
-    f16x8 av[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) av[dt] = *(const f16x8*)&vl[16 * dt];
-    const float fa = sks[slot][0] * qconst, fb = sks[slot][1] * qconst;
-    if (t0 + 2 * kUnit - 1 > pmin) {  // some column does not see the whole step (wave-uniform)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = t0 + 4 * gq + i <= pos ? sa[i] : -INFINITY;
-        sb[i] = t0 + kUnit + 4 * gq + i <= pos ? sb[i] : -INFINITY;
-      }
-    }
-    if (t0 + 2 * kUnit > vlim) {  // rows not staged, or past the context, may hold any bits
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          av[dt][j] = t0 + 4 * gq + j < vlim ? av[dt][j] : (_Float16)0.0f;
-          av[dt][4 + j] = t0 + kUnit + 4 * gq + j < vlim ? av[dt][4 + j] : (_Float16)0.0f;
-        }
-    }
-    // scales are positive: the max of the raw sums times the scale is the max score
-    const float lm = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])) * fa,
-                           fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])) * fb);
-    int evn = ev;
-    if constexpr (I8) {
-      int ea, eb;
-      frexpf(svs[slot][0], &ea);  // vscale < 2^ea
-      frexpf(svs[slot][1], &eb);
-      evn = max(ev, __builtin_amdgcn_readfirstlane(max(ea, eb)));  // one scale per unit
-    }
-    // m = -inf and ev = -1000 before the first step: both raise it
-    if (__ballot(lm > m + kSlack) != 0 || evn > ev) {  // wave-uniform
-      const float mn = fmaxf(m, max_over_lane_groups(lm));
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
-      const float ao = alpha * ldexpf(1.0f, ev - evn);  // times an exact power of two
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
-      m = mn;  // finite from the first step on: every column sees token 0
-      ev = evn;
-    }
-    float pa[4], pb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i] = __builtin_amdgcn_exp2f(fmaf(sa[i], fa, -m));  // < 2^kSlack
-      pb[i] = __builtin_amdgcn_exp2f(fmaf(sb[i], fb, -m));
-    }
-    l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
-    // P^T (times the scaled V scale) as fp16 hi + lo: contraction index 8gq + j
-    const float psa = I8 ? uniform_f(ldexpf(svs[slot][0], 14 - kSlack - ev)) : 1.f;  // p * psa < 2^14
-    const float psb = I8 ? uniform_f(ldexpf(svs[slot][1], 14 - kSlack - ev)) : 1.f;
-    f16x8 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-      f16x2 ha, la, hb, lb;
-      split_f16x2(I8 ? pa[i] * psa : pa[i], I8 ? pa[i + 1] * psa : pa[i + 1], ha, la);
-      split_f16x2(I8 ? pb[i] * psb : pb[i], I8 ? pb[i + 1] * psb : pb[i + 1], hb, lb);
-      ph[i] = ha[0];
-      ph[i + 1] = ha[1];
-      ph[4 + i] = hb[0];
-      ph[4 + i + 1] = hb[1];
-      pl[i] = la[0];
-      pl[i + 1] = la[1];
-      pl[4 + i] = lb[0];
-      pl[4 + i + 1] = lb[1];
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], ph, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], pl, o[dt], 0, 0, 0);
-    }
-  };
-
-  auto active = [&](int st) { return st * 2 * kUnit <= p_wave; };  // wave-uniform
-
-  // prologue: steps 0 and 1 staged, 2..4 requested, the scores of step 0
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  tq[0] = table_entry(0);
-  tq[1] = table_entry(1);
-  tq[2] = table_entry(2);
-  request(0, I0{});
-  request(1, I1{});
-  request(2, I2{});
-  stage(0, I0{});
-  request(3, I0{});
-  if (1 < nsteps) stage(1, I1{});
-  request(4, I1{});
-  __syncthreads();
-  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = sa;
-  if (active(0)) qk(0, I0{}, sa, sb);
-
-  for (int s0 = 0; s0 < nsteps; s0 += 3) {
-    // all three iterations run (a step past the end only requests and waits),
-    // so every path through the loop issues the same loads
-    static_for<3>([&](auto B) {  // step st = s0 + b in LDS slot b
-      constexpr int b = decltype(B)::value;
-      const int st = s0 + b;
-      f32x4 na = {0.f, 0.f, 0.f, 0.f}, nb = na;
-      if (st + 1 < nsteps && active(st + 1)) qk(st + 1, std::integral_constant<int, (b + 1) % 3>{}, na, nb);
-      if (st < nsteps && active(st)) softmax_pv(st, B, sa, sb);
-      if (st + 2 < nsteps) stage(st + 2, std::integral_constant<int, (b + 2) % 3>{});
-      request(st + 5, std::integral_constant<int, (b + 2) % 3>{});
-      __syncthreads();  // step st + 2 staged; every wavefront is done with slot b
-      sa = na;
-      sb = nb;
-    });
-  }
-  l = sum_over_lane_groups(l);
-  if (colv) {
-    float* dst = a.out + ((size_t)(qs + qi) * hq + g * G + h) * D;
-    const float inv = ldexpf(1.0f, I8 ? ev + kSlack - 14 : 0) / l;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[dt][i] * inv;
-  }
-}
-
-template <bool I8, int D, int G, int NW>
-hipError_t launch_prefill_w(const PrefillLaunch& p, hipStream_t stream) {
-  const int ngroups = ((p.max_query_len + 16 / G - 1) / (16 / G) + NW - 1) / NW;
-  const int64_t nwg = (int64_t)ngroups * p.lv.num_kv_heads * p.num_seqs;
-  if (nwg * 64 * NW >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
-  const dim3 grid((unsigned)nwg), block(64 * NW);
-  switch (p.q_dtype) {
-    case kF32: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF32, NW>), grid, block, 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF16, NW>), grid, block, 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kBF16, NW>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-// Eight tiles per workgroup halve the loads and conversions per tile, but
-// leave more wavefronts idle where causal tiles of one workgroup see
-// different lengths; they are taken when four-tile workgroups would give the
-// device at most two per compute unit, i.e. few tiles over a long context.
-template <bool I8, int D, int G>
-hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
-  const int64_t tiles = (p.max_query_len + 16 / G - 1) / (16 / G);
-  const int64_t wg4 = (tiles + 3) / 4 * p.lv.num_kv_heads * p.num_seqs;
-  return wg4 <= 2 * (int64_t)device_compute_units() ? launch_prefill_w<I8, D, G, 8>(p, stream)
-                                          : launch_prefill_w<I8, D, G, 4>(p, stream);
-}
-
-template <bool I8, int D>
-hipError_t launch_prefill_g(const PrefillLaunch& p, int group, hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_prefill_q<I8, D, 1>(p, stream);
-    case 2: return launch_prefill_q<I8, D, 2>(p, stream);
-    case 4: return launch_prefill_q<I8, D, 4>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 }  // namespace
 
 // Decode workspace owned by the library (arrival counters, then partition
@@ -2016,49 +1124,6 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     launch_merge<128>(d, chunk, grid, stream);
   else
     launch_merge<64>(d, chunk, grid, stream);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
-  if (p.num_seqs <= 0 || p.max_query_len <= 0) return hipSuccess;
-  const int group = p.num_q_heads / p.lv.num_kv_heads;
-  const bool i8 = p.lv.kv_dtype == kI8;
-  if (p.lv.head_dim == 128)
-    return i8 ? launch_prefill_g<true, 128>(p, group, stream) : launch_prefill_g<false, 128>(p, group, stream);
-  return i8 ? launch_prefill_g<true, 64>(p, group, stream) : launch_prefill_g<false, 64>(p, group, stream);
-}
-
-hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int in_dtype,
-                         const int64_t* slots, int32_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  if (lv.kv_dtype == kF16) {
-    const int64_t total = (int64_t)n * lv.num_kv_heads * 2 * (lv.head_dim / 8);
-    const dim3 grid((unsigned)((total + 255) / 256));
-    switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_f16_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_f16_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_f16_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else if (lv.seal) {
-    const int64_t waves = (int64_t)n * lv.num_kv_heads * 2;
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    const int64_t waves = (int64_t)n * lv.num_kv_heads * 2;
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_i8_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_i8_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_i8_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // kernels.h -- launch interface between the host library (pool.cpp) and the
-// gfx950 kernels (kernels.hip). Internal to libpkv.
+// gfx950 kernels (append.hip, decode.hip, prefill.hip). Internal to libpkv.
 #pragma once
 
 #include <hip/hip_runtime.h>

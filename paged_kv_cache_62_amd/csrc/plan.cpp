@@ -1,6 +1,6 @@
 // plan.cpp -- host-side sizes and device facts the decode launches are
 // planned with (workspace layout, supported shapes, compute units). Shared
-// by the host library (pool.cpp) and the kernel launchers (kernels.hip);
+// by the host library (pool.cpp) and the kernel launchers (*.hip);
 // host code only.
 
 #include <hip/hip_runtime_api.h>

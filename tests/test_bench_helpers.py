@@ -6,15 +6,22 @@ import numpy as np
 import bench
 
 
-def test_code_hash_ignores_comments_and_whitespace(tmp_path):
-    a = tmp_path / "a.hip"
-    b = tmp_path / "b.hip"
-    c = tmp_path / "c.hip"
-    a.write_text("int f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n")
-    b.write_text("// header\nint f(int x)\n{ return x + 1; }\n")
-    c.write_text("int f(int x) { return x + 2; }\n")
-    assert bench.kernels_code_hash(str(a)) == bench.kernels_code_hash(str(b))
-    assert bench.kernels_code_hash(str(a)) != bench.kernels_code_hash(str(c))
+def test_code_hash_ignores_comments_and_whitespace():
+    a = "int f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n"
+    b = "// header\nint f(int x)\n{ return x + 1; }\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench.code_hash(a) == bench.code_hash(b)
+    assert bench.code_hash(a) != bench.code_hash(c)
+
+
+def test_kernels_code_hash_covers_every_kernel_source():
+    """The hash keys on every device source the library builds."""
+    import importlib
+    import os
+    build = importlib.import_module("paged_kv_cache_62_amd.build")  # the module, not the function
+    built = {os.path.basename(s) for s in build.SOURCES if s.endswith(".hip")}
+    assert built <= set(bench.KERNEL_SOURCES)
+    assert len(bench.kernels_code_hash()) == 64
 
 
 def test_committed_summaries_parse():
