@@ -395,6 +395,13 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // with its hi part cleared in lanes n16 >= 8.
   const uint64_t colmask = __ballot(colv);
   float m = -INFINITY, l = 0.f;
+  // INT8 V enters the PV product as 1152 + code (two byte permutes per four
+  // codes, exact in fp16); lb = sum of p * pscale over the INT8 units, kept
+  // in the accumulators' scale, so that 1152 * lb is taken off once at the
+  // end. The accumulators then carry 1152 times sum(P) besides the signal:
+  // their fp32 rounding adds ~2^-24 * 1152 * sqrt(units) code units (about
+  // 1e-4 after the V scale, far inside the attention tolerance).
+  float lb = 0.f;
   // P enters the PV product as p * vscale * 2^(14 - kSlack - ev) with ev the
   // largest binary exponent of any V scale seen so far (wave-uniform), which
   // keeps the fp16 parts below 2^14 and their lo part clear of fp16
@@ -476,6 +483,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
                        ldexpf(1.0f, ev - evn);  // exact power of two
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
+      if constexpr (I8) lb *= ao;  // (lanes n16 < 8: alpha * 2^(ev - evn))
       m = mn;
       ev = evn;
     }
@@ -486,6 +494,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     const float lsum = (p[0] + p[1]) + (p[2] + p[3]);
     l += lsum;
     const float pscale = ldexpf(I8 ? vscale : 1.0f, 14 - kSlack - ev);  // p * pscale < 2^14
+    if constexpr (I8 && !TAIL) lb = fmaf(lsum, pscale, lb);
     f16x4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {  // the V scale rides on P
@@ -517,7 +526,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     for (int dt = 0; dt < NDT; ++dt) {
       f16x4 av;
       if constexpr (I8 && !TAIL) {
-        av = biased_i8x4_to_f16x4(vw[dt]);
+        av = biased_i8x4_to_f16x4_plus1152(vw[dt]);
       } else {
         av = __builtin_bit_cast(f16x4, make_uint2(vw[2 * dt], vw[2 * dt + 1]));
         if (nvalid < kUnit) {  // rows past the end may hold any bits (NaN included)
@@ -803,10 +812,11 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   // hi + lo columns, back to unit scale; l summed over the four lane groups
   const float oscale = ldexpf(1.0f, ev + kSlack - 14);
   l = sum_over_lane_groups(l);
+  const float bias = I8 ? 1152.f * sum_over_lane_groups(lb) : 0.f;  // the INT8 V offset, whole column
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i])) * oscale;
+    for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i]) - bias) * oscale;
 
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];

@@ -128,27 +128,35 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
 }
 
 // INT8 V codes are stored biased (code + 128, i.e. code ^ 0x80). Four of them
-// -> four fp16 codes, exactly: each byte becomes the low mantissa byte of
-// 1024.0 (0x6400), giving 1152 + code, and 1152 is subtracted. (Leaving the
-// 1152 in and removing 1152 * sum(P) after the product would save the two
-// subtractions, but the fp32 accumulators would then carry ~1152/|code|
-// times the signal and its rounding error.)
-__device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
+// -> four fp16 values with two byte permutes, exactly: each byte becomes the
+// low mantissa byte of 1024.0 (0x6400), giving 1152 + code.
+__device__ __forceinline__ f16x4 biased_i8x4_to_f16x4_plus1152(uint32_t u) {
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  return __builtin_bit_cast(f16x4, make_uint2(lo, hi));
+}
+// The same with the 1152 subtracted (two packed fp16 subtractions, exact):
+// the codes themselves.
+__device__ __forceinline__ f16x4 biased_i8x4_to_f16x4(uint32_t u) {
+  const f16x4 x = biased_i8x4_to_f16x4_plus1152(u);
   const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
-  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  const f16x2 a = f16x2{x[0], x[1]} - bias;
+  const f16x2 b = f16x2{x[2], x[3]} - bias;
   return f16x4{a[0], a[1], b[0], b[1]};
 }
 
-// x0, x1 as binary16 pairs hi + lo: hi is x rounded toward zero (one
-// conversion instruction, which the compiler cannot fuse with anything, so
-// every use sees the same hi) and lo = x - hi rounded to nearest; hi + lo
-// carries about 22 significant bits.
+// x0, x1 in [0, 2^14) as binary16 pairs hi + lo: hi is x rounded toward zero
+// (one conversion instruction, which the compiler cannot fuse with anything,
+// so every use sees the same hi); in the binary16 normal range that is x with
+// the low 13 of its 23 fraction bits cleared, so lo = x - hi is exact in
+// binary32 and is itself rounded toward zero into binary16. hi + lo carries
+// about 21 significant bits (|x - hi - lo| < 2^-20 |x|); below 2^-14, where
+// hi is subnormal, the remainder is dropped (|error| < 2^-24 absolute).
 __device__ __forceinline__ void split_f16x2(float x0, float x1, f16x2& hi, f16x2& lo) {
   hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  lo = f16x2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
+  const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
+  const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1));
 }
 
 // ---------------------------------------------------------------------------
