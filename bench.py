@@ -90,6 +90,9 @@ def parse():
                     help="where partitions are merged: automatic, last workgroup, or a second launch")
     ap.add_argument("--unfused", action="store_true",
                     help="append and decode as two launches per layer instead of one pkv_decode_step")
+    ap.add_argument("--contraction", choices=["mfma", "valu"], default="mfma",
+                    help="decode contractions on the matrix cores, or (with --unfused, for comparison) "
+                         "as fp32 FMAs on the vector ALUs")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -487,12 +490,15 @@ def run(args, stream):
     from paged_kv_cache_62_amd import pkv
     print(f"# building workload {args.config}", file=sys.stderr, flush=True)
     merge_flags = {"auto": 0, "fused": pkv.PKV_DECODE_FUSED_MERGE, "separate": pkv.PKV_DECODE_SEPARATE_MERGE}
+    if args.contraction == "valu" and not args.unfused:
+        sys.exit("--contraction valu times pkv_decode_attention: add --unfused")
+    valu_flag = pkv.PKV_DECODE_VALU_CONTRACTION if args.contraction == "valu" else 0
     # Every host_prep() appends one token per sequence: the one before graph
     # capture, the warm-up steps and the timed steps. The workload sizes its
     # lengths and max_context_len for exactly that many, so the first timed
     # step decodes at the configured context and no step exceeds the capacity.
     pre = args.warmup + (0 if args.no_graph else 1)
-    w = Workload(args.config, pre + args.steps, args.partition, flags=merge_flags[args.merge],
+    w = Workload(args.config, pre + args.steps, args.partition, flags=merge_flags[args.merge] | valu_flag,
                  fused=not args.unfused, warmup=pre)
     graphs = {}
     if not args.no_graph:
@@ -606,13 +612,17 @@ def run(args, stream):
                    "merge": "none (one partition)" if plan[1] == 1 else
                             "last workgroup" if plan[2] else "separate launch",
                    "hip_graph": not args.no_graph,
+                   "contraction": "vector ALU (comparison)" if valu_flag else "matrix cores",
                    "launches_per_layer": 1 if w.fused else 2,
                    "kv_read_GBps_whole_step": kv_gbs_step,
                    "append_kernel_us": append_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.config) if w.fused and not valu_flag else None,
                      "kernel": ("decode_kernel, decode step (new token's append + split-context decode + merge)"
-                                if w.fused else "decode_kernel (split-context decode incl. partition merge)"),
+                                if w.fused else "decode_kernel_valu (vector-ALU contractions; "
+                                "split-context decode incl. partition merge)" if valu_flag else
+                                "decode_kernel (split-context decode incl. partition merge)"),
                      "avg_launch_us": avg_dur_s * 1e6, "bytes_per_launch": bytes_launch,
                      "other_bytes_per_launch": other_bytes,
                      "timing": f"HIP events around {reps} replays of a graph of the {len(layers)} decode launches"},

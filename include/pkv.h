@@ -200,6 +200,12 @@ int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_
 #define PKV_DECODE_SEPARATE_MERGE 1 /* merge partitions in a second launch */
 #define PKV_DECODE_FUSED_MERGE 2    /* merge partitions in the last workgroup of
                                        each (seq, KV head) to finish */
+#define PKV_DECODE_VALU_CONTRACTION 4 /* pkv_decode_attention only, for comparing the two
+                                       forms: the same launch with both contractions (q.k
+                                       and p.v) as fp32 FMAs on the vector ALUs instead of
+                                       the matrix cores. head_dim 128, 1 or 2 query heads
+                                       per KV head, not seal_on_full layers; otherwise
+                                       PKV_ERR_UNSUPPORTED. */
 
 /* The launch plan pkv_decode_attention follows for these sizes and flags:
  * partition tokens, partitions per sequence, and 1 when partitions are

@@ -52,9 +52,10 @@ namespace {
 // the workspace and the last workgroup of the (sequence, KV head) to finish
 // merges all partitions.
 // ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT, bool APPEND, bool SEAL, int NB>
+template <bool I8, int D, int G, int QT, bool APPEND, bool SEAL, int NB, bool VALU = false>
 __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
   static_assert(!SEAL || I8, "seal-on-full: INT8 layers");
+  static_assert(!VALU || (!APPEND && !SEAL && D == 128 && G <= 2), "vector-ALU contraction: plain decode");
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int RB = D * ESZ;       // bytes per K row
   constexpr int NCH = RB / 64;      // 16-byte chunks per lane per unit (K, and V)
@@ -413,12 +414,125 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- VALU: the same decode with both contractions on the vector ALUs in
+  // fp32, for comparison with the matrix-core form (same loads, ring,
+  // bookkeeping and merge). Lane (n16, gq) holds this lane's D/4 dims of K
+  // row n16 (the ring's layout) and the query of every head over those dims;
+  // the scores are summed over the four lane groups, so every lane of row gq
+  // holds token n16's score. For P.V, lane (tg = gq, dm = n16) holds tokens
+  // 4 tg + ti of dims 16 dt + dm (the ring's V layout) and fetches their
+  // probabilities from lanes 16 tg + 4 tg + ti. INT8 codes are read as
+  // unsigned bytes (code + 128) with the 128 taken off through sum(q) and
+  // sum(p * vscale). Per head: the running max (wave-uniform, raised by more
+  // than kSlack only), this lane's share of the sum, its dims' output.
+  constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
+  float qv[VALU ? G : 1][VALU ? D / 4 : 1];
+  float qsum[VALU ? G : 1];
+  float vm[VALU ? G : 1], vl[VALU ? G : 1], vps[VALU ? G : 1];
+  float vo[VALU ? G : 1][VALU ? NDT : 1];
+  if constexpr (VALU) {
+    const float qscale = a.softmax_scale * kLog2e;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float qs = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) {
+          const int e = (16 * gq + 64 * c) / ESZ + j;
+          qv[h][c * EPC + j] = load_elem<QT>(a.q, ((size_t)s * hq + g * G + h) * D + e) * qscale;
+          qs += qv[h][c * EPC + j];
+        }
+      qsum[h] = sum_over_lane_groups(qs);
+      vm[h] = -INFINITY;
+      vl[h] = 0.f;
+      vps[h] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vo[h][dt] = 0.f;
+    }
+  }
+  auto row_sum = [](float x) {  // sum over the 16 lanes of each row, in every lane of the row
+    x += dpp_f<kQuadXor1>(x);
+    x += dpp_f<kQuadXor2>(x);
+    x += dpp_f<kHalfMirror>(x);
+    return x + dpp_f<kMirror>(x);
+  };
+  auto row_max = [](float x) {
+    x = fmaxf(x, dpp_f<kQuadXor1>(x));
+    x = fmaxf(x, dpp_f<kQuadXor2>(x));
+    x = fmaxf(x, dpp_f<kHalfMirror>(x));
+    return fmaxf(x, dpp_f<kMirror>(x));
+  };
+
   // One unit of 16 tokens. TAIL: an FP16 unit in an INT8 kernel (a
   // seal-on-full cache's partly filled last block), scored with the fp16
   // query operand and taken with V scale 1; otherwise the kernel's own type.
   auto process = [&](auto tail, const auto& kr, const auto& vr, float kscale, float vscale, int tok0) {
     constexpr bool TAIL = decltype(tail)::value;
     const int nvalid = t1 - tok0;  // rows of this unit inside the partition
+    if constexpr (VALU) {
+      float sk[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sk[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+          for (int b = 0; b < 4 / ESZ; ++b) {
+            float x;
+            if constexpr (I8) x = (float)(((w[k] ^ 0x80808080u) >> (8 * b)) & 0xFFu);  // code + 128
+            else x = f16_to_f32((w[k] >> (16 * b)) & 0xFFFFu);
+#pragma unroll
+            for (int h = 0; h < G; ++h) sk[h] = fmaf(qv[h][c * EPC + k * (4 / ESZ) + b], x, sk[h]);
+          }
+        }
+      }
+      float pt[G][4];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sc = sum_over_lane_groups(sk[h]);
+        if constexpr (I8) sc = (sc - 128.f * qsum[h]) * kscale;
+        if (n16 >= nvalid) sc = -INFINITY;  // rows past the partition's end
+        const float um = uniform_f(row_max(sc));  // finite: every unit has a valid row
+        if (um > vm[h] + kSlack) {  // wave-uniform
+          const float alpha = __builtin_amdgcn_exp2f(vm[h] - um);
+          vl[h] *= alpha;
+          vps[h] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vo[h][dt] *= alpha;
+          vm[h] = um;
+        }
+        const float p = __builtin_amdgcn_exp2f(sc - vm[h]);
+        vl[h] += p;
+        const float pv = I8 ? p * vscale : p;
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) pt[h][ti] = __shfl(pv, 20 * gq + ti);  // lane 16 gq + 4 gq + ti
+        if constexpr (I8) vps[h] += (pt[h][0] + pt[h][1]) + (pt[h][2] + pt[h][3]);
+      }
+      uint32_t vw[4 * NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        vw[4 * c] = vr[c].x; vw[4 * c + 1] = vr[c].y; vw[4 * c + 2] = vr[c].z; vw[4 * c + 3] = vr[c].w;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          float x;
+          if constexpr (I8) {  // word dt: tokens 4 gq + 0..3 of dim 16 dt + n16 (code + 128)
+            x = (float)((vw[dt] >> (8 * ti)) & 0xFFu);
+          } else {
+            x = f16_to_f32((vw[2 * dt + (ti >> 1)] >> (16 * (ti & 1))) & 0xFFFFu);
+            if (4 * gq + ti >= nvalid) x = 0.f;  // rows past the end may hold any bits
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) vo[h][dt] = fmaf(pt[h][ti], x, vo[h][dt]);
+        }
+      }
+      return;
+    }
 
     // S^T = K Q^T: lane holds tokens 4*gq + i of column n16
     float sc[4];
@@ -809,6 +923,24 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
     }
   }
 
+  __shared__ float sm_o[kWaves][G][D];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ int sm_last;
+  if constexpr (VALU) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float lt = row_sum(vl[h]);  // a row holds each of the wave's tokens once
+      const float bias = I8 ? 128.f * sum_over_lane_groups(vps[h]) : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float od = sum_over_lane_groups(vo[h][dt]) - bias;
+        if (gq == 0) sm_o[wave][h][16 * dt + n16] = od;
+      }
+      if (lane == 0) { sm_m[wave][h] = vm[h]; sm_l[wave][h] = lt; }
+    }
+  }
+
   // hi + lo columns, back to unit scale; l summed over the four lane groups
   const float oscale = ldexpf(1.0f, ev + kSlack - 14);
   l = sum_over_lane_groups(l);
@@ -818,11 +950,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch& a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[dt][i] = (o[dt][i] + dpp_f<kRowShl8>(o[dt][i]) - bias) * oscale;
 
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __shared__ int sm_last;
-  if (colv) {
+  if (colv && !VALU) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -943,6 +1071,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 void decode_kernel_f16(const DecodeLaunch a) {
   decode_body<false, D, G, QT, APPEND, false, 2>(a);
 }
+// Plain decode with both contractions on the vector ALUs (fp32 FMAs) instead
+// of the matrix cores, kept to compare the two forms; same ring depths. The
+// query of both heads over a lane's dims takes 64 more registers, so this
+// variant is allowed two wavefronts per SIMD (up to 256 registers) and does
+// not spill.
+template <bool I8, int D, int G, int QT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_kernel_valu(const DecodeLaunch a) {
+  decode_body<I8, D, G, QT, false, false, I8 ? 3 : 2, true>(a);
+}
 
 // ---------------------------------------------------------------------------
 // H3 as its own launch: merge the partitions of each (sequence, query head):
@@ -1043,6 +1181,12 @@ template <bool I8, int D, int G, int QT>
 void launch_one(const DecodeLaunch& d, hipStream_t stream) {
   const dim3 grid(d.max_partitions, d.lv.num_kv_heads, d.num_seqs);
   const bool step = d.k_new != nullptr;
+  if constexpr (D == 128 && G <= 2) {
+    if (d.valu_contraction) {  // plain decode only (the host checks the rest)
+      hipLaunchKernelGGL((decode_kernel_valu<I8, D, G, QT>), grid, dim3(kThreads), 0, stream, d);
+      return;
+    }
+  }
   if constexpr (I8) {
     if (step && d.lv.seal)
       hipLaunchKernelGGL((decode_kernel_i8<D, G, QT, true, true>), grid, dim3(kThreads), 0, stream, d);

@@ -72,6 +72,8 @@ struct DecodeLaunch {
   int32_t* counters;         // [num_seqs][Hkv] arrival counters (zero between calls)
   float* ws;                 // partials m, l [num_seqs][Hq][P], o [num_seqs][Hq][P][d]
   int32_t fused_merge;       // 1: the last workgroup of a (seq, KV head) merges
+  int32_t valu_contraction;  // 1: both contractions on the vector ALUs (comparison variant:
+                             // plain decode, head_dim 128, 1 or 2 query heads per KV head)
   // Decode step: the new token of each sequence (position len-1), rows of
   // [num_seqs][Hkv][d] in q's dtype, written into the cache before it is
   // read. Null for plain decode.

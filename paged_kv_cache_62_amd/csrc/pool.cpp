@@ -543,7 +543,7 @@ static int32_t plan_fused_merge(const pkv_pool* pool, int32_t num_seqs, int32_t 
 }
 
 static bool valid_flags(int32_t flags) {
-  return !(flags & ~(PKV_DECODE_SEPARATE_MERGE | PKV_DECODE_FUSED_MERGE)) &&
+  return !(flags & ~(PKV_DECODE_SEPARATE_MERGE | PKV_DECODE_FUSED_MERGE | PKV_DECODE_VALU_CONTRACTION)) &&
          !((flags & PKV_DECODE_SEPARATE_MERGE) && (flags & PKV_DECODE_FUSED_MERGE));
 }
 
@@ -621,6 +621,11 @@ static pkv_status decode_launch(pkv_pool* pool, int32_t layer, const void* q, pk
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (P > 65535) return fail(PKV_ERR_UNSUPPORTED, "%d partitions exceed the grid limit", P);
+  const bool valu = (flags & PKV_DECODE_VALU_CONTRACTION) != 0;
+  if (valu && (k_new || c.head_dim != 128 || group > 2 || (pool->tails && pool->tail_index[layer] >= 0)))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "PKV_DECODE_VALU_CONTRACTION: plain decode of a head_dim 128 layer (not seal_on_full) with "
+                "1 or 2 query heads per KV head");
 
   pkv::DecodeLaunch d{};
   d.lv = pool->layer_view(layer);
@@ -638,6 +643,7 @@ static pkv_status decode_launch(pkv_pool* pool, int32_t layer, const void* q, pk
   d.counters = (int32_t*)workspace;
   d.ws = need > 0 ? (float*)((char*)workspace + pkv::decode_counter_bytes(num_seqs, c.num_kv_heads)) : nullptr;
   d.fused_merge = plan_fused_merge(pool, num_seqs, P, flags);
+  d.valu_contraction = valu ? 1 : 0;
   d.k_new = k_new;
   d.v_new = v_new;
   hipError_t e = pkv::launch_decode(d, (hipStream_t)stream);

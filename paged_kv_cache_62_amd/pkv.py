@@ -36,6 +36,7 @@ STATUS_NAMES = {
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
 PKV_DECODE_SEPARATE_MERGE = 1
 PKV_DECODE_FUSED_MERGE = 2
+PKV_DECODE_VALU_CONTRACTION = 4  # comparison variant: both contractions on the vector ALUs
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p

@@ -115,7 +115,7 @@ def test_decode_plan(shape, seqs, max_ctx, flags, plan):
 def test_decode_plan_rejects_bad_arguments():
     from paged_kv_cache_62_amd import pkv
     p = pkv.Pool(1, 2, 64, 16, 64, pkv.PKV_I8, host_only=True)
-    for args in [(4, 600, 0, 3), (4, 600, 0, 4), (4, 600, 24, 0), (4, 600, 8192, 0), (0, 600, 0, 0), (4, 0, 0, 0)]:
+    for args in [(4, 600, 0, 3), (4, 600, 0, 8), (4, 600, 0, 7), (4, 600, 24, 0), (4, 600, 8192, 0), (0, 600, 0, 0), (4, 0, 0, 0)]:
         with pytest.raises(pkv.PkvError):
             p.decode_plan(*args)
 

@@ -413,3 +413,40 @@ def test_decode_step_clamped_length_appends_nothing(gpu, kind):
         np.testing.assert_array_equal(at[x], bt[x])
     for p in pools:
         p.close()
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("shape_i", [0, 1, 4])
+@pytest.mark.parametrize("flags", [pkv.PKV_DECODE_SEPARATE_MERGE, pkv.PKV_DECODE_FUSED_MERGE])
+def test_valu_contraction_variant(gpu, kv, shape_i, flags):
+    """The comparison variant with both contractions on the vector ALUs
+    (PKV_DECODE_VALU_CONTRACTION): same tolerance against the FP64 oracle,
+    head_dim 128 with one or two query heads per KV head, ragged lengths,
+    one and several partitions, both merge placements."""
+    hq, hkv, dim, bs, lens = SHAPES[shape_i]
+    nblocks = sum((n + bs - 1) // bs for n in lens) + 5
+    sh = H.Shape(layers=2, hq=hq, hkv=hkv, dim=dim, bs=bs, nblocks=nblocks, kv_dtype=kv,
+                 in_dtype="bf16", q_dtype="f32" if shape_i == 1 else "bf16", free_order_seed=3,
+                 sigma_kv="per_head", outlier_p=0.01)
+    case = H.Case(sh, 62900 + shape_i, [("allocate", s, n) for s, n in enumerate(lens)],
+                  decode_seqs=list(range(len(lens))))
+    for T in (0, 64):
+        res = H.run_decode_case(case, partition_tokens=T, compare_cache=False,
+                                flags=flags | pkv.PKV_DECODE_VALU_CONTRACTION)
+        _report(f"valu shape {SHAPES[shape_i][:4]} kv={kv} T={T}", res)
+        H.assert_attention_close(res["gpu"], res["ref"])
+
+
+def test_valu_contraction_rejects_what_it_does_not_cover(gpu):
+    """head_dim 64, four query heads per KV head, and the decode step are
+    outside the comparison variant: an error on the host, nothing launched."""
+    import torch
+    for hq, hkv, dim in ((8, 2, 128), (2, 2, 64)):
+        p = pkv.Pool(1, hkv, dim, 16, 8, pkv.PKV_I8)
+        q = torch.zeros(1, hq, dim, dtype=torch.bfloat16, device="cuda")
+        table = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+        lens = torch.ones(1, dtype=torch.int32, device="cuda")
+        with pytest.raises(pkv.PkvError) as e:
+            p.decode(0, q, table, lens, 1, 0.1, flags=pkv.PKV_DECODE_VALU_CONTRACTION)
+        assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+        p.close()
