@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (reference for HBM byte counters)")
+    ap.add_argument("--calibrate-read", type=float, default=0.0, metavar="MIB",
+                    help="only time pkv_stream_read of MIB-sized buffers (rotated past the 256 MB MALL) at "
+                         "several grid sizes: the practical HBM read floor for a launch of that many bytes")
     ap.add_argument("--extra", default="auto",
                     help="comma-separated decode workloads also timed in this run and reported under "
                          "'extra_workloads' (no CPU baseline); 'auto' = llama29,llama128 after the default "
@@ -441,6 +444,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
+    if args.calibrate_read:
+        print(json.dumps(calibrate_read(args.calibrate_read)), flush=True)
+        return
     stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
     with torch.cuda.stream(stream):
         res = (run_serve if args.config in SERVE_CONFIGS else
@@ -468,6 +474,45 @@ def main():
                   file=sys.stderr, flush=True)
             del r
     print(json.dumps(res), flush=True)
+
+
+def calibrate_read(mib):
+    """pkv_stream_read of buffers of `mib` MiB, enough of them (>= 1 GiB in all)
+    that the 256 MB MALL holds none between its reads, one launch per buffer
+    in a HIP graph replayed back to back between two events; per launch time
+    and rate for 256 to 4096 workgroups."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    nbytes = int(round(mib * (1 << 20) / 16)) * 16
+    nbuf = max(2, -(-(1 << 30) // nbytes))
+    bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device="cuda") for i in range(nbuf)]
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    rows = []
+    for wg in (256, 512, 1024, 2048, 4096):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for b in bufs:  # once eagerly (first-touch), then captured
+                pkv.pkv_stream_read(b, wg, sink, stream)
+            with torch.cuda.graph(g, stream=stream):
+                for b in bufs:
+                    pkv.pkv_stream_read(b, wg, sink, stream)
+        reps = max(3, int(2e9 // (nbytes * nbuf)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replays go to the current stream: the events' stream
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * nbuf)
+        rows.append({"workgroups": wg, "avg_launch_us": us, "GBps": nbytes / us / 1e3,
+                     "frac": nbytes / us / 1e3 / HBM_PEAK_GBS})
+    best = min(rows, key=lambda r: r["avg_launch_us"])
+    return {"calibrate_read_bytes": nbytes, "buffers": nbuf, "rows": rows, "best": best,
+            "timing": "HIP events around graph replays of one pkv_stream_read per buffer"}
 
 
 def extra_workloads(args):

@@ -440,6 +440,17 @@ pkv_status pkv_sched_get_stats(const pkv_sched* sched, pkv_sched_stats* out);
 pkv_status pkv_read_tail_blocks(const pkv_pool* pool, int32_t layer, const int32_t* blocks, int32_t n,
                                 uint16_t* f16_out);
 
+/* Measurement helper: a plain streaming read of `bytes` (a positive multiple
+ * of 16) of device memory at `buf` (16-byte aligned) with `workgroups` (1 ..
+ * 65535) workgroups of 256 threads, each thread taking 16-byte pieces
+ * workgroups*256 apart with four loads in flight; every thread stores one
+ * word to sink (device, workgroups * 256 uint32), so the reads cannot be
+ * dropped. It moves the same kind of 4 KB runs as the decode kernels and
+ * nothing else: its time for the bytes a decode launch reads is the
+ * practical floor of that launch on this GPU ("离开 N 卡后的真实世界" §3.1:
+ * decode is bound by memory bandwidth). Asynchronous on `stream`. */
+pkv_status pkv_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+
 /* The KV-bytes formula 2*L*H*d*s*B*bytes ("无 vLLM 环境下的 Paged-KV" §2). */
 uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,
                       uint64_t seqs, uint64_t bytes);

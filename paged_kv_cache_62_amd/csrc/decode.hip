@@ -1229,6 +1229,34 @@ hipError_t launch_decode_g(const DecodeLaunch& d, int group, hipStream_t stream)
 
 }  // namespace
 
+// A plain streaming read (measurement): each thread reads 16-byte pieces i,
+// i + S, i + 2S, ... (S = all threads of the grid), four loads in flight,
+// and folds them into one word it stores, so the loads cannot be dropped.
+// Consecutive threads read consecutive pieces, so every workgroup streams
+// whole 4 KB runs, as the decode kernels' units are.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, size_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = buf[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                     (const uint4*)buf, bytes / 16, sink);
+  return hipGetLastError();
+}
+
 // Decode workspace owned by the library (arrival counters, then partition
 // partials, as in a caller's workspace), for pkv_decode_step_noalloc. In host
 // code `scratch` names a host-side stand-in, not device memory: host code

@@ -117,6 +117,11 @@ size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t max_partitions);
 
+// Measurement: a plain streaming read of `bytes` (a multiple of 16) with
+// `workgroups` 256-thread workgroups; sink holds workgroups * 256 words.
+hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                              hipStream_t stream);
+
 // The library's own decode workspace for callers that cannot allocate: a
 // device array of kScratchBytes on every GPU the library runs on, zero-filled
 // once. scratch_setup() finds its address on the current device (once per

@@ -829,6 +829,17 @@ pkv_status pkv_read_tail_blocks(const pkv_pool* pool, int32_t layer, const int32
   return ok();
 }
 
+pkv_status pkv_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(PKV_ERR_INVALID_ARG, "NULL buffer or sink");
+  if (bytes == 0 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "bytes %zu must be a positive multiple of 16 and buf 16-byte aligned", bytes);
+  if (workgroups < 1 || workgroups > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "workgroups %d outside [1, 65535]", workgroups);
+  const hipError_t e = pkv::launch_stream_read(buf, bytes, workgroups, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream-read launch");
+  return ok();
+}
+
 uint64_t pkv_kv_bytes(uint64_t layers, uint64_t heads, uint64_t head_dim, uint64_t tokens,
                       uint64_t seqs, uint64_t bytes) {
   return 2ull * layers * heads * head_dim * tokens * seqs * bytes;

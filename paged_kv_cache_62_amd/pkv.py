@@ -107,6 +107,7 @@ SIGNATURES = {
     "pkv_decode_step_noalloc": (C.c_int, [_vp, _i32, _vp, _vp, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _i32,
                                           _f32, _i32, _i32, _vp, _vp]),
     "pkv_read_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
+    "pkv_stream_read": (C.c_int, [_vp, _sz, _i32, _vp, _vp]),
     "pkv_sched_create": (C.c_int, [_vp, _vp, _vp]),
     "pkv_sched_destroy": (None, [_vp]),
     "pkv_sched_submit": (C.c_int, [_vp, _i64, _i32, _i32, _i64]),
@@ -331,6 +332,14 @@ def pkv_read_blocks(h, layer: int, blocks, num_kv_heads: int, block_size: int, h
     _check(lib().pkv_read_blocks(h, layer, _np_ptr(blocks), len(blocks), _np_ptr(codes),
                                  _np_ptr(scales)))
     return codes, scales
+
+
+def pkv_stream_read(buf, workgroups: int, sink, stream=None) -> None:
+    """Measurement: stream-read the device tensor `buf` (all its bytes) with
+    `workgroups` workgroups; sink: uint32 device tensor of workgroups * 256."""
+    assert buf.is_contiguous() and sink.numel() >= workgroups * 256 and sink.element_size() == 4
+    _check(lib().pkv_stream_read(_vp(buf.data_ptr()), int(buf.numel() * buf.element_size()), int(workgroups),
+                                 _vp(sink.data_ptr()), _stream_ptr(stream)))
 
 
 def pkv_kv_bytes(L, H, d, s, B, nbytes) -> int:

@@ -76,6 +76,7 @@ hipError_t launch_append(const LayerView&, const void*, const void*, int, const 
 }
 hipError_t launch_decode(const DecodeLaunch&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill(const PrefillLaunch&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_stream_read(const void*, size_t, int32_t, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t scratch_setup() { return hipSuccess; }
 void* scratch_ptr(int) { return nullptr; }
 

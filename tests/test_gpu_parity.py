@@ -450,3 +450,22 @@ def test_valu_contraction_rejects_what_it_does_not_cover(gpu):
             p.decode(0, q, table, lens, 1, 0.1, flags=pkv.PKV_DECODE_VALU_CONTRACTION)
         assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
         p.close()
+
+
+def test_stream_read_probe_reads_every_byte(gpu):
+    """The measurement probe (pkv_stream_read) reads every 16-byte piece once:
+    the XOR of what its threads store equals the XOR of the buffer, for grids
+    that divide the buffer evenly and that do not; bad sizes are rejected."""
+    import torch
+    x = torch.randint(0, 2 ** 31 - 1, (1 << 18,), dtype=torch.int32, device="cuda")  # 1 MiB
+    want = np.bitwise_xor.reduce(x.cpu().numpy().view(np.uint32))
+    sink = torch.zeros(512 * 256, dtype=torch.int32, device="cuda")
+    for wg in (1, 7, 512):
+        sink.zero_()
+        pkv.pkv_stream_read(x, wg, sink)
+        torch.cuda.synchronize()
+        assert np.bitwise_xor.reduce(sink[: wg * 256].cpu().numpy().view(np.uint32)) == want, wg
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_stream_read(x[:5], 1, sink)  # 20 bytes: not a multiple of 16
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_stream_read(x, 0, sink)
