@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (50; serving configs 100)")
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
+    ap.add_argument("--piece-tokens", type=int, default=0,
+                    help="prefill configs: context piece tokens, a multiple of 64 (0 = automatic)")
     ap.add_argument("--merge", choices=["auto", "fused", "separate"], default="auto",
                     help="where partitions are merged: automatic, last workgroup, or a second launch")
     ap.add_argument("--unfused", action="store_true",
@@ -880,7 +882,7 @@ class PrefillWorkload:
     and, per layer, queries for the last `chunk` tokens of each sequence.
     `prefill(layer)` is the launch a benchmark step makes per layer."""
 
-    def __init__(self, name, stream=None):
+    def __init__(self, name, stream=None, piece_tokens=0):
         import torch
         from paged_kv_cache_62_amd import pkv, synth
         c = self.c = PREFILL_CONFIGS[name]
@@ -908,10 +910,15 @@ class PrefillWorkload:
         self.qs = [torch.randn(B * C, hq, dim, generator=gen, device=dev).to(torch.bfloat16) for _ in range(L)]
         self.q = self.qs[0]  # what the CPU baseline reads
         self.out = torch.empty(B * C, hq, dim, dtype=torch.float32, device=dev)
+        # the context split and its workspace, planned once (every layer's
+        # launch reuses it in turn on the one stream)
+        self.piece_tokens, self.pieces, nb = self.pool.prefill_plan(pkv.PKV_BF16, hq, B, C, ctx, piece_tokens)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
 
     def prefill(self, layer):
         self.pool.prefill(layer, self.qs[layer], self.d_qstart, self.C, self.d_table, self.d_lens, self.scale,
-                          out=self.out, stream=self.stream)
+                          self.ctx, out=self.out, workspace=self.ws, piece_tokens=self.piece_tokens,
+                          stream=self.stream)
         return self.out
 
 
@@ -955,7 +962,7 @@ def run_prefill(args, stream):
     `chunk` tokens of every sequence, as a HIP graph replayed K times."""
     import torch
     print(f"# building prefill workload {args.config}", file=sys.stderr, flush=True)
-    w = PrefillWorkload(args.config, stream)
+    w = PrefillWorkload(args.config, stream, args.piece_tokens)
     c = w.c
     L, hq, dim, B, ctx, C = w.L, w.hq, w.dim, w.B, w.ctx, w.C
 
@@ -999,12 +1006,15 @@ def run_prefill(args, stream):
         "dtype": "int8 kv, fp16 matrix-core products / fp32 accumulate",
         "data": "synthetic (seeded K/V and queries), cache filled before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": B, "query_tokens_per_seq": C,
-                   "context": ctx, "layers_per_step": L, "hip_graph": True},
+                   "context": ctx, "layers_per_step": L, "hip_graph": True,
+                   "context_pieces": w.pieces, "piece_tokens": w.piece_tokens if w.pieces > 1 else None},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": measured_traffic(args.config),
-                     "kernel": "prefill_kernel (causal paged attention, fp16 matrix cores)",
+                     "kernel": ("prefill_kernel (causal paged attention, fp16 matrix cores)"
+                                + (" + prefill_merge_kernel" if w.pieces > 1 else "")),
                      "avg_launch_us": avg_dur_s * 1e6, "flops_per_launch": flops,
-                     "timing": f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"},
+                     "timing": (f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"
+                                + (" (each with its merge launch)" if w.pieces > 1 else ""))},
     }
     res["_workload"] = w
     return res

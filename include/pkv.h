@@ -306,7 +306,18 @@ pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q,
  *     sequence after sequence; out: same shape, fp32.
  *   query_start: [num_seqs+1] int32 (device), query_start[0] = 0, non-decreasing,
  *     1 <= q_len <= context_lens[s]; max_query_len >= every q_len (sizes the grid).
- *   block_tables, context_lens: as for pkv_decode_attention (device).
+ *   block_tables, context_lens: as for pkv_decode_attention (device);
+ *     max_context_len >= every context_lens[s] (plans the context split; a
+ *     longer context is still computed in full, only less evenly split).
+ *   piece_tokens: context split (0 = automatic, else a multiple of 64): each
+ *     sequence's context is cut into pieces of this many tokens, each (group
+ *     of query tiles, piece) one workgroup, and a second launch merges the
+ *     pieces' partial softmax sums per query (log-sum-exp, as the decode
+ *     partitions). The automatic split cuts only when the query tiles alone
+ *     would leave compute units idle. pkv_prefill_plan gives the split.
+ *   workspace: device memory of at least the bytes pkv_prefill_plan gives
+ *     (16-byte aligned), holding the partials; may be NULL when that is 0
+ *     (one piece). Calls that overlap in time need separate workspaces.
  * The K/V operands go through fp16 matrix-core products (INT8 codes convert
  * exactly), probabilities as fp16 hi + lo parts, fp32 accumulation.
  * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4}, F16 and
@@ -314,8 +325,17 @@ pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q,
 pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
                                  int32_t num_q_heads, const int32_t* query_start, int32_t max_query_len,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                 const int32_t* context_lens, int32_t num_seqs, float softmax_scale,
-                                 float* out, void* stream);
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                 float softmax_scale, int32_t piece_tokens, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The context split pkv_prefill_attention makes for these sizes: the piece
+ * size in tokens, the number of pieces per sequence and the workspace bytes
+ * it needs (0 for one piece). Output pointers may be NULL. Host only,
+ * synchronous; the same argument checks as pkv_prefill_attention. */
+pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
+                            int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
+                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out);
 
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as

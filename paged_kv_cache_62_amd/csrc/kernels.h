@@ -96,9 +96,36 @@ struct PrefillLaunch {
   int32_t num_seqs;
   float softmax_scale;
   float* out;                 // [total][Hq][d] fp32
+  // Context split: pieces of piece_tokens (a multiple of 64; the last piece
+  // takes the rest), each (query tile group, piece) one workgroup; with
+  // pieces > 1 their partials go to ws and a merge launch combines them.
+  int32_t pieces;
+  int32_t piece_tokens;
+  float* ws;                  // prefill_workspace_bytes(...) bytes when pieces > 1
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+
+// Wavefronts of a prefill workgroup, and the query tokens a workgroup takes
+// for planning: two 16-column tiles per wavefront (one for an fp32 query), a
+// tile being 16 / group query tokens. (A binary16 cache at head_dim 128 runs
+// one tile per wavefront; the plan does not depend on the layer.)
+constexpr int kPrefillWaves = 4;
+constexpr int prefill_query_tokens_per_workgroup(int group, int q_dtype) {
+  return kPrefillWaves * (q_dtype == kF32 ? 1 : 2) * (16 / group);
+}
+
+// The context split of a prefill launch: piece_tokens (0: automatic, else a
+// multiple of 64) -> the piece size used and the number of pieces. The
+// automatic split cuts the context only when the query tiles alone give
+// fewer than two workgroups per compute unit (cus of them), and keeps pieces
+// of at least 1024 tokens.
+void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
+                  int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
+                  int32_t* pieces_out);
+// Workspace bytes of a launch with this many pieces (0 for one piece).
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads, int32_t head_dim,
+                               int32_t pieces);
 
 // Longest decode partition (tokens) the kernels take.
 constexpr int32_t kMaxPartitionTokens = 4096;

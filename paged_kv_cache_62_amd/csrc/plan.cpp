@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "kernels.h"
@@ -40,6 +41,32 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
   if (max_partitions <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
   return decode_counter_bytes(num_seqs, num_kv_heads) + rows * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
+                  int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
+                  int32_t* pieces_out) {
+  constexpr int32_t kMinPiece = 1024;
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  int32_t t = piece_tokens;
+  if (t <= 0) {
+    const int32_t wq = prefill_query_tokens_per_workgroup(group, q_dtype);
+    const int64_t items = (int64_t)((max_query_len + wq - 1) / wq) * num_kv_heads * num_seqs;
+    const int64_t want = 2 * (int64_t)cus;
+    int64_t n = items >= want || items <= 0 ? 1 : (want + items - 1) / items;
+    n = std::min<int64_t>(n, std::max(1, ctx / kMinPiece));
+    t = (int32_t)((((int64_t)ctx + n - 1) / n + 63) / 64 * 64);
+  }
+  const int32_t n = (int32_t)(((int64_t)ctx + t - 1) / t);
+  *piece_out = n > 1 ? t : std::max(t, ((ctx + 63) / 64) * 64);
+  *pieces_out = n;
+}
+
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads, int32_t head_dim,
+                               int32_t pieces) {
+  if (pieces <= 1) return 0;
+  const size_t slots = (size_t)num_seqs * max_query_len * num_q_heads * pieces;
+  return slots * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 }  // namespace pkv

@@ -706,16 +706,12 @@ pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q,
                        ws, pkv::kScratchBytes, stream);
 }
 
-pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
-                                 int32_t num_q_heads, const int32_t* query_start, int32_t max_query_len,
-                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                 const int32_t* context_lens, int32_t num_seqs, float softmax_scale,
-                                 float* out, void* stream) {
+// Checks shared by the prefill plan and the launch: group size, head_dim,
+// query dtype, sizes and piece size.
+static pkv_status prefill_check(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
+                                int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
-  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
   const pkv_pool_config& c = pool->cfg;
-  if (layer < 0 || layer >= c.num_layers)
-    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
   if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_INVALID_ARG, "q_dtype must be F32, F16 or BF16");
   if (num_q_heads < 1 || num_q_heads % c.num_kv_heads != 0)
@@ -724,13 +720,62 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   if (!pkv::decode_supported(c.head_dim, num_q_heads / c.num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d with %d query heads per KV head", c.head_dim,
                 num_q_heads / c.num_kv_heads);
+  if (num_seqs < 0 || max_query_len < 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d, max_query_len %d, max_context_len %d", num_seqs,
+                max_query_len, max_context_len);
+  if (num_seqs > 0 && (max_query_len < 1 || max_context_len < max_query_len))
+    return fail(PKV_ERR_INVALID_ARG, "max_query_len %d must be in [1, max_context_len %d]", max_query_len,
+                max_context_len);
+  if (piece_tokens < 0 || piece_tokens % 64 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "piece_tokens %d is not a non-negative multiple of 64", piece_tokens);
+  return ok();
+}
+
+pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
+                            int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
+                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out) {
+  const pkv_status st =
+      prefill_check(pool, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d must be >= 1", num_seqs);
+  const pkv_pool_config& c = pool->cfg;
+  int32_t T = 0, n = 0;
+  pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
+                    max_context_len, piece_tokens, &T, &n);
+  if (piece_tokens_out) *piece_tokens_out = T;
+  if (pieces_out) *pieces_out = n;
+  if (workspace_bytes_out)
+    *workspace_bytes_out = pkv::prefill_workspace_bytes(num_seqs, max_query_len, num_q_heads, c.head_dim, n);
+  return ok();
+}
+
+pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
+                                 int32_t num_q_heads, const int32_t* query_start, int32_t max_query_len,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                 float softmax_scale, int32_t piece_tokens, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const pkv_status st =
+      prefill_check(pool, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens);
+  if (st != PKV_OK) return st;
+  if (!pool->arena) return fail(PKV_ERR_UNSUPPORTED, "host-only pool has no device cache");
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.num_layers);
   if (pool->tails && pool->tail_index[layer] >= 0)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_prefill_attention: layer %d quantizes on seal", layer);
-  if (num_seqs < 0 || max_query_len < 0 || max_blocks_per_seq < 1)
-    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d, max_query_len %d, max_blocks_per_seq %d", num_seqs,
-                max_query_len, max_blocks_per_seq);
-  if (num_seqs > 0 && (!q || !query_start || !block_tables || !context_lens || !out))
+  if (max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq %d must be >= 1", max_blocks_per_seq);
+  if (num_seqs == 0) return ok();
+  if (!q || !query_start || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID_ARG, "NULL q, query_start, block_tables, context_lens or out");
+  int32_t T = 0, n = 0;
+  pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
+                    max_context_len, piece_tokens, &T, &n);
+  const size_t need = pkv::prefill_workspace_bytes(num_seqs, max_query_len, num_q_heads, c.head_dim, n);
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes at %p, %zu bytes (16-byte aligned) needed",
+                workspace_bytes, workspace, need);
   pkv::PrefillLaunch p{};
   p.lv = pool->layer_view(layer);
   p.q = q;
@@ -744,6 +789,9 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   p.num_seqs = num_seqs;
   p.softmax_scale = softmax_scale;
   p.out = out;
+  p.pieces = n;
+  p.piece_tokens = T;
+  p.ws = n > 1 ? (float*)workspace : nullptr;
   hipError_t e = pkv::launch_prefill(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

@@ -14,13 +14,17 @@ namespace {
 // sits at position p = len - q_len + i and attends to positions 0..p.
 //
 // A tile is 16 matrix-core columns = 16/G query tokens x the G query heads of
-// one KV head. A workgroup takes NW (4 or 8) consecutive tiles of one
-// sequence and KV head, one per wavefront, and streams that head's context
+// one KV head. A workgroup of four wavefronts takes 4 * NTW consecutive tiles
+// of one sequence and KV head, NTW per wavefront, and streams a range of that
+// head's context (the whole of what its queries see, or one piece of it)
 // through them in steps of two 16-token units (A, B). Its wavefronts read the
-// same units, so the workgroup loads each once: every thread requests 16-byte pieces of a
-// step into registers three steps ahead and writes them into a three-slot LDS
-// ring as binary16 (INT8 codes convert exactly; the block scales stay factors
-// of the scores and of P). Per step and wavefront:
+// same units, so the workgroup loads each once: every thread requests 16-byte
+// pieces of a step into registers three steps ahead and writes them into a
+// three-slot LDS ring as binary16 (INT8 codes convert exactly; the block
+// scales stay factors of the scores and of P). Each wavefront's share of a
+// step lies in one unit's K or V, so its requests are one buffer descriptor
+// (scalar) and a fixed per-lane offset. Per step and wavefront, for each of
+// its tiles (the K and V operands read from LDS once for all of them):
 //   S^T[token][col] = K[token][:] . Q^T[:][col]   per unit (fp16 products, fp32 sums)
 //   O^T[dim][col]  += V^T[dim][k] . P^T[k][col]   over the step's 32 tokens, P as
 //                                                 fp16 hi + lo parts
@@ -34,31 +38,45 @@ namespace {
 // power of two into fp16 (a lo part too for an fp32 query). Scores are in
 // base 2; each column keeps a running max that may trail the true maximum by
 // up to kSlack and is raised (the accumulators rescaled) only when a score
-// exceeds it by more.
+// exceeds it by more. The running max starts at a finite floor, so a column
+// that sees no token of the workgroup's range keeps zero weights.
 //
 // The loop is software-pipelined: a wavefront issues the QK products of step
 // st + 1 before the softmax of step st, so its vector ALU work overlaps the
 // matrix-core queue; the ring holds step st (V), st + 1 (K) and st + 2 (being
 // written).
 //
-// Workgroups are numbered so that the tiles of one (sequence, KV head) pair
-// run on one XCD, whose L2 then serves the pair's context to all of them
-// (consecutive workgroup ids go to the eight XCDs in turn), and so that on each
-// XCD the tiles with the longest context start first.
+// Context pieces: with few query tiles over a long context, the context is
+// cut into pieces of piece_tokens (a multiple of 64) and each (tile group,
+// piece) is a workgroup. Each writes, per (query, head), its partial (m, l,
+// o/l) -- m the base-2 running max, l the sum of weights relative to it --
+// and prefill_merge_kernel combines the pieces a query sees. With one piece
+// the workgroup writes the output itself.
+//
+// Workgroups are numbered so that those of one (sequence, KV head, piece)
+// run on one XCD, whose L2 then serves that context range to all of them
+// (consecutive workgroup ids go to the eight XCDs in turn), and so that on
+// each XCD the tiles with the longest context start first.
 // ---------------------------------------------------------------------------
-template <bool I8, int D, int G, int QT, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
+constexpr float kMaxFloor = -1e30f;  // running max before any visible token (finite: no inf - inf)
+
+template <bool I8, int D, int G, int QT, int NTW>
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(const PrefillLaunch a) {
+  constexpr int NW = kPrefillWaves;
   constexpr int NT = 64 * NW;               // threads
   constexpr int TQ = 16 / G;                // query tokens per tile
+  constexpr int WQ = NW * NTW * TQ;         // query tokens per workgroup
   constexpr int ESZ = I8 ? 1 : 2;           // bytes per cached element
   constexpr int NK = D / 32;                // 16-byte binary16 pieces of a K row per lane
   constexpr int NDT = D / 16;               // 16-dim tiles of the PV product
   constexpr int QE = D / 4;                 // query, K and V elements per lane
   constexpr int GB = kUnit * D * ESZ;       // cache bytes of a unit's K (or V)
-  constexpr int NCH = 2 * GB / 16;          // 16-byte cache pieces per unit, K and V together
+  constexpr int HP = GB / 16;               // 16-byte pieces of a unit's K (or V)
+  constexpr int NCH = 2 * HP;               // pieces per unit, K and V together
   constexpr int SP = 2 * NCH;               // pieces per step
-  constexpr int CPS = (SP + NT - 1) / NT;   // pieces per thread per step
+  static_assert(SP % NT == 0 && HP % 64 == 0, "a wavefront's share of a step lies in one unit's K or V");
+  constexpr int CPS = SP / NT;              // pieces per thread per step
   constexpr int PE = 16 / ESZ;              // elements per piece
   constexpr int RP = 2 * D + 16;            // LDS pitch of a binary16 K row (padded against bank conflicts)
   constexpr int VP = 16 * NDT + 16;         // LDS pitch of a lane's V operands
@@ -69,42 +87,62 @@ void prefill_kernel(const PrefillLaunch a) {
   const int n16 = lane & 15, gq = lane >> 4;
   const int hq = a.num_q_heads, hkv = a.lv.num_kv_heads, bs = a.lv.block_size;
 
-  // workgroup -> (pair, tile group); XCD x runs ids x, x + 8, ... and takes
-  // the x-th contiguous stretch of pair-major, longest-first order
-  const int ngroups = ((a.max_query_len + TQ - 1) / TQ + NW - 1) / NW;
+  // workgroup -> (pair, piece, tile group); XCD x runs ids x, x + 8, ... and
+  // takes the x-th contiguous stretch of (pair, piece)-major, longest-first
+  // order
+  const int ngroups = (a.max_query_len + WQ - 1) / WQ;
+  const int npc = a.pieces;
   const int nwg = gridDim.x, xcd = blockIdx.x & 7, base = nwg >> 3, rem = nwg & 7;
   const int jo = xcd * base + min(xcd, rem) + (blockIdx.x >> 3);
-  const int pair = jo / ngroups, grp = ngroups - 1 - jo % ngroups;
+  const int pair = jo / (ngroups * npc), rr = jo % (ngroups * npc);
+  const int piece = rr / ngroups, grp = ngroups - 1 - rr % ngroups;
   const int g = pair % hkv, s = pair / hkv;
 
   const int lupb = __builtin_ctz(bs / kUnit);
   const int qs = a.query_start[s];
   const int ql = min(a.query_start[s + 1] - qs, a.max_query_len);
   const int len = min(a.lens[s], a.max_blocks * bs);
-  const int jw = grp * NW * TQ;        // first query of the workgroup's tiles
+  const int jw = grp * WQ;             // first query of the workgroup's tiles
   if (jw >= ql || ql > len) return;    // the whole workgroup (no barrier passed yet)
-  const int j0 = jw + wave * TQ;       // this wavefront's tile (may lie past the chunk)
+  const int plast = len - ql + min(jw + WQ, ql) - 1;  // last position the workgroup's queries see
+  const int c0 = piece * a.piece_tokens;              // its context range: tokens [c0, cend)
+  if (c0 > plast) return;              // a piece past what its queries see (no partial is read)
+  // the last piece takes the rest of the context (also past max_context_len)
+  const int cend = piece == npc - 1 ? plast + 1 : min(c0 + a.piece_tokens, plast + 1);
+  const int u0 = c0 / kUnit;                          // c0 is a multiple of 64
+  const int nun = (cend - c0 + kUnit - 1) / kUnit;    // units the workgroup reads
+  const int nsteps = (nun + 1) / 2;
+  const int vlim = min(len, c0 + nun * kUnit);        // rows from here on are not staged or not cached
 
-  // lane column n16: query j0 + n16 / G, head n16 % G. A column past the
-  // chunk computes over the whole context (its query is zero) and is not
-  // written.
-  const int qi = j0 + n16 / G, h = n16 % G;
-  const bool colv = qi < ql;
-  const int pos = colv ? len - ql + qi : len - 1;  // last position the column sees
-  const int pmin = len - ql + j0;                  // the tile's first query position
-  const int p_wave = j0 < ql ? len - ql + min(j0 + TQ, ql) - 1 : -1;  // last position the tile sees
-  const int nunits = (len - ql + min(jw + NW * TQ, ql) - 1) / kUnit + 1;  // units the workgroup reads
-  const int nsteps = (nunits + 1) / 2;
-  const int vlim = min(len, nunits * kUnit);       // rows from here on are not staged or not cached
-
-  // ---- query operand (B of QK): D/4 elements per lane, fp16 hi (+ lo)
-  f16x8 qh[NK], ql8[QT == kF32 ? NK : 1];
-  float qconst;
-  {
-    float qv[QE];
-    const size_t qrow = ((size_t)(qs + (colv ? qi : 0)) * hq + g * G + h) * D + gq * QE;
+  // lane column n16 of tile t: query j0[t] + n16 / G, head n16 % G. A column
+  // past the chunk computes over the whole range (its query is zero) and is
+  // not written. Every wavefront runs every step of the workgroup's range
+  // (masking covers what its columns do not see), so that no branch splits
+  // a step's matrix-core and vector work.
+  const int h = n16 % G;
+  int qi[NTW], pos[NTW], pmin[NTW];
+  bool colv[NTW];
 #pragma unroll
-    for (int e = 0; e < QE; ++e) qv[e] = colv ? load_elem<QT>(a.q, qrow + e) : 0.f;
+  for (int t = 0; t < NTW; ++t) {
+    const int j0 = jw + (wave * NTW + t) * TQ;
+    qi[t] = j0 + n16 / G;
+    colv[t] = qi[t] < ql;
+    pos[t] = colv[t] ? len - ql + qi[t] : len - 1;   // last position the column sees
+    pmin[t] = len - ql + j0;                         // the tile's first query position
+  }
+
+  // ---- query operands (B of QK): D/4 elements per lane and tile, fp16 hi (+ lo)
+  f16x8 qh[NTW][NK], ql8[NTW][QT == kF32 ? NK : 1];
+  float qconst[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    float qv[QE];
+    const size_t qrow = ((size_t)(qs + (colv[t] ? qi[t] : 0)) * hq + g * G + h) * D + gq * QE;
+#pragma unroll
+    for (int e = 0; e < QE; ++e) {
+      const float x = load_elem<QT>(a.q, qrow + e);  // row qs (valid) for a column past the chunk
+      qv[e] = colv[t] ? x : 0.f;
+    }
     float qm = 0.f;
 #pragma unroll
     for (int e = 0; e < QE; ++e) qm = fmaxf(qm, fabsf(qv[e]));
@@ -117,11 +155,11 @@ void prefill_kernel(const PrefillLaunch a) {
       for (int e = 0; e < 8; ++e) {
         const float y = ldexpf(qv[8 * c + e], 15 - qexp);
         const _Float16 hi = (_Float16)y;
-        qh[c][e] = hi;
-        if constexpr (QT == kF32) ql8[c][e] = (_Float16)(y - (float)hi);
+        qh[t][c][e] = hi;
+        if constexpr (QT == kF32) ql8[t][c][e] = (_Float16)(y - (float)hi);
       }
     }
-    qconst = ldexpf(a.softmax_scale * kLog2e, qexp - 15);  // > 0
+    qconst[t] = ldexpf(a.softmax_scale * kLog2e, qexp - 15);  // > 0
   }
 
   // ---- the unit stream. Every request issues the same vector loads (steps
@@ -133,34 +171,49 @@ void prefill_kernel(const PrefillLaunch a) {
   const char* kcodes = (const char*)a.lv.k_codes;
   const char* vcodes = (const char*)a.lv.v_codes;
   const uint64_t tile_bytes = (uint64_t)bs * D * ESZ;
-  auto table_entry = [&](int x) {  // lane j = 0, 1: the block of unit 2x + j
-    const int u = min(2 * x + (lane & 1), nunits - 1);
+  auto table_entry = [&](int x) {  // lane j = 0, 1: the block of unit 2x + j of the range
+    const int u = u0 + min(2 * x + (lane & 1), nun - 1);
     return table[u >> lupb];
   };
-  auto piece = [&](int c, int& V, int& o) {  // unit and byte of this thread's piece c of a step
-    if constexpr (NCH % NT == 0) {  // a thread's pieces of one unit: the unit index is static
-      V = NT * c / NCH;
-      o = 16 * ((NT * c) % NCH + (int)threadIdx.x);
+  // Thread piece c of a step: unit shV[c] (0: A, 1: B) and half shK[c] (K or
+  // V), both wave-uniform, byte shO[c] within that K (or V); the same every
+  // step. With an even count each thread takes as many K pieces as V pieces,
+  // so the wavefronts convert alike.
+  int shV[CPS], shO[CPS];
+  bool shK[CPS];
+#pragma unroll
+  for (int c = 0; c < CPS; ++c) {
+    int v, r;
+    bool k;
+    if constexpr (CPS % 2 == 0) {
+      k = c < CPS / 2;
+      r = (int)threadIdx.x + NT * (c % (CPS / 2));  // over 2 * HP pieces of K (or V)
+      v = r / HP;
     } else {
-      const int q = min((int)threadIdx.x + NT * c, SP - 1);
-      V = q / NCH;
-      o = 16 * (q % NCH);
+      const int q = (int)threadIdx.x + NT * c;
+      v = q / NCH;
+      r = q % NCH;
+      k = r < HP;
     }
-  };
+    shV[c] = __builtin_amdgcn_readfirstlane(v);
+    shK[c] = __builtin_amdgcn_readfirstlane(k ? 1 : 0) != 0;
+    shO[c] = 16 * (r % HP);
+  }
   int tq[3];                 // table entries of the next requests, by step % 3
   i32x4 ring[3][CPS];        // requested steps' pieces, by step % 3
   float rsc[3];              // and their scales: lane 0/1 K scale of unit A/B, lane 2/3 V scale
   auto request = [&](int st, auto r) {  // wave-uniform st; r = st % 3
     const int ba = min(max(__builtin_amdgcn_readlane(tq[r], 0), 0), a.lv.num_blocks - 1);
     const int bb = min(max(__builtin_amdgcn_readlane(tq[r], 1), 0), a.lv.num_blocks - 1);
+    const int umask = (1 << lupb) - 1;
+    const uint64_t sub[2] = {
+        ((uint64_t)ba * hkv + g) * tile_bytes + (uint64_t)((u0 + min(2 * st, nun - 1)) & umask) * GB,
+        ((uint64_t)bb * hkv + g) * tile_bytes + (uint64_t)((u0 + min(2 * st + 1, nun - 1)) & umask) * GB};
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
-      int V, o;  // piece NT * c + threadIdx.x of the step: unit V, byte o of its K (o < GB) or V
-      piece(c, V, o);
-      const int u = min(2 * st + V, nunits - 1);
-      const uint64_t sub =
-          ((uint64_t)(V == 0 ? ba : bb) * hkv + g) * tile_bytes + (uint64_t)(u & ((1 << lupb) - 1)) * GB;
-      ring[r][c] = *(const i32x4*)(o < GB ? kcodes + sub + o : vcodes + sub + (o - GB));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr((shK[c] ? kcodes : vcodes) + sub[shV[c]]), (short)0, GB, kRsrcWord3);
+      ring[r][c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, shO[c], 0, 0));
     }
     if constexpr (I8) {
       const float* sp = (lane & 2) ? a.lv.v_scales : a.lv.k_scales;
@@ -175,7 +228,7 @@ void prefill_kernel(const PrefillLaunch a) {
       sks[slot][V] = 1.f;
       svs[slot][V] = 1.f;
       if constexpr (I8) {
-        if (2 * st + V < nunits) {
+        if (2 * st + V < nun) {
           sks[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), V));
           svs[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), 2 + V));
         }
@@ -183,53 +236,55 @@ void prefill_kernel(const PrefillLaunch a) {
     });
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
-      if (SP % NT != 0 && (int)threadIdx.x + NT * c >= SP) continue;
-      int V, o;
-      piece(c, V, o);
-      if (2 * st + V >= nunits) continue;  // the last step of an odd count has no unit B
-      {
-        const bool isk = o < GB;
-        const int e = (isk ? o : o - GB) / ESZ;  // first element of the piece within K (V)
-        const i32x4 w = ring[slot][c];
-        f16x4 x[PE / 4];
-        if constexpr (I8) {  // 16 codes -> 16 binary16 values (K signed, V stored biased)
-          const uint32_t flip = isk ? 0x80808080u : 0u;
+      const int V = shV[c];
+      const bool isk = shK[c];
+      if (2 * st + V >= nun) continue;  // (uniform) the last step of an odd count has no unit B
+      const int e = shO[c] / ESZ;       // first element of the piece within K (V)
+      const i32x4 w = ring[slot][c];
+      f16x4 x[PE / 4];
+      if constexpr (I8) {  // 16 codes -> 16 binary16 values (K signed, V stored biased)
+        const uint32_t flip = isk ? 0x80808080u : 0u;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) x[k] = biased_i8x4_to_f16x4((uint32_t)w[k] ^ flip);
-        } else {
-          x[0] = __builtin_bit_cast(f16x4, make_uint2(w[0], w[1]));
-          x[1] = __builtin_bit_cast(f16x4, make_uint2(w[2], w[3]));
-        }
-        unsigned char* sl = lds[slot];
-        if (isk) {  // K row e / D, elements e % D ..
-          unsigned char* dst = sl + V * KS + (e / D) * RP + 2 * (e % D);
+        for (int k = 0; k < 4; ++k) x[k] = biased_i8x4_to_f16x4((uint32_t)w[k] ^ flip);
+      } else {
+        x[0] = __builtin_bit_cast(f16x4, make_uint2(w[0], w[1]));
+        x[1] = __builtin_bit_cast(f16x4, make_uint2(w[2], w[3]));
+      }
+      unsigned char* sl = lds[slot];
+      if (isk) {  // K row e / D, elements e % D ..
+        unsigned char* dst = sl + V * KS + (e / D) * RP + 2 * (e % D);
 #pragma unroll
-          for (int k = 0; k < PE / 8; ++k)
-            *(f16x8*)(dst + 16 * k) = f16x8{x[2 * k][0], x[2 * k][1], x[2 * k][2], x[2 * k][3],
-                                            x[2 * k + 1][0], x[2 * k + 1][1], x[2 * k + 1][2], x[2 * k + 1][3]};
-        } else {  // lane e / QE's V elements: four per dim tile, unit A's then unit B's
-          unsigned char* dst = sl + 2 * KS + (e / QE) * VP + 4 * (e % QE) + 8 * V;
+        for (int k = 0; k < PE / 8; ++k)
+          *(f16x8*)(dst + 16 * k) = f16x8{x[2 * k][0], x[2 * k][1], x[2 * k][2], x[2 * k][3],
+                                          x[2 * k + 1][0], x[2 * k + 1][1], x[2 * k + 1][2], x[2 * k + 1][3]};
+      } else {  // lane e / QE's V elements: four per dim tile, unit A's then unit B's
+        unsigned char* dst = sl + 2 * KS + (e / QE) * VP + 4 * (e % QE) + 8 * V;
 #pragma unroll
-          for (int k = 0; k < PE / 4; ++k) *(f16x4*)(dst + 16 * k) = x[k];
-        }
+        for (int k = 0; k < PE / 4; ++k) *(f16x4*)(dst + 16 * k) = x[k];
       }
     }
   };
 
-  float m = -INFINITY, l = 0.f;
-  // P enters the PV product as p * vscale * 2^(14 - kSlack - ev), ev the
-  // largest binary exponent of any V scale so far (uniform): the fp16 hi and
-  // lo parts stay below 2^14 and clear of fp16 subnormals however small the
-  // scales. The accumulators are rescaled exactly when ev grows and scaled
-  // back by 2^(ev + kSlack - 14) at the end. A binary16 cache has no scale:
-  // ev stays 0.
+  float m[NTW], l[NTW];
+  // P enters the PV product as P' = p * vscale * 2^(14 - kSlack - ev), ev
+  // the largest binary exponent of any V scale so far (uniform), computed
+  // as one exponential, 2^(s f - m + log2(vscale) + 14 - kSlack - ev): its
+  // fp16 hi and lo parts stay below 2^14 and clear of fp16 subnormals
+  // however small the scales. The accumulators are rescaled exactly when ev
+  // grows and scaled back by 2^(ev + kSlack - 14) at the end. A binary16
+  // cache has no scale: P' = p.
   int ev = I8 ? -1000 : 0;
-  f32x4 o[NDT];
+  f32x4 o[NTW][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NTW; ++t) {
+    m[t] = kMaxFloor;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // S^T of step st (LDS slot), both units
-  auto qk = [&](int st, auto slot, f32x4& sa, f32x4& sb) {
+  // S^T of the step in an LDS slot, both units, every tile
+  auto qk = [&](auto slot, f32x4 (&sa)[NTW], f32x4 (&sb)[NTW]) {
     const unsigned char* sl = lds[slot];
     f16x8 ka[NK], kb[NK];
 #pragma unroll
@@ -237,34 +292,30 @@ void prefill_kernel(const PrefillLaunch a) {
       ka[c] = *(const f16x8*)&sl[n16 * RP + gq * (2 * QE) + 16 * c];
       kb[c] = *(const f16x8*)&sl[KS + n16 * RP + gq * (2 * QE) + 16 * c];
     }
-    sa = f32x4{0.f, 0.f, 0.f, 0.f};
-    sb = sa;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qh[c], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], qh[c], sb, 0, 0, 0);
-      if constexpr (QT == kF32) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], ql8[c], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], ql8[c], sb, 0, 0, 0);
+    for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+      for (int c = 0; c < NK; ++c) {
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qh[t][c], c == 0 ? zero : sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], qh[t][c], c == 0 ? zero : sb[t], 0, 0, 0);
+        if constexpr (QT == kF32) {
+          sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], ql8[t][c], sa[t], 0, 0, 0);
+          sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[c], ql8[t][c], sb[t], 0, 0, 0);
+        }
       }
     }
   };
 
-  // softmax of step st from its scores, then O += V^T P^T
-  auto softmax_pv = [&](int st, auto slot, f32x4 sa, f32x4 sb) {
-    const int t0 = st * 2 * kUnit;  // the step's first token
+  // Step st (LDS slot): softmax from its scores sa, sb; the next step's
+  // scores (LDS slot nslot, possibly past the range: then unused) into the
+  // same arrays; O += V^T P^T, every tile.
+  auto step = [&](int st, auto slot, auto nslot, f32x4 (&sa)[NTW], f32x4 (&sb)[NTW]) {
+    const int t0 = c0 + st * 2 * kUnit;  // the step's first token
     const unsigned char* vl = &lds[slot][2 * KS + lane * VP];
     f16x8 av[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) av[dt] = *(const f16x8*)&vl[16 * dt];
-    const float fa = sks[slot][0] * qconst, fb = sks[slot][1] * qconst;
-    if (t0 + 2 * kUnit - 1 > pmin) {  // some column does not see the whole step (wave-uniform)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = t0 + 4 * gq + i <= pos ? sa[i] : -INFINITY;
-        sb[i] = t0 + kUnit + 4 * gq + i <= pos ? sb[i] : -INFINITY;
-      }
-    }
     if (t0 + 2 * kUnit > vlim) {  // rows not staged, or past the context, may hold any bits
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -274,9 +325,6 @@ void prefill_kernel(const PrefillLaunch a) {
           av[dt][4 + j] = t0 + kUnit + 4 * gq + j < vlim ? av[dt][4 + j] : (_Float16)0.0f;
         }
     }
-    // scales are positive: the max of the raw sums times the scale is the max score
-    const float lm = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])) * fa,
-                           fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])) * fb);
     int evn = ev;
     if constexpr (I8) {
       int ea, eb;
@@ -284,50 +332,89 @@ void prefill_kernel(const PrefillLaunch a) {
       frexpf(svs[slot][1], &eb);
       evn = max(ev, __builtin_amdgcn_readfirstlane(max(ea, eb)));  // one scale per unit
     }
-    // m = -inf and ev = -1000 before the first step: both raise it
-    if (__ballot(lm > m + kSlack) != 0 || evn > ev) {  // wave-uniform
-      const float mn = fmaxf(m, max_over_lane_groups(lm));
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
-      const float ao = alpha * ldexpf(1.0f, ev - evn);  // times an exact power of two
+    float fa[NTW], fb[NTW], lm[NTW];
+    bool raise = evn > ev;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= ao;
-      m = mn;  // finite from the first step on: every column sees token 0
+    for (int t = 0; t < NTW; ++t) {
+      fa[t] = sks[slot][0] * qconst[t];
+      fb[t] = sks[slot][1] * qconst[t];
+      if (t0 + 2 * kUnit - 1 > pmin[t]) {  // some column does not see the whole step (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa[t][i] = t0 + 4 * gq + i <= pos[t] ? sa[t][i] : -INFINITY;
+          sb[t][i] = t0 + kUnit + 4 * gq + i <= pos[t] ? sb[t][i] : -INFINITY;
+        }
+      }
+      // scales are positive: the max of the raw sums times the scale is the max score
+      lm[t] = fmaxf(fmaxf(fmaxf(sa[t][0], sa[t][1]), fmaxf(sa[t][2], sa[t][3])) * fa[t],
+                    fmaxf(fmaxf(sb[t][0], sb[t][1]), fmaxf(sb[t][2], sb[t][3])) * fb[t]);
+      raise = raise || __ballot(lm[t] > m[t] + kSlack) != 0;  // wave-uniform
+    }
+    // the first step with a visible token raises it (m starts at a finite floor)
+    if (raise) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float mn = fmaxf(m[t], max_over_lane_groups(lm[t]));
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+        l[t] *= alpha;
+        const float ao = alpha * ldexpf(1.0f, ev - evn);  // times an exact power of two
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= ao;
+        m[t] = mn;
+      }
       ev = evn;
     }
-    float pa[4], pb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i] = __builtin_amdgcn_exp2f(fmaf(sa[i], fa, -m));  // < 2^kSlack
-      pb[i] = __builtin_amdgcn_exp2f(fmaf(sb[i], fb, -m));
+    // log2 of each unit's P' / p, and its inverse for l (uniform)
+    float la = 0.f, lb = 0.f, ia = 1.f, ib = 1.f;
+    if constexpr (I8) {
+      la = uniform_f(__builtin_amdgcn_logf(svs[slot][0]) + (float)(14 - kSlack - ev));
+      lb = uniform_f(__builtin_amdgcn_logf(svs[slot][1]) + (float)(14 - kSlack - ev));
+      ia = uniform_f(__builtin_amdgcn_exp2f(-la));
+      ib = uniform_f(__builtin_amdgcn_exp2f(-lb));
     }
-    l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
-    // P^T (times the scaled V scale) as fp16 hi + lo: contraction index 8gq + j
-    const float psa = I8 ? uniform_f(ldexpf(svs[slot][0], 14 - kSlack - ev)) : 1.f;  // p * psa < 2^14
-    const float psb = I8 ? uniform_f(ldexpf(svs[slot][1], 14 - kSlack - ev)) : 1.f;
-    f16x8 ph, pl;
+    f32x4 sc[NTW], sd[NTW];  // this step's scores; sa, sb take the next step's
 #pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-      f16x2 ha, la, hb, lb;
-      split_f16x2(I8 ? pa[i] * psa : pa[i], I8 ? pa[i + 1] * psa : pa[i + 1], ha, la);
-      split_f16x2(I8 ? pb[i] * psb : pb[i], I8 ? pb[i + 1] * psb : pb[i + 1], hb, lb);
-      ph[i] = ha[0];
-      ph[i + 1] = ha[1];
-      ph[4 + i] = hb[0];
-      ph[4 + i + 1] = hb[1];
-      pl[i] = la[0];
-      pl[i + 1] = la[1];
-      pl[4 + i] = lb[0];
-      pl[4 + i + 1] = lb[1];
+    for (int t = 0; t < NTW; ++t) {
+      sc[t] = sa[t];
+      sd[t] = sb[t];
     }
+    qk(nslot, sa, sb);
+    const f16x2 m0 = {(_Float16)-1.0f, (_Float16)0.0f}, m1 = {(_Float16)0.0f, (_Float16)-1.0f};
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], ph, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], pl, o[dt], 0, 0, 0);
+    for (int t = 0; t < NTW; ++t) {
+      const float ca = la - m[t], cb = lb - m[t];
+      float pa[4], pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pa[i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], fa[t], ca));  // < 2^14
+        pb[i] = __builtin_amdgcn_exp2f(fmaf(sd[t][i], fb[t], cb));
+      }
+      const float sA = (pa[0] + pa[1]) + (pa[2] + pa[3]), sB = (pb[0] + pb[1]) + (pb[2] + pb[3]);
+      l[t] += I8 ? fmaf(sA, ia, sB * ib) : sA + sB;
+      // P'^T as fp16 hi + lo, contraction index 8gq + j: hi is P' rounded
+      // toward zero; P' - hi is exact in binary32 (a dot product with -1
+      // takes it in one instruction) and is rounded to nearest into lo
+      f16x8 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const f16x2 ha = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[i], pa[i + 1]));
+        const f16x2 hb = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pb[i], pb[i + 1]));
+        ph[i] = ha[0];
+        ph[i + 1] = ha[1];
+        ph[4 + i] = hb[0];
+        ph[4 + i + 1] = hb[1];
+        pl[i] = (_Float16)__builtin_amdgcn_fdot2(ha, m0, pa[i], false);
+        pl[i + 1] = (_Float16)__builtin_amdgcn_fdot2(ha, m1, pa[i + 1], false);
+        pl[4 + i] = (_Float16)__builtin_amdgcn_fdot2(hb, m0, pb[i], false);
+        pl[4 + i + 1] = (_Float16)__builtin_amdgcn_fdot2(hb, m1, pb[i + 1], false);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], ph, o[t][dt], 0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], pl, o[t][dt], 0, 0, 0);
+      }
     }
   };
-
-  auto active = [&](int st) { return st * 2 * kUnit <= p_wave; };  // wave-uniform
 
   // prologue: steps 0 and 1 staged, 2..4 requested, the scores of step 0
   using I0 = std::integral_constant<int, 0>;
@@ -344,8 +431,8 @@ void prefill_kernel(const PrefillLaunch a) {
   if (1 < nsteps) stage(1, I1{});
   request(4, I1{});
   __syncthreads();
-  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = sa;
-  if (active(0)) qk(0, I0{}, sa, sb);
+  f32x4 sa[NTW], sb[NTW];
+  qk(I0{}, sa, sb);
 
   for (int s0 = 0; s0 < nsteps; s0 += 3) {
     // all three iterations run (a step past the end only requests and waits),
@@ -353,52 +440,104 @@ void prefill_kernel(const PrefillLaunch a) {
     static_for<3>([&](auto B) {  // step st = s0 + b in LDS slot b
       constexpr int b = decltype(B)::value;
       const int st = s0 + b;
-      f32x4 na = {0.f, 0.f, 0.f, 0.f}, nb = na;
-      if (st + 1 < nsteps && active(st + 1)) qk(st + 1, std::integral_constant<int, (b + 1) % 3>{}, na, nb);
-      if (st < nsteps && active(st)) softmax_pv(st, B, sa, sb);
+      if (st < nsteps) step(st, B, std::integral_constant<int, (b + 1) % 3>{}, sa, sb);
       if (st + 2 < nsteps) stage(st + 2, std::integral_constant<int, (b + 2) % 3>{});
       request(st + 5, std::integral_constant<int, (b + 2) % 3>{});
       __syncthreads();  // step st + 2 staged; every wavefront is done with slot b
-      sa = na;
-      sb = nb;
     });
   }
-  l = sum_over_lane_groups(l);
-  if (colv) {
-    float* dst = a.out + ((size_t)(qs + qi) * hq + g * G + h) * D;
-    const float inv = ldexpf(1.0f, I8 ? ev + kSlack - 14 : 0) / l;
+
+  // the output (one piece), or this piece's partial (m, l, o/l)
+  const float oscale = ldexpf(1.0f, I8 ? ev + kSlack - 14 : 0);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int t = 0; t < NTW; ++t) {
+    const float lt = sum_over_lane_groups(l[t]);
+    if (!colv[t]) continue;
+    const size_t row = (size_t)s * a.max_query_len + qi[t];  // (sequence, query) slot of the workspace
+    if (npc == 1) {
+      float* dst = a.out + ((size_t)(qs + qi[t]) * hq + g * G + h) * D;
+      const float inv = oscale / lt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[dt][i] * inv;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
+    } else {
+      const size_t slot = (row * hq + g * G + h) * npc + piece;
+      const size_t nslot = (size_t)a.num_seqs * a.max_query_len * hq * npc;
+      const float inv = lt > 0.f ? oscale / lt : 0.f;
+      float* dst = a.ws + 2 * nslot + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
+      if (gq == 0) {
+        a.ws[slot] = m[t];
+        a.ws[nslot + slot] = lt;
+      }
+    }
   }
 }
 
-template <bool I8, int D, int G, int NW>
-hipError_t launch_prefill_w(const PrefillLaunch& p, hipStream_t stream) {
-  const int ngroups = ((p.max_query_len + 16 / G - 1) / (16 / G) + NW - 1) / NW;
-  const int64_t nwg = (int64_t)ngroups * p.lv.num_kv_heads * p.num_seqs;
-  if (nwg * 64 * NW >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
-  const dim3 grid((unsigned)nwg), block(64 * NW);
-  switch (p.q_dtype) {
-    case kF32: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF32, NW>), grid, block, 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kF16, NW>), grid, block, 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((prefill_kernel<I8, D, G, kBF16, NW>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+// The pieces a query sees, merged: for query i of sequence s at position p,
+// pieces 0 .. p / piece_tokens, each with its partial (m, l, o/l):
+//   M = max m,  w = l * 2^(m - M),  out = sum w * (o/l) / sum w.
+// One workgroup per (sequence, query); 256 / D heads at a time.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillLaunch a) {
+  const int mq = a.max_query_len;
+  const int s = blockIdx.x / mq, qi = blockIdx.x % mq;
+  const int qs = a.query_start[s];
+  const int ql = min(a.query_start[s + 1] - qs, mq);
+  const int len = min(a.lens[s], a.max_blocks * a.lv.block_size);
+  if (qi >= ql || ql > len) return;
+  const int p = len - ql + qi;
+  const int npc = a.pieces, np = min(p / a.piece_tokens + 1, npc);
+  const int hq = a.num_q_heads;
+  const size_t nslot = (size_t)a.num_seqs * mq * hq * npc;
+  const size_t row = (size_t)s * mq + qi;
+  const int dd = threadIdx.x % D;
+  for (int hh = threadIdx.x / D; hh < hq; hh += 256 / D) {
+    const size_t base = (row * hq + hh) * npc;
+    float M = kMaxFloor;
+    for (int c = 0; c < np; ++c) M = fmaxf(M, a.ws[base + c]);
+    float L = 0.f, O = 0.f;
+    for (int c = 0; c < np; ++c) {
+      const float w = a.ws[nslot + base + c] * __builtin_amdgcn_exp2f(a.ws[base + c] - M);
+      L += w;
+      O = fmaf(w, a.ws[2 * nslot + (base + c) * D + dd], O);
+    }
+    a.out[((size_t)(qs + qi) * hq + hh) * D + dd] = O / L;
   }
+}
+
+template <bool I8, int D, int G, int QT, int NTW>
+hipError_t launch_prefill_t(const PrefillLaunch& p, hipStream_t stream) {
+  constexpr int WQ = kPrefillWaves * NTW * (16 / G);
+  const int64_t ngroups = (p.max_query_len + WQ - 1) / WQ;
+  const int64_t nwg = ngroups * p.pieces * p.lv.num_kv_heads * p.num_seqs;
+  if (nwg * 64 * kPrefillWaves >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
+  hipLaunchKernelGGL((prefill_kernel<I8, D, G, QT, NTW>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.pieces <= 1) return e;
+  const int64_t rows = (int64_t)p.num_seqs * p.max_query_len;
+  if (rows >= (int64_t{1} << 31)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-// Eight tiles per workgroup halve the loads and conversions per tile, but
-// leave more wavefronts idle where causal tiles of one workgroup see
-// different lengths; they are taken when four-tile workgroups would give the
-// device at most two per compute unit, i.e. few tiles over a long context.
+// Tiles per wavefront: two share each K and V operand read from LDS, except
+// where their registers would not fit two wavefronts per SIMD: an fp32 query
+// (its lo parts) and a binary16 cache at head_dim 128 (its staging pieces).
 template <bool I8, int D, int G>
 hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
-  const int64_t tiles = (p.max_query_len + 16 / G - 1) / (16 / G);
-  const int64_t wg4 = (tiles + 3) / 4 * p.lv.num_kv_heads * p.num_seqs;
-  return wg4 <= 2 * (int64_t)device_compute_units() ? launch_prefill_w<I8, D, G, 8>(p, stream)
-                                          : launch_prefill_w<I8, D, G, 4>(p, stream);
+  constexpr int NTW = I8 || D == 64 ? 2 : 1;
+  switch (p.q_dtype) {
+    case kF32: return launch_prefill_t<I8, D, G, kF32, 1>(p, stream);
+    case kF16: return launch_prefill_t<I8, D, G, kF16, NTW>(p, stream);
+    case kBF16: return launch_prefill_t<I8, D, G, kBF16, NTW>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool I8, int D>

@@ -114,8 +114,9 @@ SIGNATURES = {
     "pkv_sched_step": (C.c_int, [_vp, _vp, _i32, _vp, _vp]),
     "pkv_sched_get_stats": (C.c_int, [_vp, _vp]),
     "pkv_read_tail_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp]),
-    "pkv_prefill_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _i32,
-                                        _f32, _vp, _vp]),
+    "pkv_prefill_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
+                                        _f32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_prefill_plan": (C.c_int, [_vp, C.c_int, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
 }
@@ -474,10 +475,19 @@ class Pool:
                                 softmax_scale, out, partition_tokens, stream, flags)
         return out
 
+    def prefill_plan(self, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens=0):
+        """(piece tokens, pieces, workspace bytes) of pkv_prefill_attention for these sizes."""
+        T, n, nb = _i32(), _i32(), _sz()
+        _check(lib().pkv_prefill_plan(self.h, int(q_dtype), int(num_q_heads), int(num_seqs), int(max_query_len),
+                                      int(max_context_len), int(piece_tokens), C.byref(T), C.byref(n),
+                                      C.byref(nb)))
+        return T.value, n.value, nb.value
+
     def prefill(self, layer, q, query_start, max_query_len, block_tables, context_lens, softmax_scale,
-                out=None, stream=None):
+                max_context_len, out=None, workspace=None, piece_tokens=0, stream=None):
         """Causal attention of each sequence's last q_len cached tokens (q rows packed by
-        sequence, query_start [B+1] int32 on the device) -- pkv_prefill_attention."""
+        sequence, query_start [B+1] int32 on the device) -- pkv_prefill_attention. A
+        workspace of the planned size is allocated when none is given."""
         import torch
         for t in (q, query_start, block_tables, context_lens):
             assert t.is_contiguous()
@@ -485,11 +495,18 @@ class Pool:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         assert out.is_contiguous() and out.dtype == torch.float32 and out.shape == q.shape
+        B = int(context_lens.shape[0])
+        if workspace is None and B > 0:
+            nb = self.prefill_plan(_torch_dtype_code(q), q.shape[1], B, max_query_len, max_context_len,
+                                   piece_tokens)[2]
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
+        ws_ptr = _vp(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
         _check(lib().pkv_prefill_attention(
             self.h, layer, _vp(q.data_ptr()), _torch_dtype_code(q), int(q.shape[1]), _vp(query_start.data_ptr()),
             int(max_query_len), _vp(block_tables.data_ptr()), int(block_tables.shape[1]),
-            _vp(context_lens.data_ptr()), int(context_lens.shape[0]), float(softmax_scale),
-            _vp(out.data_ptr()), _stream_ptr(stream)))
+            _vp(context_lens.data_ptr()), B, int(max_context_len), float(softmax_scale), int(piece_tokens),
+            _vp(out.data_ptr()), ws_ptr, ws_bytes, _stream_ptr(stream)))
         return out
 
     def read_tail_blocks(self, layer, blocks):

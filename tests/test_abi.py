@@ -160,3 +160,32 @@ def test_graft_entry_build_calls_the_library_build(monkeypatch):
     entry = importlib.import_module("__graft_entry__")
     entry.build()
     assert calls == [1]
+
+
+@pytest.mark.parametrize("args,plan", [
+    # (q dtype, Hq, B, max_query_len, max_context_len, piece_tokens) -> (piece tokens, pieces, workspace bytes)
+    (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 4 * 512 * 16 * 2 * 130 * 4)),  # 256 workgroups of queries: split
+    (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0)),                         # 1024 workgroups: one piece
+    (("F32", 16, 4, 512, 8000, 0), (8000, 1, 0)),                           # one tile per wavefront: 512
+    (("BF16", 16, 1, 64, 900, 0), (960, 1, 0)),                              # under 1024 tokens: never cut
+    (("BF16", 16, 2, 64, 455, 64), (64, 8, 2 * 64 * 16 * 8 * 130 * 4)),      # explicit pieces
+    (("BF16", 16, 2, 64, 455, 512), (512, 1, 0)),
+])
+def test_prefill_plan(args, plan):
+    """The context split pkv_prefill_attention makes (a 256-CU planning
+    figure on a host-only pool): pieces only when the query tiles leave
+    compute units idle, never under 1024 tokens, workspace for the partials."""
+    from paged_kv_cache_62_amd import pkv
+    p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
+    qd, hq, B, mq, mctx, T = args
+    assert p.prefill_plan(getattr(pkv, "PKV_" + qd), hq, B, mq, mctx, T) == plan
+
+
+def test_prefill_plan_rejects_bad_arguments():
+    from paged_kv_cache_62_amd import pkv
+    p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
+    for args in [(pkv.PKV_BF16, 16, 2, 64, 455, 96), (pkv.PKV_BF16, 16, 2, 64, 455, -64),
+                 (pkv.PKV_BF16, 16, 2, 64, 32, 0), (pkv.PKV_BF16, 12, 2, 64, 455, 0),
+                 (pkv.PKV_BF16, 64, 2, 64, 455, 0), (pkv.PKV_I8, 16, 2, 64, 455, 0), (pkv.PKV_BF16, 16, 0, 64, 455, 0)]:
+        with pytest.raises(pkv.PkvError):
+            p.prefill_plan(*args)

@@ -3,7 +3,8 @@ FP64 oracle (orc_prefill_attention) over the GPU's own cache read back:
 causal attention of each sequence's last q_len cached tokens, within max-abs
 2e-3 and row max-rel 1e-2. Whole prompts, chunks at an offset, one-token
 chunks, ragged tiles; INT8 and FP16 layers; G 1/2/4; head_dim 64/128;
-block sizes 16/32/64; fp32/bf16/fp16 queries; four- and eight-tile workgroups."""
+block sizes 16/32/64; fp32/bf16/fp16 queries; one context piece and the
+context cut into pieces merged by log-sum-exp."""
 import numpy as np
 import pytest
 
@@ -14,7 +15,7 @@ from tests import harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _prefill(case, qlens, q_dtype):
+def _prefill(case, qlens, q_dtype, piece_tokens=0, max_context_len=None):
     import torch
     sh = case.shape
     pool = H.make_gpu_pool(case)
@@ -31,9 +32,13 @@ def _prefill(case, qlens, q_dtype):
     dev = pool.arena.device
     outs, refs = [], []
     rows = H.used_blocks_with_rows(o, seqs, table.shape[1])
+    mctx = int(max(lens)) if max_context_len is None else max_context_len
+    print(f"prefill case seed={case.seed} qlens={list(qlens)} piece_tokens={piece_tokens} max_ctx={mctx}",
+          flush=True)
     for layer in range(sh.layers):
         out = pool.prefill(layer, q.to(dev), torch.from_numpy(qstart).to(dev), int(max(qlens)),
-                           torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev), sh.scale)
+                           torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev), sh.scale, mctx,
+                           piece_tokens=piece_tokens)
         torch.cuda.synchronize()
         kc, vc, ks, vs = H.gpu_layer_arrays(pool, layer, rows.keys(), sh)
         refs.append(orc.prefill_attention(sh.dtype(layer), kc, vc, ks, vs, synth.as_f32(q), qstart, table, lens,
@@ -54,21 +59,24 @@ def _case(kv, hq, hkv, dim, bs, lens, seed, in_dtype="bf16", sigma="per_head"):
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (8, 2)])
 @pytest.mark.parametrize("bs", [16, 64])
-def test_prefill_whole_prompts_and_chunks(gpu, kv, hq, hkv, bs):
+@pytest.mark.parametrize("piece_tokens", [0, 64])
+def test_prefill_whole_prompts_and_chunks(gpu, kv, hq, hkv, bs, piece_tokens):
     lens = [1, 15, 16, 47, 200, 333]
     qlens = [1, 15, 16, 47, 37, 100]      # whole prompts, then chunks at an offset
     c = _case(kv, hq, hkv, 128, bs, lens, 64000 + hq * 10 + bs + kv)
-    got, ref, ma, mr = _prefill(c, qlens, "bf16")
-    print(f"prefill kv={kv} hq={hq} bs={bs}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+    got, ref, ma, mr = _prefill(c, qlens, "bf16", piece_tokens)
+    print(f"prefill kv={kv} hq={hq} bs={bs} pieces of {piece_tokens}: max_abs={ma:.3e} max_rel={mr:.3e}",
+          flush=True)
     H.assert_attention_close(got, ref)
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
 @pytest.mark.parametrize("q_dtype", ["f32", "f16"])
-def test_prefill_head_dim_64_and_query_types(gpu, kv, q_dtype):
+@pytest.mark.parametrize("piece_tokens", [0, 128])
+def test_prefill_head_dim_64_and_query_types(gpu, kv, q_dtype, piece_tokens):
     lens = [5, 64, 130]
     c = _case(kv, 4, 2, 64, 32, lens, 64100 + kv, in_dtype=q_dtype, sigma="unit")
-    got, ref, ma, mr = _prefill(c, [5, 33, 130], q_dtype)
+    got, ref, ma, mr = _prefill(c, [5, 33, 130], q_dtype, piece_tokens)
     print(f"prefill d64 kv={kv} q={q_dtype}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
     H.assert_attention_close(got, ref)
 
@@ -85,21 +93,57 @@ def test_prefill_one_token_chunks_equal_decode(gpu):
     qstart = torch.arange(4, dtype=torch.int32, device=dev)
     for layer in range(c.shape.layers):
         out = pool.prefill(layer, q, qstart, 1, torch.from_numpy(res["table"]).to(dev),
-                           torch.from_numpy(res["lens"]).to(dev), c.shape.scale)
+                           torch.from_numpy(res["lens"]).to(dev), c.shape.scale, int(res["lens"].max()))
         H.assert_attention_close(out.cpu().numpy(), res["ref"][layer])
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
-def test_prefill_many_tiles(gpu, kv):
-    """Enough tiles (4 sequences x 8 KV heads, chunks of 530-600 queries with
-    G = 2) that the launch takes four-tile workgroups on a 256-CU device; the
-    small cases above take eight-tile ones."""
+@pytest.mark.parametrize("piece_tokens", [0, 192])
+def test_prefill_many_tiles(gpu, kv, piece_tokens):
+    """Many tiles (4 sequences x 8 KV heads, chunks of 530-600 queries with
+    G = 2), the context whole or in pieces of 192 tokens: several pieces per
+    workgroup of queries, the last partial."""
     lens = [600, 620, 545, 700]
     c = _case(kv, 16, 8, 128, 16, lens, 64300 + kv)
-    got, ref, ma, mr = _prefill(c, [600, 530, 545, 580], "bf16")
+    got, ref, ma, mr = _prefill(c, [600, 530, 545, 580], "bf16", piece_tokens)
     print(f"prefill many tiles kv={kv}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
     H.assert_attention_close(got, ref)
     # P's hi + lo parts carry ~22 bits, so the error sits near 2e-5 here; a
     # hi part rounded twice (once for the product, once for the lo
     # subtraction) showed up as ~2.5e-3 on this case
     assert ma < 2e-4, f"max abs error {ma:.3e}: P split lost precision"
+
+
+def test_prefill_context_longer_than_planned(gpu):
+    """max_context_len below the real contexts (only max_query_len is
+    checked against it): the pieces are planned from it and the last piece
+    takes the rest of each context, so the result is still whole."""
+    lens = [300, 455, 210]
+    c = _case(orc.I8, 8, 2, 128, 16, lens, 64400)
+    got, ref, ma, mr = _prefill(c, [40, 64, 17], "bf16", piece_tokens=64, max_context_len=128)
+    print(f"prefill short plan: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+    H.assert_attention_close(got, ref)
+
+
+def test_prefill_plan_and_workspace_checks(gpu):
+    """The plan reports the split and its workspace; a launch that needs a
+    workspace rejects a missing or short one on the host."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    c = _case(orc.I8, 8, 2, 128, 16, [300, 455], 64500)
+    pool = H.make_gpu_pool(c)
+    T, n, nb = pool.prefill_plan(pkv.PKV_BF16, 8, 2, 64, 455, 64)
+    assert (T, n) == (64, 8) and nb == 2 * 64 * 8 * n * (2 + 128) * 4
+    assert pool.prefill_plan(pkv.PKV_BF16, 8, 2, 64, 455, 0)[1:] == (1, 0)  # short contexts: one piece
+    dev = pool.arena.device
+    q = torch.zeros(128, 8, 128, dtype=torch.bfloat16, device=dev)
+    qs = torch.tensor([0, 64, 128], dtype=torch.int32, device=dev)
+    table = torch.zeros(2, 29, dtype=torch.int32, device=dev)
+    lens = torch.tensor([300, 455], dtype=torch.int32, device=dev)
+    short = torch.empty(nb - 16, dtype=torch.uint8, device=dev)
+    with pytest.raises(pkv.PkvError):
+        pool.prefill(0, q, qs, 64, table, lens, 1.0, 455, workspace=short, piece_tokens=64)
+    with pytest.raises(pkv.PkvError):
+        pool.prefill(0, q, qs, 64, table, lens, 1.0, 455, piece_tokens=96)  # not a multiple of 64
+    with pytest.raises(pkv.PkvError):
+        pool.prefill(0, q, qs, 64, table, lens, 1.0, 32)  # max_context_len < max_query_len
