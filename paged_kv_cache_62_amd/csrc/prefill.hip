@@ -60,6 +60,25 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr float kMaxFloor = -1e30f;  // running max before any visible token (finite: no inf - inf)
 
+// The order in which a workgroup's lanes take the 16-byte pieces of a unit's
+// K (V): piece = the lane's index q with bits 2 and up permuted (dst[i] is
+// where bit 2 + i goes). Four consecutive lanes keep 64 contiguous bytes;
+// the LDS addresses the staging writes then reach from 8 (16) consecutive
+// lanes fall in distinct banks of 32 (64) banks of 4 bytes, for the row
+// pitches and V operand layout of prefill_kernel (checked exhaustively for
+// each of the four configurations when the orders were chosen).
+template <bool I8, int D>
+__device__ __forceinline__ int piece_order(int q, bool k) {
+  constexpr int n = (I8 ? D : 2 * D) == 64 ? 4 : (I8 ? D : 2 * D) == 128 ? 5 : 6;  // bits above the low two
+  constexpr int kd[4][6] = {{2, 5, 3, 4, 0, 0}, {3, 2, 4, 5, 6, 0}, {2, 6, 3, 4, 5, 0}, {2, 3, 4, 5, 6, 7}};
+  constexpr int vd[4][6] = {{2, 3, 4, 5, 0, 0}, {2, 4, 3, 5, 6, 0}, {3, 4, 2, 5, 6, 0}, {2, 5, 3, 4, 6, 7}};
+  constexpr int cfg = I8 ? (D == 64 ? 0 : 1) : (D == 64 ? 2 : 3);
+  int p = q & 3;
+#pragma unroll
+  for (int i = 0; i < n; ++i) p |= ((q >> (2 + i)) & 1) << (k ? kd[cfg][i] : vd[cfg][i]);
+  return p;
+}
+
 template <bool I8, int D, int G, int QT, int NTW>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(const PrefillLaunch a) {
@@ -73,10 +92,9 @@ void prefill_kernel(const PrefillLaunch a) {
   constexpr int QE = D / 4;                 // query, K and V elements per lane
   constexpr int GB = kUnit * D * ESZ;       // cache bytes of a unit's K (or V)
   constexpr int HP = GB / 16;               // 16-byte pieces of a unit's K (or V)
-  constexpr int NCH = 2 * HP;               // pieces per unit, K and V together
-  constexpr int SP = 2 * NCH;               // pieces per step
-  static_assert(SP % NT == 0 && HP % 64 == 0, "a wavefront's share of a step lies in one unit's K or V");
-  constexpr int CPS = SP / NT;              // pieces per thread per step
+  // A thread stages pairs: the same piece of units A and B, of K or of V
+  static_assert(HP % 64 == 0, "a wavefront's pairs lie in K or in V");
+  constexpr int PPT = (2 * HP + NT - 1) / NT;  // pairs per thread per step (some threads idle at PPT = 1)
   constexpr int PE = 16 / ESZ;              // elements per piece
   constexpr int RP = 2 * D + 16;            // LDS pitch of a binary16 K row (padded against bank conflicts)
   constexpr int VP = 16 * NDT + 16;         // LDS pitch of a lane's V operands
@@ -120,7 +138,7 @@ void prefill_kernel(const PrefillLaunch a) {
   // (masking covers what its columns do not see), so that no branch splits
   // a step's matrix-core and vector work.
   const int h = n16 % G;
-  int qi[NTW], pos[NTW], pmin[NTW];
+  int qi[NTW], pos[NTW], pmin[NTW];  // pmin grows with t
   bool colv[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
@@ -175,33 +193,25 @@ void prefill_kernel(const PrefillLaunch a) {
     const int u = u0 + min(2 * x + (lane & 1), nun - 1);
     return table[u >> lupb];
   };
-  // Thread piece c of a step: unit shV[c] (0: A, 1: B) and half shK[c] (K or
-  // V), both wave-uniform, byte shO[c] within that K (or V); the same every
-  // step. With an even count each thread takes as many K pieces as V pieces,
-  // so the wavefronts convert alike.
-  int shV[CPS], shO[CPS];
-  bool shK[CPS];
+  // Pair c of a thread: piece q of K (shK[c]) or of V, byte shO[c] of each
+  // unit's K (V), the same every step; shA[c] false for a thread without a
+  // pair c. Pieces are taken in an order (a permutation of the piece index
+  // that keeps four lanes on 64 contiguous bytes) under which the LDS
+  // writes of 8 (16) consecutive lanes fall in distinct banks of 32 (64).
+  int shO[PPT];
+  bool shK[PPT], shA[PPT];
 #pragma unroll
-  for (int c = 0; c < CPS; ++c) {
-    int v, r;
-    bool k;
-    if constexpr (CPS % 2 == 0) {
-      k = c < CPS / 2;
-      r = (int)threadIdx.x + NT * (c % (CPS / 2));  // over 2 * HP pieces of K (or V)
-      v = r / HP;
-    } else {
-      const int q = (int)threadIdx.x + NT * c;
-      v = q / NCH;
-      r = q % NCH;
-      k = r < HP;
-    }
-    shV[c] = __builtin_amdgcn_readfirstlane(v);
+  for (int c = 0; c < PPT; ++c) {
+    const int pr = (int)threadIdx.x + NT * c;
+    const bool k = pr < HP;
+    const int q = pr % HP;
+    shA[c] = __builtin_amdgcn_readfirstlane(pr < 2 * HP ? 1 : 0) != 0;
     shK[c] = __builtin_amdgcn_readfirstlane(k ? 1 : 0) != 0;
-    shO[c] = 16 * (r % HP);
+    shO[c] = 16 * piece_order<I8, D>(q, k);
   }
-  int tq[3];                 // table entries of the next requests, by step % 3
-  i32x4 ring[3][CPS];        // requested steps' pieces, by step % 3
-  float rsc[3];              // and their scales: lane 0/1 K scale of unit A/B, lane 2/3 V scale
+  int tq[3];                    // table entries of the next requests, by step % 3
+  i32x4 ring[3][PPT][2];        // requested steps' pieces, by step % 3, pair and unit
+  float rsc[3];                 // and their scales: lane 0/1 K scale of unit A/B, lane 2/3 V scale
   auto request = [&](int st, auto r) {  // wave-uniform st; r = st % 3
     const int ba = min(max(__builtin_amdgcn_readlane(tq[r], 0), 0), a.lv.num_blocks - 1);
     const int bb = min(max(__builtin_amdgcn_readlane(tq[r], 1), 0), a.lv.num_blocks - 1);
@@ -210,10 +220,14 @@ void prefill_kernel(const PrefillLaunch a) {
         ((uint64_t)ba * hkv + g) * tile_bytes + (uint64_t)((u0 + min(2 * st, nun - 1)) & umask) * GB,
         ((uint64_t)bb * hkv + g) * tile_bytes + (uint64_t)((u0 + min(2 * st + 1, nun - 1)) & umask) * GB};
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr((shK[c] ? kcodes : vcodes) + sub[shV[c]]), (short)0, GB, kRsrcWord3);
-      ring[r][c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, shO[c], 0, 0));
+    for (int c = 0; c < PPT; ++c) {
+      if (!shA[c]) continue;
+#pragma unroll
+      for (int V = 0; V < 2; ++V) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr((shK[c] ? kcodes : vcodes) + sub[V]), (short)0, GB, kRsrcWord3);
+        ring[r][c][V] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, shO[c], 0, 0));
+      }
     }
     if constexpr (I8) {
       const float* sp = (lane & 2) ? a.lv.v_scales : a.lv.k_scales;
@@ -222,45 +236,62 @@ void prefill_kernel(const PrefillLaunch a) {
     tq[r] = table_entry(st + 3);
   };
   __shared__ __align__(16) unsigned char lds[3][SS];
-  float sks[3][2], svs[3][2];  // scales of the steps in the LDS slots
-  auto stage = [&](int st, auto slot) {  // the requested step st -> LDS slot st % 3, as binary16
+  // Per LDS slot and unit (uniform): the K scale; log2 and reciprocal of the
+  // V scale; the larger binary exponent of the two V scales. Derived when
+  // the step is staged, off the path of the step that uses them.
+  float sks[3][2], lsv[3][2], isv[3][2];
+  int esv[3];
+  // The requested step st -> LDS slot st % 3, as binary16. Without a unit B
+  // (the last step of an odd count) the pieces of the last unit stand in
+  // for it: finite values, behind the causal mask and the V row limit.
+  auto stage = [&](int st, auto slot) {
+    esv[slot] = -1000;
     static_for<2>([&](auto V) {
       sks[slot][V] = 1.f;
-      svs[slot][V] = 1.f;
+      lsv[slot][V] = 0.f;
+      isv[slot][V] = 1.f;
       if constexpr (I8) {
         if (2 * st + V < nun) {
+          const float vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), 2 + V));
           sks[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), V));
-          svs[slot][V] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsc[slot]), 2 + V));
+          lsv[slot][V] = uniform_f(__builtin_amdgcn_logf(vs));
+          isv[slot][V] = uniform_f(__builtin_amdgcn_rcpf(vs));
+          int e;
+          frexpf(vs, &e);  // vs < 2^e
+          esv[slot] = max(esv[slot], __builtin_amdgcn_readfirstlane(e));
         }
       }
     });
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      const int V = shV[c];
+    for (int c = 0; c < PPT; ++c) {
+      if (!shA[c]) continue;
       const bool isk = shK[c];
-      if (2 * st + V >= nun) continue;  // (uniform) the last step of an odd count has no unit B
-      const int e = shO[c] / ESZ;       // first element of the piece within K (V)
-      const i32x4 w = ring[slot][c];
-      f16x4 x[PE / 4];
-      if constexpr (I8) {  // 16 codes -> 16 binary16 values (K signed, V stored biased)
-        const uint32_t flip = isk ? 0x80808080u : 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = biased_i8x4_to_f16x4((uint32_t)w[k] ^ flip);
-      } else {
-        x[0] = __builtin_bit_cast(f16x4, make_uint2(w[0], w[1]));
-        x[1] = __builtin_bit_cast(f16x4, make_uint2(w[2], w[3]));
-      }
+      const int e = shO[c] / ESZ;  // first element of the piece within K (V)
+      // four elements of piece V of the pair, as binary16 (INT8: K signed,
+      // V stored biased)
+      auto four = [&](int V, int k) {
+        const uint32_t w = (uint32_t)ring[slot][c][V][k];
+        if constexpr (I8) return biased_i8x4_to_f16x4(w ^ (isk ? 0x80808080u : 0u));
+        else return __builtin_bit_cast(f16x4, make_uint2(ring[slot][c][V][2 * (k & 1)], ring[slot][c][V][2 * (k & 1) + 1]));
+      };
       unsigned char* sl = lds[slot];
-      if (isk) {  // K row e / D, elements e % D ..
-        unsigned char* dst = sl + V * KS + (e / D) * RP + 2 * (e % D);
+      if (isk) {  // K row e / D of each unit, elements e % D ..
 #pragma unroll
-        for (int k = 0; k < PE / 8; ++k)
-          *(f16x8*)(dst + 16 * k) = f16x8{x[2 * k][0], x[2 * k][1], x[2 * k][2], x[2 * k][3],
-                                          x[2 * k + 1][0], x[2 * k + 1][1], x[2 * k + 1][2], x[2 * k + 1][3]};
-      } else {  // lane e / QE's V elements: four per dim tile, unit A's then unit B's
-        unsigned char* dst = sl + 2 * KS + (e / QE) * VP + 4 * (e % QE) + 8 * V;
+        for (int V = 0; V < 2; ++V) {
+          unsigned char* dst = sl + V * KS + (e / D) * RP + 2 * (e % D);
 #pragma unroll
-        for (int k = 0; k < PE / 4; ++k) *(f16x4*)(dst + 16 * k) = x[k];
+          for (int k = 0; k < PE / 8; ++k) {
+            const f16x4 x0 = four(V, 2 * k), x1 = four(V, 2 * k + 1);
+            *(f16x8*)(dst + 16 * k) = f16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          }
+        }
+      } else {  // lane e / QE's V elements: per dim tile four rows of unit A, then four of B
+        unsigned char* dst = sl + 2 * KS + (e / QE) * VP + 4 * (e % QE);
+#pragma unroll
+        for (int k = 0; k < PE / 4; ++k) {
+          const f16x4 xa = four(0, k), xb = four(1, k);
+          *(f16x8*)(dst + 16 * k) = f16x8{xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+        }
       }
     }
   };
@@ -307,15 +338,22 @@ void prefill_kernel(const PrefillLaunch a) {
     }
   };
 
-  // Step st (LDS slot): softmax from its scores sa, sb; the next step's
-  // scores (LDS slot nslot, possibly past the range: then unused) into the
-  // same arrays; O += V^T P^T, every tile.
-  auto step = [&](int st, auto slot, auto nslot, f32x4 (&sa)[NTW], f32x4 (&sb)[NTW]) {
-    const int t0 = c0 + st * 2 * kUnit;  // the step's first token
+  // V operands of the step in an LDS slot
+  auto read_v = [&](auto slot, f16x8 (&av)[NDT]) {
     const unsigned char* vl = &lds[slot][2 * KS + lane * VP];
-    f16x8 av[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) av[dt] = *(const f16x8*)&vl[16 * dt];
+  };
+
+  // Step st (LDS slot): softmax from its scores sa, sb and V operands vv;
+  // the next step's scores (LDS slot nslot, possibly past the range: then
+  // unused) into sa, sb and its V operands into vv (that slot was staged
+  // before the last barrier); O += V^T P^T, every tile.
+  auto step = [&](int st, auto slot, auto nslot, f32x4 (&sa)[NTW], f32x4 (&sb)[NTW], f16x8 (&vv)[NDT]) {
+    const int t0 = c0 + st * 2 * kUnit;  // the step's first token
+    f16x8 av[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) av[dt] = vv[dt];
     if (t0 + 2 * kUnit > vlim) {  // rows not staged, or past the context, may hold any bits
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -325,12 +363,24 @@ void prefill_kernel(const PrefillLaunch a) {
           av[dt][4 + j] = t0 + kUnit + 4 * gq + j < vlim ? av[dt][4 + j] : (_Float16)0.0f;
         }
     }
-    int evn = ev;
-    if constexpr (I8) {
-      int ea, eb;
-      frexpf(svs[slot][0], &ea);  // vscale < 2^ea
-      frexpf(svs[slot][1], &eb);
-      evn = max(ev, __builtin_amdgcn_readfirstlane(max(ea, eb)));  // one scale per unit
+    f32x4 sc[NTW], sd[NTW];  // this step's scores; sa, sb take the next step's
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      sc[t] = sa[t];
+      sd[t] = sb[t];
+    }
+    qk(nslot, sa, sb);  // first, so that the matrix cores work through what follows
+    const int evn = I8 ? max(ev, esv[slot]) : ev;
+    // some column does not see the whole step (wave-uniform; the first tile
+    // has the earliest queries, so it decides for all)
+    if (t0 + 2 * kUnit - 1 > pmin[0]) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[t][i] = t0 + 4 * gq + i <= pos[t] ? sc[t][i] : -INFINITY;
+          sd[t][i] = t0 + kUnit + 4 * gq + i <= pos[t] ? sd[t][i] : -INFINITY;
+        }
     }
     float fa[NTW], fb[NTW], lm[NTW];
     bool raise = evn > ev;
@@ -338,16 +388,9 @@ void prefill_kernel(const PrefillLaunch a) {
     for (int t = 0; t < NTW; ++t) {
       fa[t] = sks[slot][0] * qconst[t];
       fb[t] = sks[slot][1] * qconst[t];
-      if (t0 + 2 * kUnit - 1 > pmin[t]) {  // some column does not see the whole step (wave-uniform)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sa[t][i] = t0 + 4 * gq + i <= pos[t] ? sa[t][i] : -INFINITY;
-          sb[t][i] = t0 + kUnit + 4 * gq + i <= pos[t] ? sb[t][i] : -INFINITY;
-        }
-      }
       // scales are positive: the max of the raw sums times the scale is the max score
-      lm[t] = fmaxf(fmaxf(fmaxf(sa[t][0], sa[t][1]), fmaxf(sa[t][2], sa[t][3])) * fa[t],
-                    fmaxf(fmaxf(sb[t][0], sb[t][1]), fmaxf(sb[t][2], sb[t][3])) * fb[t]);
+      lm[t] = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])) * fa[t],
+                    fmaxf(fmaxf(sd[t][0], sd[t][1]), fmaxf(sd[t][2], sd[t][3])) * fb[t]);
       raise = raise || __ballot(lm[t] > m[t] + kSlack) != 0;  // wave-uniform
     }
     // the first step with a visible token raises it (m starts at a finite floor)
@@ -364,21 +407,14 @@ void prefill_kernel(const PrefillLaunch a) {
       }
       ev = evn;
     }
-    // log2 of each unit's P' / p, and its inverse for l (uniform)
+    // log2 of each unit's P' / p, and p / P' for l (uniform)
     float la = 0.f, lb = 0.f, ia = 1.f, ib = 1.f;
     if constexpr (I8) {
-      la = uniform_f(__builtin_amdgcn_logf(svs[slot][0]) + (float)(14 - kSlack - ev));
-      lb = uniform_f(__builtin_amdgcn_logf(svs[slot][1]) + (float)(14 - kSlack - ev));
-      ia = uniform_f(__builtin_amdgcn_exp2f(-la));
-      ib = uniform_f(__builtin_amdgcn_exp2f(-lb));
+      la = lsv[slot][0] + (float)(14 - kSlack - ev);
+      lb = lsv[slot][1] + (float)(14 - kSlack - ev);
+      ia = ldexpf(isv[slot][0], ev + kSlack - 14);
+      ib = ldexpf(isv[slot][1], ev + kSlack - 14);
     }
-    f32x4 sc[NTW], sd[NTW];  // this step's scores; sa, sb take the next step's
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      sc[t] = sa[t];
-      sd[t] = sb[t];
-    }
-    qk(nslot, sa, sb);
     const f16x2 m0 = {(_Float16)-1.0f, (_Float16)0.0f}, m1 = {(_Float16)0.0f, (_Float16)-1.0f};
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
@@ -414,6 +450,7 @@ void prefill_kernel(const PrefillLaunch a) {
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt], pl, o[t][dt], 0, 0, 0);
       }
     }
+    read_v(nslot, vv);
   };
 
   // prologue: steps 0 and 1 staged, 2..4 requested, the scores of step 0
@@ -432,7 +469,9 @@ void prefill_kernel(const PrefillLaunch a) {
   request(4, I1{});
   __syncthreads();
   f32x4 sa[NTW], sb[NTW];
+  f16x8 vv[NDT];
   qk(I0{}, sa, sb);
+  read_v(I0{}, vv);
 
   for (int s0 = 0; s0 < nsteps; s0 += 3) {
     // all three iterations run (a step past the end only requests and waits),
@@ -440,8 +479,10 @@ void prefill_kernel(const PrefillLaunch a) {
     static_for<3>([&](auto B) {  // step st = s0 + b in LDS slot b
       constexpr int b = decltype(B)::value;
       const int st = s0 + b;
-      if (st < nsteps) step(st, B, std::integral_constant<int, (b + 1) % 3>{}, sa, sb);
+      // slot (b + 2) % 3 was last read in step st - 1: stage into it first,
+      // so that the writes complete while the step computes
       if (st + 2 < nsteps) stage(st + 2, std::integral_constant<int, (b + 2) % 3>{});
+      if (st < nsteps) step(st, B, std::integral_constant<int, (b + 1) % 3>{}, sa, sb, vv);
       request(st + 5, std::integral_constant<int, (b + 2) % 3>{});
       __syncthreads();  // step st + 2 staged; every wavefront is done with slot b
     });
