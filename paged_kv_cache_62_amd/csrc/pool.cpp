@@ -530,6 +530,18 @@ static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t ma
   // At least one workgroup per compute unit.
   while (T > 128 && pairs * ceil_div(max_context_len, T) < cus) T /= 2;
   if (T < c.block_size) T = c.block_size;
+  // A last partition of at most a quarter of T is folded into the others:
+  // one partition fewer, all a little longer (T rounded up to the block
+  // size). Its workgroups would pay a whole start-up for a few tokens;
+  // Llama-2-7B 29 x 4141 (FP16): 9 x 512 tokens 351.5 us per launch, 8 x 528
+  // 344.2 us.
+  // (Kept only if the block-size rounding leaves no new short last partition.)
+  const int64_t P = ceil_div(max_context_len, T);
+  if (P >= 2 && max_context_len - (P - 1) * T <= T / 4) {
+    const int64_t T2 = ceil_div(ceil_div(max_context_len, P - 1), c.block_size) * c.block_size;
+    const int64_t P2 = ceil_div(max_context_len, T2);
+    if (T2 <= pkv::kMaxPartitionTokens && max_context_len - (P2 - 1) * T2 > T2 / 4) T = (int32_t)T2;
+  }
   return T;
 }
 

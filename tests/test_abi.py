@@ -89,7 +89,7 @@ def test_device_calls_on_host_only_pool_are_unsupported():
 @pytest.mark.parametrize("shape,seqs,max_ctx,flags,plan", [
     # (layers, Hkv, d, bs, blocks, dtype), B, max_context_len, flags -> (T, P, fused)
     ((28, 8, 128, 16, 2048, "I8"), 4, 8044, 0, (1024, 8, 1)),      # Qwen3-TTS talker
-    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 0, (512, 9, 0)),    # Llama-2-7B, 29 x 4096
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 0, (528, 8, 0)),    # Llama-2-7B, 29 x 4096: 8 x 528, not 9 x 512
     ((32, 32, 128, 16, 8192, "F16"), 128, 1068, 0, (2048, 1, 0)),  # Llama-2-7B, 128 x 1024
     ((32, 8, 128, 16, 15000, "I8"), 128, 1270, 0, (2048, 1, 0)),  # continuous-batching mix
     ((32, 8, 128, 16, 15000, "I8"), 32, 1024, 0, (1024, 1, 1)),    # 256 (seq, KV head) pairs: one partition
@@ -98,8 +98,12 @@ def test_device_calls_on_host_only_pool_are_unsupported():
     ((1, 2, 64, 16, 64, "I8"), 4, 600, 0, (128, 5, 1)),            # tiny
     ((1, 2, 64, 16, 64, "I8"), 4, 600, 1, (128, 5, 0)),
     ((28, 8, 128, 16, 2048, "I8"), 4, 8044, 2, (1024, 8, 1)),
-    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 2, (512, 9, 1)),
-    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 1, (512, 9, 0)),
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 2, (528, 8, 1)),
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4141, 1, (528, 8, 0)),
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4200, 0, (528, 8, 0)),     # 8 x 528 >= 4200
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4224, 0, (528, 8, 0)),     # last 512-token part of 128: folded
+    ((32, 32, 128, 16, 8192, "F16"), 29, 4300, 0, (512, 9, 0)),     # last part of 204 tokens: kept
+    ((2, 8, 128, 64, 4200, "I8"), 8, 32800, 2, (1024, 33, 1)),      # bs 64 rounding would leave 160: kept
 ])
 def test_decode_plan(shape, seqs, max_ctx, flags, plan):
     """The automatic partition size and merge placement for the benchmark shapes."""

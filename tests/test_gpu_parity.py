@@ -16,12 +16,14 @@ def _report(tag, res):
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
-@pytest.mark.parametrize("T", [16, 64, 512, 0])
+@pytest.mark.parametrize("T", [16, 64, 80, 512, 0])
 @pytest.mark.parametrize("flags", [0, 1, 2])
 def test_tiny_config(gpu, kv, T, flags):
     """Lengths 1, 15, 16, 600; 4q/2kv; d64; bs16; 64 blocks, seeded free order;
     partitions merged automatically (flags 0), in a second launch (1) or in the
-    last workgroup (2)."""
+    last workgroup (2). 80-token partitions are five units: the four
+    wavefronts of a workgroup take unequal shares, as with the automatic
+    plan's folded partition sizes."""
     res = H.run_decode_case(H.tiny_case(kv), partition_tokens=T, flags=flags)
     _report(f"tiny kv={kv} T={T} flags={flags}", res)
     H.assert_attention_close(res["gpu"], res["ref"])
@@ -177,7 +179,7 @@ def test_largest_partition(gpu, kv, bs):
 
 
 @pytest.mark.parametrize("kv", [orc.I8, orc.F16])
-@pytest.mark.parametrize("T", [16, 64, 0])
+@pytest.mark.parametrize("T", [16, 64, 80, 0])
 @pytest.mark.parametrize("flags", [1, 2])
 def test_decode_step_tiny(gpu, kv, T, flags):
     """pkv_decode_step on the tiny config (lengths 1, 15, 16, 600 -> 2, 16, 17,
