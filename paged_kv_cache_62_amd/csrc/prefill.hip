@@ -382,22 +382,49 @@ void prefill_kernel(const PrefillLaunch a) {
           sd[t][i] = t0 + kUnit + 4 * gq + i <= pos[t] ? sd[t][i] : -INFINITY;
         }
     }
-    float fa[NTW], fb[NTW], lm[NTW];
-    bool raise = evn > ev;
+    float fa[NTW], fb[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       fa[t] = sks[slot][0] * qconst[t];
       fb[t] = sks[slot][1] * qconst[t];
-      // scales are positive: the max of the raw sums times the scale is the max score
-      lm[t] = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])) * fa[t],
-                    fmaxf(fmaxf(sd[t][0], sd[t][1]), fmaxf(sd[t][2], sd[t][3])) * fb[t]);
-      raise = raise || __ballot(lm[t] > m[t] + kSlack) != 0;  // wave-uniform
+    }
+    // log2 of each unit's P' / p (uniform) and the exponent arguments
+    // s f - m + log2(P' / p), at the current m and ev
+    float la = 0.f, lb = 0.f, xa[NTW][4], xb[NTW][4];
+    auto arguments = [&]() {
+      if constexpr (I8) {
+        la = lsv[slot][0] + (float)(14 - kSlack - ev);
+        lb = lsv[slot][1] + (float)(14 - kSlack - ev);
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float ca = la - m[t], cb = lb - m[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xa[t][i] = fmaf(sc[t][i], fa[t], ca);
+          xb[t][i] = fmaf(sd[t][i], fb[t], cb);
+        }
+      }
+    };
+    arguments();
+    // raise the running max when a score exceeds it by more than kSlack (its
+    // argument, less log2(P' / p), above kSlack) or a V scale has a larger
+    // exponent
+    bool raise = evn > ev;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const float mx = fmaxf(fmaxf(fmaxf(xa[t][0], xa[t][1]), fmaxf(xa[t][2], xa[t][3])) - la,
+                             fmaxf(fmaxf(xb[t][0], xb[t][1]), fmaxf(xb[t][2], xb[t][3])) - lb);
+      raise = raise || __ballot(mx > kSlack) != 0;  // wave-uniform
     }
     // the first step with a visible token raises it (m starts at a finite floor)
     if (raise) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        const float mn = fmaxf(m[t], max_over_lane_groups(lm[t]));
+        // the step's maximum score from the raw sums (scales are positive)
+        const float lm = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])) * fa[t],
+                               fmaxf(fmaxf(sd[t][0], sd[t][1]), fmaxf(sd[t][2], sd[t][3])) * fb[t]);
+        const float mn = fmaxf(m[t], max_over_lane_groups(lm));
         const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
         l[t] *= alpha;
         const float ao = alpha * ldexpf(1.0f, ev - evn);  // times an exact power of two
@@ -406,24 +433,22 @@ void prefill_kernel(const PrefillLaunch a) {
         m[t] = mn;
       }
       ev = evn;
+      arguments();
     }
-    // log2 of each unit's P' / p, and p / P' for l (uniform)
-    float la = 0.f, lb = 0.f, ia = 1.f, ib = 1.f;
+    // p / P' for l (uniform)
+    float ia = 1.f, ib = 1.f;
     if constexpr (I8) {
-      la = lsv[slot][0] + (float)(14 - kSlack - ev);
-      lb = lsv[slot][1] + (float)(14 - kSlack - ev);
       ia = ldexpf(isv[slot][0], ev + kSlack - 14);
       ib = ldexpf(isv[slot][1], ev + kSlack - 14);
     }
     const f16x2 m0 = {(_Float16)-1.0f, (_Float16)0.0f}, m1 = {(_Float16)0.0f, (_Float16)-1.0f};
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const float ca = la - m[t], cb = lb - m[t];
       float pa[4], pb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pa[i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], fa[t], ca));  // < 2^14
-        pb[i] = __builtin_amdgcn_exp2f(fmaf(sd[t][i], fb[t], cb));
+        pa[i] = __builtin_amdgcn_exp2f(xa[t][i]);  // < 2^14
+        pb[i] = __builtin_amdgcn_exp2f(xb[t][i]);
       }
       const float sA = (pa[0] + pa[1]) + (pa[2] + pa[3]), sB = (pb[0] + pb[1]) + (pb[2] + pb[3]);
       l[t] += I8 ? fmaf(sA, ia, sB * ib) : sA + sB;
