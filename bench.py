@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 
 # rocprofv3 FETCH_SIZE + WRITE_SIZE summaries (scaled by a plain-copy reference)
-# per workload; used only while the kernel source still has the hash they record.
+# per workload; used only while the kernel sources they depend on still have
+# the hash they record.
 TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md",
                     "mix16": "profiles/decode_kernel_mix_bs16_int8.md",
@@ -42,7 +43,14 @@ TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "prefill2k": "profiles/prefill_kernel_qwen3_tts_prompt2048_int8.md"}
 
 
+# The kernel sources, and those each workload's launches are built from.
 KERNEL_SOURCES = ("device.h", "append.hip", "decode.hip", "prefill.hip")
+DECODE_SOURCES = ("device.h", "append.hip", "decode.hip")
+PREFILL_SOURCES = ("device.h", "prefill.hip")
+
+
+def workload_sources(config):
+    return PREFILL_SOURCES if config.startswith("prefill") else DECODE_SOURCES
 
 
 def code_hash(text):
@@ -55,16 +63,17 @@ def code_hash(text):
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-def kernels_code_hash():
-    """code_hash of the kernel sources (device.h, append.hip, decode.hip,
-    prefill.hip, concatenated in that order)."""
+def kernels_code_hash(sources=KERNEL_SOURCES):
+    """code_hash of the given kernel sources (paged_kv_cache_62_amd/csrc),
+    concatenated in that order."""
     return code_hash("\n".join(open(os.path.join(ROOT, "paged_kv_cache_62_amd", "csrc", name),
-                                    encoding="utf-8").read() for name in KERNEL_SOURCES))
+                                    encoding="utf-8").read() for name in sources))
 
 
 def measured_traffic(config):
-    """HBM bytes per decode launch from the committed counter summary, or
-    None when there is none or the kernels' code changed since it was taken."""
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the code of the kernels the workload runs changed since
+    it was taken."""
     import re
     path = TRAFFIC_PROFILES.get(config)
     if path is None or not os.path.exists(os.path.join(ROOT, path)):
@@ -72,7 +81,7 @@ def measured_traffic(config):
     text = open(os.path.join(ROOT, path), encoding="utf-8").read()
     t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
     h = re.search(r"kernels_code_sha256: ([0-9a-f]{64})", text)
-    if not t or not h or kernels_code_hash() != h.group(1):
+    if not t or not h or kernels_code_hash(workload_sources(config)) != h.group(1):
         return None
     return int(t.group(1))
 

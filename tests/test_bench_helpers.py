@@ -22,6 +22,10 @@ def test_kernels_code_hash_covers_every_kernel_source():
     built = {os.path.basename(s) for s in build.SOURCES if s.endswith(".hip")}
     assert built <= set(bench.KERNEL_SOURCES)
     assert len(bench.kernels_code_hash()) == 64
+    # decode workloads key on the append and decode units, prefill on its own
+    assert set(bench.workload_sources("qwen")) == {"device.h", "append.hip", "decode.hip"}
+    assert set(bench.workload_sources("prefill512")) == {"device.h", "prefill.hip"}
+    assert bench.kernels_code_hash(bench.DECODE_SOURCES) != bench.kernels_code_hash(bench.PREFILL_SOURCES)
 
 
 def test_committed_summaries_parse():
