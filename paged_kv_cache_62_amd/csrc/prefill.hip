@@ -18,13 +18,13 @@ namespace {
 // of one sequence and KV head, NTW per wavefront, and streams a range of that
 // head's context (the whole of what its queries see, or one piece of it)
 // through them in steps of two 16-token units (A, B). Its wavefronts read the
-// same units, so the workgroup loads each once: every thread requests 16-byte
-// pieces of a step into registers three steps ahead and writes them into a
-// three-slot LDS ring as binary16 (INT8 codes convert exactly; the block
-// scales stay factors of the scores and of P). Each wavefront's share of a
-// step lies in one unit's K or V, so its requests are one buffer descriptor
-// (scalar) and a fixed per-lane offset. Per step and wavefront, for each of
-// its tiles (the K and V operands read from LDS once for all of them):
+// same units, so the workgroup loads each once: every thread requests the same
+// 16-byte piece of both units of a step (of K or of V, alike across its
+// wavefront, so each request is a scalar buffer descriptor and a fixed
+// per-lane offset) into registers three steps ahead, and writes the pair into
+// a three-slot LDS ring as binary16 (INT8 codes convert exactly; the block
+// scales stay factors of the scores and of P). Per step and wavefront, for
+// each of its tiles (the K and V operands read from LDS once for all of them):
 //   S^T[token][col] = K[token][:] . Q^T[:][col]   per unit (fp16 products, fp32 sums)
 //   O^T[dim][col]  += V^T[dim][k] . P^T[k][col]   over the step's 32 tokens, P as
 //                                                 fp16 hi + lo parts
@@ -41,10 +41,11 @@ namespace {
 // exceeds it by more. The running max starts at a finite floor, so a column
 // that sees no token of the workgroup's range keeps zero weights.
 //
-// The loop is software-pipelined: a wavefront issues the QK products of step
-// st + 1 before the softmax of step st, so its vector ALU work overlaps the
-// matrix-core queue; the ring holds step st (V), st + 1 (K) and st + 2 (being
-// written).
+// The loop is software-pipelined. Step st first stages step st + 2 into the
+// slot step st - 1 last read, then issues the QK products of step st + 1,
+// then the softmax and PV products of step st, and reads the V operands of
+// step st + 1 last; one barrier per step. The ring holds step st (V read a
+// step early), st + 1 (K) and st + 2 (being written).
 //
 // Context pieces: with few query tiles over a long context, the context is
 // cut into pieces of piece_tokens (a multiple of 64) and each (tile group,
@@ -61,8 +62,8 @@ namespace {
 constexpr float kMaxFloor = -1e30f;  // running max before any visible token (finite: no inf - inf)
 
 // The order in which a workgroup's lanes take the 16-byte pieces of a unit's
-// K (V): piece = the lane's index q with bits 2 and up permuted (dst[i] is
-// where bit 2 + i goes). Four consecutive lanes keep 64 contiguous bytes;
+// K (V): piece = the lane's index q with bits 2 and up permuted (kd[cfg][i],
+// vd[cfg][i] is where bit 2 + i goes). Four consecutive lanes keep 64 contiguous bytes;
 // the LDS addresses the staging writes then reach from 8 (16) consecutive
 // lanes fall in distinct banks of 32 (64) banks of 4 bytes, for the row
 // pitches and V operand layout of prefill_kernel (checked exhaustively for
