@@ -923,7 +923,7 @@ class PrefillWorkload:
         # the context split and its workspace, planned once (every layer's
         # launch reuses it in turn on the one stream)
         self.piece_tokens, self.pieces, nb = self.pool.prefill_plan(pkv.PKV_BF16, hq, B, C, ctx, piece_tokens)
-        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
+        self.ws = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
 
     def prefill(self, layer):
         self.pool.prefill(layer, self.qs[layer], self.d_qstart, self.C, self.d_table, self.d_lens, self.scale,
@@ -1020,11 +1020,10 @@ def run_prefill(args, stream):
                    "context_pieces": w.pieces, "piece_tokens": w.piece_tokens if w.pieces > 1 else None},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": measured_traffic(args.config),
-                     "kernel": ("prefill_kernel (causal paged attention, fp16 matrix cores)"
-                                + (" + prefill_merge_kernel" if w.pieces > 1 else "")),
+                     "kernel": ("prefill_kernel (causal paged attention, fp16 matrix cores"
+                                + (", context pieces merged by the last to finish)" if w.pieces > 1 else ")")),
                      "avg_launch_us": avg_dur_s * 1e6, "flops_per_launch": flops,
-                     "timing": (f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"
-                                + (" (each with its merge launch)" if w.pieces > 1 else ""))},
+                     "timing": f"HIP events around {args.steps} replays of a graph of the {L} prefill launches"},
     }
     res["_workload"] = w
     return res

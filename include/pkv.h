@@ -184,10 +184,17 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, const void* k, const voi
                          pkv_dtype in_dtype, const int64_t* slot_mapping, int32_t n_tokens,
                          void* stream);
 
-/* Workspace bytes pkv_decode_attention needs for these sizes: one int32
- * arrival counter per (sequence, KV head), then the partition partials m, l
- * and o/l in fp32. 0 when every sequence fits in one partition.
- * partition_tokens 0 = the automatic choice. */
+/* Every decode and prefill workspace starts with PKV_MERGE_COUNTER_BYTES of
+ * int32 arrival counters (the merges done by the last workgroup to finish use
+ * the first ones; a call leaves them at zero), whatever the call's sizes: so
+ * one zero-filled workspace serves calls of any sizes in turn, none of
+ * whose partials ever overwrite the counters another call reads. */
+#define PKV_MERGE_COUNTER_BYTES 65536
+
+/* Workspace bytes pkv_decode_attention needs for these sizes: the counter
+ * prefix (one counter per (sequence, KV head) for a fused merge), then the
+ * partition partials m, l and o/l in fp32. 0 when every sequence fits in
+ * one partition. partition_tokens 0 = the automatic choice. */
 size_t pkv_decode_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_tokens);
 
@@ -199,7 +206,9 @@ int32_t pkv_decode_auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_
 /* flags for pkv_decode_attention (0: automatic merge placement) */
 #define PKV_DECODE_SEPARATE_MERGE 1 /* merge partitions in a second launch */
 #define PKV_DECODE_FUSED_MERGE 2    /* merge partitions in the last workgroup of
-                                       each (seq, KV head) to finish */
+                                       each (seq, KV head) to finish; at most
+                                       PKV_MERGE_COUNTER_BYTES / 4 (seq, KV head)
+                                       pairs, else PKV_ERR_UNSUPPORTED */
 #define PKV_DECODE_VALU_CONTRACTION 4 /* pkv_decode_attention only, for comparing the two
                                        forms: the same launch with both contractions (q.k
                                        and p.v) as fp32 FMAs on the vector ALUs instead of
@@ -233,12 +242,13 @@ pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_c
  *     log-sum-exp merge, done by the last workgroup of each (sequence, KV
  *     head) to finish (PKV_DECODE_FUSED_MERGE) or by a second launch
  *     (PKV_DECODE_SEPARATE_MERGE). flags 0 picks the first when the whole
- *     grid fits on the device at once, the second otherwise; both flags set
- *     is an error.
+ *     grid fits on the device at once (and its counters fit the prefix), the
+ *     second otherwise; both flags set is an error.
  *   workspace: at least pkv_decode_workspace_bytes(...) bytes (device). It
  *     must be zero-filled before its first use; every call leaves its
- *     counters at zero again, so one workspace serves any number of calls on
- *     one stream (calls that overlap in time need separate workspaces).
+ *     counters at zero again, so one workspace serves any number of calls of
+ *     any sizes on one stream (calls that overlap in time need separate
+ *     workspaces).
  * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4}. */
 pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, const void* q, pkv_dtype q_dtype,
                                 int32_t num_q_heads, const int32_t* block_tables,
@@ -311,13 +321,20 @@ pkv_status pkv_decode_step_noalloc(pkv_pool* pool, int32_t layer, const void* q,
  *     longer context is still computed in full, only less evenly split).
  *   piece_tokens: context split (0 = automatic, else a multiple of 64): each
  *     sequence's context is cut into pieces of this many tokens, each (group
- *     of query tiles, piece) one workgroup, and a second launch merges the
- *     pieces' partial softmax sums per query (log-sum-exp, as the decode
- *     partitions). The automatic split cuts only when the query tiles alone
- *     would leave compute units idle. pkv_prefill_plan gives the split.
+ *     of query tiles, piece) one workgroup; the last workgroup of a tile
+ *     group to finish merges its pieces' partial softmax sums per query
+ *     (log-sum-exp, as the decode partitions). The automatic split cuts only
+ *     when the query tiles alone would leave compute units idle.
+ *     pkv_prefill_plan gives the split.
  *   workspace: device memory of at least the bytes pkv_prefill_plan gives
- *     (16-byte aligned), holding the partials; may be NULL when that is 0
- *     (one piece). Calls that overlap in time need separate workspaces.
+ *     (16-byte aligned): the counter prefix (PKV_MERGE_COUNTER_BYTES; one
+ *     counter per (sequence, KV head, group of query tiles), at most
+ *     PKV_MERGE_COUNTER_BYTES / 4, else PKV_ERR_UNSUPPORTED), then the
+ *     partials; may be NULL when that is 0 (one piece). It must be
+ *     zero-filled before its first use; every call leaves its counters at
+ *     zero again, so one workspace serves any number of calls on one stream,
+ *     decode calls included (calls that overlap in time need separate
+ *     workspaces).
  * The K/V operands go through fp16 matrix-core products (INT8 codes convert
  * exactly), probabilities as fp16 hi + lo parts, fp32 accumulation.
  * Supported: head_dim 64/128, num_q_heads/num_kv_heads in {1,2,4}, F16 and

@@ -98,10 +98,12 @@ struct PrefillLaunch {
   float* out;                 // [total][Hq][d] fp32
   // Context split: pieces of piece_tokens (a multiple of 64; the last piece
   // takes the rest), each (query tile group, piece) one workgroup; with
-  // pieces > 1 their partials go to ws and a merge launch combines them.
+  // pieces > 1 their partials go to ws and the last piece of each tile group
+  // to finish merges them.
   int32_t pieces;
   int32_t piece_tokens;
-  float* ws;                  // prefill_workspace_bytes(...) bytes when pieces > 1
+  int32_t* counters;          // [num_seqs][Hkv][tile groups] arrival counters (zero between calls)
+  float* ws;                  // partials m, l [num_seqs][max_query_len][Hq][pieces], then o (x head_dim)
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
@@ -123,9 +125,22 @@ constexpr int prefill_query_tokens_per_workgroup(int group, int q_dtype) {
 void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
                   int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
                   int32_t* pieces_out);
-// Workspace bytes of a launch with this many pieces (0 for one piece).
+// Query tile groups per (sequence, KV head) of any prefill launch: at most
+// this many (at least one 16 / group query-token tile per wavefront).
+constexpr int32_t prefill_tile_groups_bound(int32_t max_query_len, int32_t group) {
+  return (max_query_len + kPrefillWaves * (16 / group) - 1) / (kPrefillWaves * (16 / group));
+}
+// Workspace bytes of a launch with this many pieces (0 for one piece): the
+// counter prefix, then the partials.
 size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads, int32_t head_dim,
                                int32_t pieces);
+
+// Arrival counters of the merges that the last workgroup to finish does: the
+// first kMergeCounterBytes of every decode or prefill workspace, whatever the
+// call's sizes, so that no call's partials land on counters a later call
+// reads (every call leaves the counters it used at zero).
+constexpr size_t kMergeCounterBytes = size_t{64} << 10;
+constexpr int64_t kMergeCounters = int64_t(kMergeCounterBytes / sizeof(int32_t));
 
 // Longest decode partition (tokens) the kernels take.
 constexpr int32_t kMaxPartitionTokens = 4096;
@@ -139,8 +154,7 @@ int device_compute_units();
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 
-// Workspace: counters first (256-byte aligned), then the partials.
-size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
+// Workspace: the counter prefix, then the partials (0 bytes for one partition).
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t max_partitions);
 

@@ -12,10 +12,6 @@
 
 namespace pkv {
 
-namespace {
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-}  // namespace
-
 int device_compute_units() {
   static std::atomic<int> cus[64];
   int dev = 0;
@@ -32,15 +28,11 @@ bool decode_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
 }
 
-size_t decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
-}
-
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t max_partitions) {
   if (max_partitions <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
-  return decode_counter_bytes(num_seqs, num_kv_heads) + rows * (2 + (size_t)head_dim) * sizeof(float);
+  return kMergeCounterBytes + rows * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
@@ -66,7 +58,7 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t 
                                int32_t pieces) {
   if (pieces <= 1) return 0;
   const size_t slots = (size_t)num_seqs * max_query_len * num_q_heads * pieces;
-  return slots * (2 + (size_t)head_dim) * sizeof(float);
+  return kMergeCounterBytes + slots * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 }  // namespace pkv

@@ -551,7 +551,19 @@ static int32_t auto_partition(const pkv_pool* pool, int32_t num_seqs, int32_t ma
 static int32_t plan_fused_merge(const pkv_pool* pool, int32_t num_seqs, int32_t P, int32_t flags) {
   if (flags & PKV_DECODE_FUSED_MERGE) return 1;
   if (flags & PKV_DECODE_SEPARATE_MERGE) return 0;
-  return (int64_t)num_seqs * pool->cfg.num_kv_heads * P <= resident_workgroups(pool) ? 1 : 0;
+  const int64_t pairs = (int64_t)num_seqs * pool->cfg.num_kv_heads;
+  return pairs <= pkv::kMergeCounters && pairs * P <= resident_workgroups(pool) ? 1 : 0;
+}
+
+// A fused merge counts arrivals in the workspace's counter prefix: one
+// counter per (sequence, KV head).
+static_assert(PKV_MERGE_COUNTER_BYTES == pkv::kMergeCounterBytes, "counter prefix of pkv.h and the kernels");
+
+static pkv_status check_fused_counters(const pkv_pool* pool, int32_t num_seqs, int32_t P, int32_t fused) {
+  if (fused && P > 1 && (int64_t)num_seqs * pool->cfg.num_kv_heads > pkv::kMergeCounters)
+    return fail(PKV_ERR_UNSUPPORTED, "PKV_DECODE_FUSED_MERGE over %lld (sequence, KV head) pairs; at most %lld",
+                (long long)num_seqs * pool->cfg.num_kv_heads, (long long)pkv::kMergeCounters);
+  return ok();
 }
 
 static bool valid_flags(int32_t flags) {
@@ -575,7 +587,10 @@ pkv_status pkv_decode_plan(const pkv_pool* pool, int32_t num_seqs, int32_t max_c
   const int32_t P = (max_context_len + T - 1) / T;
   if (partition_out) *partition_out = T;
   if (partitions_out) *partitions_out = P;
-  if (fused_merge_out) *fused_merge_out = plan_fused_merge(pool, num_seqs, P, flags);
+  const int32_t fused = plan_fused_merge(pool, num_seqs, P, flags);
+  const pkv_status st = check_fused_counters(pool, num_seqs, P, fused);
+  if (st != PKV_OK) return st;
+  if (fused_merge_out) *fused_merge_out = fused;
   return ok();
 }
 
@@ -653,8 +668,10 @@ static pkv_status decode_launch(pkv_pool* pool, int32_t layer, const void* q, pk
   d.softmax_scale = softmax_scale;
   d.out = out;
   d.counters = (int32_t*)workspace;
-  d.ws = need > 0 ? (float*)((char*)workspace + pkv::decode_counter_bytes(num_seqs, c.num_kv_heads)) : nullptr;
+  d.ws = need > 0 ? (float*)((char*)workspace + pkv::kMergeCounterBytes) : nullptr;
   d.fused_merge = plan_fused_merge(pool, num_seqs, P, flags);
+  const pkv_status fst = check_fused_counters(pool, num_seqs, P, d.fused_merge);
+  if (fst != PKV_OK) return fst;
   d.valu_contraction = valu ? 1 : 0;
   d.k_new = k_new;
   d.v_new = v_new;
@@ -743,6 +760,18 @@ static pkv_status prefill_check(const pkv_pool* pool, pkv_dtype q_dtype, int32_t
   return ok();
 }
 
+// A split context counts arrivals in the workspace's counter prefix: one
+// counter per (sequence, KV head, query tile group).
+static pkv_status check_prefill_counters(const pkv_pool* pool, int32_t num_q_heads, int32_t num_seqs,
+                                         int32_t max_query_len, int32_t pieces) {
+  const int32_t hkv = pool->cfg.num_kv_heads;
+  const int64_t n = (int64_t)num_seqs * hkv * pkv::prefill_tile_groups_bound(max_query_len, num_q_heads / hkv);
+  if (pieces > 1 && n > pkv::kMergeCounters)
+    return fail(PKV_ERR_UNSUPPORTED, "context pieces over %lld (sequence, KV head, query tile group) triples; at most %lld",
+                (long long)n, (long long)pkv::kMergeCounters);
+  return ok();
+}
+
 pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
                             int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
                             int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out) {
@@ -754,6 +783,8 @@ pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num
   int32_t T = 0, n = 0;
   pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
                     max_context_len, piece_tokens, &T, &n);
+  const pkv_status cst = check_prefill_counters(pool, num_q_heads, num_seqs, max_query_len, n);
+  if (cst != PKV_OK) return cst;
   if (piece_tokens_out) *piece_tokens_out = T;
   if (pieces_out) *pieces_out = n;
   if (workspace_bytes_out)
@@ -784,6 +815,8 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   int32_t T = 0, n = 0;
   pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
                     max_context_len, piece_tokens, &T, &n);
+  const pkv_status cst = check_prefill_counters(pool, num_q_heads, num_seqs, max_query_len, n);
+  if (cst != PKV_OK) return cst;
   const size_t need = pkv::prefill_workspace_bytes(num_seqs, max_query_len, num_q_heads, c.head_dim, n);
   if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
     return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes at %p, %zu bytes (16-byte aligned) needed",
@@ -803,7 +836,10 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   p.out = out;
   p.pieces = n;
   p.piece_tokens = T;
-  p.ws = n > 1 ? (float*)workspace : nullptr;
+  if (n > 1) {
+    p.counters = (int32_t*)workspace;
+    p.ws = (float*)((char*)workspace + pkv::kMergeCounterBytes);
+  }
   hipError_t e = pkv::launch_prefill(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

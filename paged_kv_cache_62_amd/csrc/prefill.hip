@@ -51,8 +51,9 @@ namespace {
 // cut into pieces of piece_tokens (a multiple of 64) and each (tile group,
 // piece) is a workgroup. Each writes, per (query, head), its partial (m, l,
 // o/l) -- m the base-2 running max, l the sum of weights relative to it --
-// and prefill_merge_kernel combines the pieces a query sees. With one piece
-// the workgroup writes the output itself.
+// and counts its arrival; the last piece of a tile group to finish combines
+// the group's pieces (log-sum-exp) and writes the output. With one piece the
+// workgroup writes the output itself.
 //
 // Workgroups are numbered so that those of one (sequence, KV head, piece)
 // run on one XCD, whose L2 then serves that context range to all of them
@@ -514,67 +515,124 @@ void prefill_kernel(const PrefillLaunch a) {
     });
   }
 
-  // the output (one piece), or this piece's partial (m, l, o/l)
+  // The output, or this piece's partial (m, l, o/l) and, in the last piece of
+  // the tile group to finish, the merge of all its pieces. The tile group runs
+  // the pieces that start at or before plast; a piece holds l = 0 (and m at
+  // the floor) for a column that sees none of its tokens, which weighs nothing
+  // in the merge.
   const float oscale = ldexpf(1.0f, I8 ? ev + kSlack - 14 : 0);
+  const int nvis = min(plast / a.piece_tokens + 1, npc);
+  float lt[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) lt[t] = sum_over_lane_groups(l[t]);
+  if (nvis == 1) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      if (!colv[t]) continue;
+      float* dst = a.out + ((size_t)(qs + qi[t]) * hq + g * G + h) * D;
+      const float inv = oscale / lt[t];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
+    }
+    return;
+  }
+  // Partials, piece-major: slot (piece, sequence, query, head). They are
+  // written through to the point of coherence of all XCDs (device scope: the
+  // o/l vectors as 16-byte stores with the SC1 cache-policy bit, m and l as
+  // atomic stores), so the workgroup that merges them needs no cache
+  // write-back or invalidate. Lane (n16, gq) holds dims 16 dt + 4 gq .. + 3 of
+  // its column: four lanes write 64 contiguous bytes of a row.
+  constexpr int kScopeDevice = 16;  // cache-policy operand of buffer instructions: SC1
+  const size_t nrow = (size_t)a.num_seqs * a.max_query_len * hq;  // slots per piece
+  float* ws_m = a.ws;
+  float* ws_l = a.ws + nrow * npc;
+  float* ws_o = a.ws + 2 * nrow * npc;
+  const int col = (n16 / G) * hq + h;  // the lane's slot past its tile's first
+  const uint32_t lane_off = (uint32_t)(col * D + 4 * gq) * 4;
+  // tile t's first slot of piece c (the same in every lane)
+  auto tile_slot = [&](int t, int c) {
+    return (size_t)c * nrow + ((size_t)s * a.max_query_len + qi[t] - n16 / G) * hq + g * G;
+  };
+  auto o_rsrc = [&](int t, int c) {
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(ws_o + tile_slot(t, c) * D), (short)0, 0x7fffffff,
+                                             kRsrcWord3);
+  };
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
-    const float lt = sum_over_lane_groups(l[t]);
     if (!colv[t]) continue;
-    const size_t row = (size_t)s * a.max_query_len + qi[t];  // (sequence, query) slot of the workspace
-    if (npc == 1) {
-      float* dst = a.out + ((size_t)(qs + qi[t]) * hq + g * G + h) * D;
-      const float inv = oscale / lt;
+    const float inv = lt[t] > 0.f ? oscale / lt[t] : 0.f;
+    const auto rs = o_rsrc(t, piece);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[t][dt] * inv), rs, lane_off + 64 * dt, 0,
+                                             kScopeDevice);
+    if (gq == 0) {
+      const size_t slot = tile_slot(t, piece) + col;
+      __hip_atomic_store(&ws_m[slot], m[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws_l[slot], lt[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // Every thread's stores complete before the barrier; then one thread counts
+  // the arrival, and the workgroup that brings the count to nvis merges.
+  __shared__ int sm_last;
+  int32_t* counter = a.counters + ((size_t)s * hkv + g) * ngroups + grp;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nvis - 1;
+  __syncthreads();
+  if (!sm_last) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
-    } else {
-      const size_t slot = (row * hq + g * G + h) * npc + piece;
-      const size_t nslot = (size_t)a.num_seqs * a.max_query_len * hq * npc;
-      const float inv = lt > 0.f ? oscale / lt : 0.f;
-      float* dst = a.ws + 2 * nslot + slot * D;
+  for (int t = 0; t < NTW; ++t) {
+    if (!colv[t]) continue;
+    const float inv = lt[t] > 0.f ? oscale / lt[t] : 0.f;
+    // pieces in order, each folded in against the running maximum M:
+    //   M' = max(M, m_c),  L' = L 2^(M - M') + l_c 2^(m_c - M'),  O' likewise with l_c (o/l)_c
+    float M = kMaxFloor, L = 0.f;
+    f32x4 O[NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nvis; ++c) {
+      float mc, lc;
+      f32x4 oc[NDT];
+      if (c == piece) {
+        mc = m[t];
+        lc = lt[t];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = o[t][dt][i] * inv;
-      if (gq == 0) {
-        a.ws[slot] = m[t];
-        a.ws[nslot + slot] = lt;
+        for (int dt = 0; dt < NDT; ++dt) oc[dt] = o[t][dt] * inv;
+      } else {
+        const size_t slot = tile_slot(t, c) + col;
+        mc = __hip_atomic_load(&ws_m[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lc = __hip_atomic_load(&ws_l[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const auto rs = o_rsrc(t, c);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          oc[dt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + 64 * dt, 0,
+                                                                                   kScopeDevice));
       }
+      const float Mn = fmaxf(M, mc);
+      const float rs = __builtin_amdgcn_exp2f(M - Mn);
+      const float w = lc * __builtin_amdgcn_exp2f(mc - Mn);
+      L = fmaf(L, rs, w);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[dt][i] = fmaf(w, oc[dt][i], O[dt][i] * rs);
+      M = Mn;
     }
+    float* dst = a.out + ((size_t)(qs + qi[t]) * hq + g * G + h) * D;
+    const float rl = 1.0f / L;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[16 * dt + 4 * gq + i] = O[dt][i] * rl;
   }
-}
-
-// The pieces a query sees, merged: for query i of sequence s at position p,
-// pieces 0 .. p / piece_tokens, each with its partial (m, l, o/l):
-//   M = max m,  w = l * 2^(m - M),  out = sum w * (o/l) / sum w.
-// One workgroup per (sequence, query); 256 / D heads at a time.
-template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillLaunch a) {
-  const int mq = a.max_query_len;
-  const int s = blockIdx.x / mq, qi = blockIdx.x % mq;
-  const int qs = a.query_start[s];
-  const int ql = min(a.query_start[s + 1] - qs, mq);
-  const int len = min(a.lens[s], a.max_blocks * a.lv.block_size);
-  if (qi >= ql || ql > len) return;
-  const int p = len - ql + qi;
-  const int npc = a.pieces, np = min(p / a.piece_tokens + 1, npc);
-  const int hq = a.num_q_heads;
-  const size_t nslot = (size_t)a.num_seqs * mq * hq * npc;
-  const size_t row = (size_t)s * mq + qi;
-  const int dd = threadIdx.x % D;
-  for (int hh = threadIdx.x / D; hh < hq; hh += 256 / D) {
-    const size_t base = (row * hq + hh) * npc;
-    float M = kMaxFloor;
-    for (int c = 0; c < np; ++c) M = fmaxf(M, a.ws[base + c]);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < np; ++c) {
-      const float w = a.ws[nslot + base + c] * __builtin_amdgcn_exp2f(a.ws[base + c] - M);
-      L += w;
-      O = fmaf(w, a.ws[2 * nslot + (base + c) * D + dd], O);
-    }
-    a.out[((size_t)(qs + qi) * hq + hh) * D + dd] = O / L;
-  }
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool I8, int D, int G, int QT, int NTW>
@@ -583,13 +641,10 @@ hipError_t launch_prefill_t(const PrefillLaunch& p, hipStream_t stream) {
   const int64_t ngroups = (p.max_query_len + WQ - 1) / WQ;
   const int64_t nwg = ngroups * p.pieces * p.lv.num_kv_heads * p.num_seqs;
   if (nwg * 64 * kPrefillWaves >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
+  if (p.pieces > 1 && ngroups * p.lv.num_kv_heads * p.num_seqs > kMergeCounters)  // one counter per tile group
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<I8, D, G, QT, NTW>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, stream,
                      p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.pieces <= 1) return e;
-  const int64_t rows = (int64_t)p.num_seqs * p.max_query_len;
-  if (rows >= (int64_t{1} << 31)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

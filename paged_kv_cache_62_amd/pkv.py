@@ -37,6 +37,7 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
 PKV_DECODE_SEPARATE_MERGE = 1
 PKV_DECODE_FUSED_MERGE = 2
 PKV_DECODE_VALU_CONTRACTION = 4  # comparison variant: both contractions on the vector ALUs
+MERGE_COUNTER_BYTES = 65536  # PKV_MERGE_COUNTER_BYTES: the arrival-counter prefix of every workspace
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p
@@ -499,7 +500,7 @@ class Pool:
         if workspace is None and B > 0:
             nb = self.prefill_plan(_torch_dtype_code(q), q.shape[1], B, max_query_len, max_context_len,
                                    piece_tokens)[2]
-            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
+            workspace = torch.zeros(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
         ws_ptr = _vp(workspace.data_ptr()) if workspace is not None else None
         ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
         _check(lib().pkv_prefill_attention(

@@ -38,6 +38,49 @@ def test_library_exports_every_declared_symbol():
         assert name in pkv.SIGNATURES, f"{name} missing from the binding"
 
 
+def test_binding_constants_match_the_header():
+    from paged_kv_cache_62_amd import pkv
+    text = open(HEADER, encoding="utf-8").read()
+    defines = dict(re.findall(r"#define (PKV_\w+) (\d+)", text))
+    assert int(defines["PKV_MERGE_COUNTER_BYTES"]) == pkv.MERGE_COUNTER_BYTES
+    for name in ("PKV_DECODE_SEPARATE_MERGE", "PKV_DECODE_FUSED_MERGE", "PKV_DECODE_VALU_CONTRACTION",
+                 "PKV_EV_ADMIT", "PKV_EV_EOS", "PKV_EV_MAX_LENGTH", "PKV_EV_PREEMPT", "PKV_EV_WAIT"):
+        assert int(defines[name]) == getattr(pkv, name), name
+
+
+def test_workspaces_start_with_the_counter_prefix():
+    """Decode and prefill workspaces: the fixed counter prefix, then the
+    partials (decode: m, l, o/l per (sequence, query head, partition));
+    nothing when there is a single partition or piece."""
+    from paged_kv_cache_62_amd import pkv
+    p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
+    assert p.workspace_bytes(4, 16, 8000, 1024) == pkv.MERGE_COUNTER_BYTES + 4 * 16 * 8 * 130 * 4
+    assert p.workspace_bytes(3, 8, 100, 64) == pkv.MERGE_COUNTER_BYTES + 3 * 8 * 2 * 130 * 4
+    assert p.workspace_bytes(4, 16, 1000, 1024) == 0
+
+
+def test_merge_counters_bound_fused_merges_and_context_pieces():
+    """One counter per (sequence, KV head) for a fused decode merge and per
+    (sequence, KV head, query tile group) for a split prefill context: a
+    forced fused merge or a forced split beyond the prefix is refused on the
+    host, the automatic decode plan falls back to the separate merge."""
+    from paged_kv_cache_62_amd import pkv
+    n = pkv.MERGE_COUNTER_BYTES // 4
+    p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
+    seqs = n // 8
+    assert p.decode_plan(seqs, 4096, 1024, pkv.PKV_DECODE_FUSED_MERGE) == (1024, 4, 1)
+    with pytest.raises(pkv.PkvError) as e:
+        p.decode_plan(seqs + 1, 4096, 1024, pkv.PKV_DECODE_FUSED_MERGE)
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+    assert p.decode_plan(seqs + 1, 4096, 1024, 0)[2] == 0
+    # prefill: 16 query heads over 8 KV heads, 32-query tile groups at most
+    assert p.prefill_plan(pkv.PKV_BF16, 16, 64, 1024, 4096, 2048)[1] == 2  # 64 x 8 x 32 = n counters
+    with pytest.raises(pkv.PkvError) as e:
+        p.prefill_plan(pkv.PKV_BF16, 16, 64, 1056, 4096, 2048)
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+    assert p.prefill_plan(pkv.PKV_BF16, 16, 64, 1056, 4096, 0)[1] == 1  # the automatic plan keeps one piece
+
+
 def test_kv_bytes_entry_point():
     from paged_kv_cache_62_amd import pkv
     assert pkv.pkv_kv_bytes(28, 8, 128, 8000, 4, 2) == 3_670_016_000
@@ -167,12 +210,13 @@ def test_graft_entry_build_calls_the_library_build(monkeypatch):
 
 
 @pytest.mark.parametrize("args,plan", [
-    # (q dtype, Hq, B, max_query_len, max_context_len, piece_tokens) -> (piece tokens, pieces, workspace bytes)
-    (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 4 * 512 * 16 * 2 * 130 * 4)),  # 256 workgroups of queries: split
+    # (q dtype, Hq, B, max_query_len, max_context_len, piece_tokens) -> (piece tokens, pieces, workspace bytes);
+    # the workspace holds the 64 KiB counter prefix, then the partials
+    (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 65536 + 4 * 512 * 16 * 2 * 130 * 4)),  # 256 workgroups: split
     (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0)),                         # 1024 workgroups: one piece
     (("F32", 16, 4, 512, 8000, 0), (8000, 1, 0)),                           # one tile per wavefront: 512
     (("BF16", 16, 1, 64, 900, 0), (960, 1, 0)),                              # under 1024 tokens: never cut
-    (("BF16", 16, 2, 64, 455, 64), (64, 8, 2 * 64 * 16 * 8 * 130 * 4)),      # explicit pieces
+    (("BF16", 16, 2, 64, 455, 64), (64, 8, 65536 + 2 * 64 * 16 * 8 * 130 * 4)),  # explicit pieces
     (("BF16", 16, 2, 64, 455, 512), (512, 1, 0)),
 ])
 def test_prefill_plan(args, plan):

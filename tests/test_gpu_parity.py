@@ -55,6 +55,33 @@ def test_workspace_shared_across_merge_placements(gpu, kv):
             H.assert_attention_close(out.cpu().numpy(), res["ref"][layer])
 
 
+def test_workspace_reused_with_fewer_then_more_sequences(gpu):
+    """One workspace for fused-merge calls whose batch shrinks and grows
+    again (12, 3, 12, 1, 12 sequences over 8 KV heads), as a serving loop
+    makes them: the partials of a small batch never land on the counters a
+    larger one reads, since every workspace starts with the fixed counter
+    prefix. Every call matches the oracle on its sequences."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    lens = [37, 200, 5, 120, 64, 300, 17, 90, 250, 1, 180, 75]
+    sh = H.Shape(layers=1, hq=16, hkv=8, dim=128, bs=16, nblocks=sum(-(-n // 16) for n in lens) + 4,
+                 kv_dtype=orc.I8, in_dtype="bf16", q_dtype="bf16", free_order_seed=3)
+    case = H.Case(sh, 62600, [("allocate", s, n) for s, n in enumerate(lens)], decode_seqs=list(range(len(lens))))
+    res = H.run_decode_case(case, partition_tokens=64, flags=pkv.PKV_DECODE_FUSED_MERGE)
+    pool, table, t_lens, q = res["pool"], res["table"], res["lens"], res["q"]
+    dev = pool.arena.device
+    t_table, t_lens = torch.from_numpy(table).to(dev), torch.from_numpy(t_lens).to(dev)
+    max_ctx = max(lens)
+    ws = torch.zeros(pool.workspace_bytes(len(lens), sh.hq, max_ctx, 64), dtype=torch.uint8, device=dev)
+    for n in (12, 3, 12, 1, 12):
+        print(f"decode reused workspace: {n} sequences", flush=True)
+        out = pool.decode(0, q[:n].to(dev), t_table[:n], t_lens[:n], max_ctx, sh.scale, workspace=ws,
+                          partition_tokens=64, flags=pkv.PKV_DECODE_FUSED_MERGE)
+        torch.cuda.synchronize()
+        H.assert_attention_close(out.cpu().numpy(), res["ref"][0][:n])
+        assert int(torch.count_nonzero(ws[:pkv.MERGE_COUNTER_BYTES])) == 0, f"{n} sequences: counters not reset"
+
+
 @pytest.mark.parametrize("dim", [64, 128])
 @pytest.mark.parametrize("T", [256, 128, 64, 16])
 @pytest.mark.parametrize("flags", [1, 2])

@@ -15,7 +15,7 @@ from tests import harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _prefill(case, qlens, q_dtype, piece_tokens=0, max_context_len=None):
+def _prefill(case, qlens, q_dtype, piece_tokens=0, max_context_len=None, workspace=None):
     import torch
     sh = case.shape
     pool = H.make_gpu_pool(case)
@@ -38,7 +38,7 @@ def _prefill(case, qlens, q_dtype, piece_tokens=0, max_context_len=None):
     for layer in range(sh.layers):
         out = pool.prefill(layer, q.to(dev), torch.from_numpy(qstart).to(dev), int(max(qlens)),
                            torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev), sh.scale, mctx,
-                           piece_tokens=piece_tokens)
+                           workspace=workspace, piece_tokens=piece_tokens)
         torch.cuda.synchronize()
         kc, vc, ks, vs = H.gpu_layer_arrays(pool, layer, rows.keys(), sh)
         refs.append(orc.prefill_attention(sh.dtype(layer), kc, vc, ks, vs, synth.as_f32(q), qstart, table, lens,
@@ -133,7 +133,7 @@ def test_prefill_plan_and_workspace_checks(gpu):
     c = _case(orc.I8, 8, 2, 128, 16, [300, 455], 64500)
     pool = H.make_gpu_pool(c)
     T, n, nb = pool.prefill_plan(pkv.PKV_BF16, 8, 2, 64, 455, 64)
-    assert (T, n) == (64, 8) and nb == 2 * 64 * 8 * n * (2 + 128) * 4
+    assert (T, n) == (64, 8) and nb == pkv.MERGE_COUNTER_BYTES + 2 * 64 * 8 * n * (2 + 128) * 4
     assert pool.prefill_plan(pkv.PKV_BF16, 8, 2, 64, 455, 0)[1:] == (1, 0)  # short contexts: one piece
     dev = pool.arena.device
     q = torch.zeros(128, 8, 128, dtype=torch.bfloat16, device=dev)
@@ -147,3 +147,25 @@ def test_prefill_plan_and_workspace_checks(gpu):
         pool.prefill(0, q, qs, 64, table, lens, 1.0, 455, piece_tokens=96)  # not a multiple of 64
     with pytest.raises(pkv.PkvError):
         pool.prefill(0, q, qs, 64, table, lens, 1.0, 32)  # max_context_len < max_query_len
+
+
+def test_prefill_workspace_reused(gpu):
+    """One workspace for every call: the pieces' arrival counters are back at
+    zero after each launch, so later launches of other shapes (both layers,
+    then shorter chunks with fewer tile groups) merge correctly in it."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    lens = [600, 620, 545, 700]
+    c = _case(orc.I8, 16, 8, 128, 16, lens, 64500)
+    sh = c.shape
+    big = [600, 530, 545, 580]
+    pool = H.make_gpu_pool(c)
+    _, _, nb = pool.prefill_plan(pkv.PKV_BF16, sh.hq, len(lens), max(big), max(lens), 192)
+    slots = len(lens) * max(big) * sh.hq * -(-max(lens) // 192)
+    assert nb == pkv.MERGE_COUNTER_BYTES + slots * (2 + sh.dim) * 4
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    for qlens in (big, [70, 1, 200, 33], big):
+        got, ref, ma, mr = _prefill(c, qlens, "bf16", piece_tokens=192, max_context_len=max(lens), workspace=ws)
+        print(f"prefill reused workspace qlens={qlens}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+        H.assert_attention_close(got, ref)
+        assert int(torch.count_nonzero(ws[:pkv.MERGE_COUNTER_BYTES])) == 0, "arrival counters not left at zero"
