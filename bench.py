@@ -922,7 +922,8 @@ class PrefillWorkload:
         self.out = torch.empty(B * C, hq, dim, dtype=torch.float32, device=dev)
         # the context split and its workspace, planned once (every layer's
         # launch reuses it in turn on the one stream)
-        self.piece_tokens, self.pieces, nb = self.pool.prefill_plan(pkv.PKV_BF16, hq, B, C, ctx, piece_tokens)
+        self.piece_tokens, self.pieces, nb, self.waves = self.pool.prefill_plan(pkv.PKV_BF16, hq, B, C, ctx,
+                                                                               piece_tokens, waves=True)
         self.ws = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
 
     def prefill(self, layer):
@@ -1017,7 +1018,8 @@ def run_prefill(args, stream):
         "data": "synthetic (seeded K/V and queries), cache filled before timing",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": B, "query_tokens_per_seq": C,
                    "context": ctx, "layers_per_step": L, "hip_graph": True,
-                   "context_pieces": w.pieces, "piece_tokens": w.piece_tokens if w.pieces > 1 else None},
+                   "context_pieces": w.pieces, "piece_tokens": w.piece_tokens if w.pieces > 1 else None,
+                   "wavefronts_per_workgroup": w.waves},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": measured_traffic(args.config),
                      "kernel": ("prefill_kernel (causal paged attention, fp16 matrix cores"

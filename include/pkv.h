@@ -346,13 +346,17 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
                                  float softmax_scale, int32_t piece_tokens, float* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
-/* The context split pkv_prefill_attention makes for these sizes: the piece
- * size in tokens, the number of pieces per sequence and the workspace bytes
- * it needs (0 for one piece). Output pointers may be NULL. Host only,
- * synchronous; the same argument checks as pkv_prefill_attention. */
+/* The launch plan pkv_prefill_attention follows for these sizes: the piece
+ * size in tokens, the number of pieces per sequence, the workspace bytes it
+ * needs (0 for one piece) and the wavefronts per workgroup (4; 8 when the
+ * automatic split cuts the context and the query tiles fill the larger
+ * workgroups, which then share each staged step of the context among twice
+ * the tiles). Output pointers may be NULL. Host only, synchronous; the same
+ * argument checks as pkv_prefill_attention. */
 pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
                             int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
-                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out);
+                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out,
+                            int32_t* waves_out);
 
 /* Synchronous host export of blocks of one layer in canonical order:
  * codes_out (host) [n][2 (K,V)][Hkv][bs][d] (int8 codes, or binary16 bits as

@@ -102,29 +102,39 @@ struct PrefillLaunch {
   // to finish merges them.
   int32_t pieces;
   int32_t piece_tokens;
+  int32_t waves;              // wavefronts per workgroup: kPrefillWaves or kPrefillWavesLong
   int32_t* counters;          // [num_seqs][Hkv][tile groups] arrival counters (zero between calls)
   float* ws;                  // partials m, l [num_seqs][max_query_len][Hq][pieces], then o (x head_dim)
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 
-// Wavefronts of a prefill workgroup, and the query tokens a workgroup takes
-// for planning: two 16-column tiles per wavefront (one for an fp32 query), a
-// tile being 16 / group query tokens. (A binary16 cache at head_dim 128 runs
-// one tile per wavefront; the plan does not depend on the layer.)
+// Wavefronts of a prefill workgroup, and the query tokens a four-wavefront
+// workgroup takes for planning: two 16-column tiles per wavefront (one for an
+// fp32 query), a tile being 16 / group query tokens. (A binary16 cache at
+// head_dim 128 runs one tile per wavefront; the plan does not depend on the
+// layer.) Launches whose context the automatic plan cuts into pieces run
+// eight wavefronts per workgroup instead: twice the query tiles share each
+// staged step of the context, in half as many workgroups (one per compute
+// unit at two wavefronts per SIMD); the piece count comes out the same.
 constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWavesLong = 8;
 constexpr int prefill_query_tokens_per_workgroup(int group, int q_dtype) {
   return kPrefillWaves * (q_dtype == kF32 ? 1 : 2) * (16 / group);
 }
 
 // The context split of a prefill launch: piece_tokens (0: automatic, else a
-// multiple of 64) -> the piece size used and the number of pieces. The
-// automatic split cuts the context only when the query tiles alone give
-// fewer than two workgroups per compute unit (cus of them), and keeps pieces
-// of at least 1024 tokens.
+// multiple of 64) -> the piece size used, the number of pieces and the
+// wavefronts per workgroup. The automatic split cuts the context only when
+// the query tiles alone give fewer than two four-wavefront workgroups per
+// compute unit (cus of them), and keeps pieces of at least 1024 tokens. The
+// launch runs kPrefillWavesLong wavefronts per workgroup when the automatic
+// split cuts (whatever piece_tokens is) and the four-wavefront workgroups of
+// a sequence and KV head come in an even number (so the larger ones leave no
+// more query slots idle).
 void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
                   int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
-                  int32_t* pieces_out);
+                  int32_t* pieces_out, int32_t* waves_out);
 // Query tile groups per (sequence, KV head) of any prefill launch: at most
 // this many (at least one 16 / group query-token tile per wavefront).
 constexpr int32_t prefill_tile_groups_bound(int32_t max_query_len, int32_t group) {

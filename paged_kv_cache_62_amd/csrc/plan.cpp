@@ -37,21 +37,21 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
 
 void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
                   int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
-                  int32_t* pieces_out) {
+                  int32_t* pieces_out, int32_t* waves_out) {
   constexpr int32_t kMinPiece = 1024;
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
-  int32_t t = piece_tokens;
-  if (t <= 0) {
-    const int32_t wq = prefill_query_tokens_per_workgroup(group, q_dtype);
-    const int64_t items = (int64_t)((max_query_len + wq - 1) / wq) * num_kv_heads * num_seqs;
-    const int64_t want = 2 * (int64_t)cus;
-    int64_t n = items >= want || items <= 0 ? 1 : (want + items - 1) / items;
-    n = std::min<int64_t>(n, std::max(1, ctx / kMinPiece));
-    t = (int32_t)((((int64_t)ctx + n - 1) / n + 63) / 64 * 64);
-  }
+  const int32_t wq = prefill_query_tokens_per_workgroup(group, q_dtype);
+  const int32_t groups = (max_query_len + wq - 1) / wq;  // of four-wavefront workgroups
+  const int64_t items = (int64_t)groups * num_kv_heads * num_seqs;
+  const int64_t want = 2 * (int64_t)cus;
+  int64_t na = items >= want || items <= 0 ? 1 : (want + items - 1) / items;
+  na = std::min<int64_t>(na, std::max(1, ctx / kMinPiece));
+  const int32_t t = piece_tokens > 0 ? piece_tokens : (int32_t)((((int64_t)ctx + na - 1) / na + 63) / 64 * 64);
   const int32_t n = (int32_t)(((int64_t)ctx + t - 1) / t);
   *piece_out = n > 1 ? t : std::max(t, ((ctx + 63) / 64) * 64);
   *pieces_out = n;
+  // eight wavefronts only where they leave no more query slots idle than four
+  *waves_out = na > 1 && groups % 2 == 0 ? kPrefillWavesLong : kPrefillWaves;
 }
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads, int32_t head_dim,

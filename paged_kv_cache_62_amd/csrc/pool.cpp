@@ -774,19 +774,21 @@ static pkv_status check_prefill_counters(const pkv_pool* pool, int32_t num_q_hea
 
 pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
                             int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
-                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out) {
+                            int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out,
+                            int32_t* waves_out) {
   const pkv_status st =
       prefill_check(pool, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens);
   if (st != PKV_OK) return st;
   if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d must be >= 1", num_seqs);
   const pkv_pool_config& c = pool->cfg;
-  int32_t T = 0, n = 0;
+  int32_t T = 0, n = 0, w = 0;
   pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
-                    max_context_len, piece_tokens, &T, &n);
+                    max_context_len, piece_tokens, &T, &n, &w);
   const pkv_status cst = check_prefill_counters(pool, num_q_heads, num_seqs, max_query_len, n);
   if (cst != PKV_OK) return cst;
   if (piece_tokens_out) *piece_tokens_out = T;
   if (pieces_out) *pieces_out = n;
+  if (waves_out) *waves_out = w;
   if (workspace_bytes_out)
     *workspace_bytes_out = pkv::prefill_workspace_bytes(num_seqs, max_query_len, num_q_heads, c.head_dim, n);
   return ok();
@@ -812,9 +814,9 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   if (num_seqs == 0) return ok();
   if (!q || !query_start || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID_ARG, "NULL q, query_start, block_tables, context_lens or out");
-  int32_t T = 0, n = 0;
+  int32_t T = 0, n = 0, w = 0;
   pkv::prefill_plan(pool->cus, num_seqs, c.num_kv_heads, num_q_heads / c.num_kv_heads, q_dtype, max_query_len,
-                    max_context_len, piece_tokens, &T, &n);
+                    max_context_len, piece_tokens, &T, &n, &w);
   const pkv_status cst = check_prefill_counters(pool, num_q_heads, num_seqs, max_query_len, n);
   if (cst != PKV_OK) return cst;
   const size_t need = pkv::prefill_workspace_bytes(num_seqs, max_query_len, num_q_heads, c.head_dim, n);
@@ -836,6 +838,7 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
   p.out = out;
   p.pieces = n;
   p.piece_tokens = T;
+  p.waves = w;
   if (n > 1) {
     p.counters = (int32_t*)workspace;
     p.ws = (float*)((char*)workspace + pkv::kMergeCounterBytes);

@@ -14,15 +14,18 @@ namespace {
 // sits at position p = len - q_len + i and attends to positions 0..p.
 //
 // A tile is 16 matrix-core columns = 16/G query tokens x the G query heads of
-// one KV head. A workgroup of four wavefronts takes 4 * NTW consecutive tiles
-// of one sequence and KV head, NTW per wavefront, and streams a range of that
-// head's context (the whole of what its queries see, or one piece of it)
-// through them in steps of two 16-token units (A, B). Its wavefronts read the
-// same units, so the workgroup loads each once: every thread requests the same
-// 16-byte piece of both units of a step (of K or of V, alike across its
-// wavefront, so each request is a scalar buffer descriptor and a fixed
-// per-lane offset) into registers three steps ahead, and writes the pair into
-// a three-slot LDS ring as binary16 (INT8 codes convert exactly; the block
+// one KV head. A workgroup of NW wavefronts (four; eight where the context is
+// cut into pieces, so that twice the tiles share each staged step) takes
+// NW * NTW consecutive tiles of one sequence and KV head, NTW per wavefront,
+// and streams a range of that head's context (the whole of what its queries
+// see, or one piece of it) through them in steps of two 16-token units (A, B).
+// Its wavefronts read the same units, so the workgroup loads each once: each
+// staging thread (all of them, or the first half with eight wavefronts and an
+// INT8 cache) requests the same 16-byte piece of both units of a step (of K or
+// of V, alike across its wavefront, so each request is a scalar buffer
+// descriptor and a fixed per-lane offset) into registers three steps ahead,
+// and writes the pair into a three-slot LDS ring as binary16 (INT8 codes
+// convert exactly; the block
 // scales stay factors of the scores and of P). Per step and wavefront, for
 // each of its tiles (the K and V operands read from LDS once for all of them):
 //   S^T[token][col] = K[token][:] . Q^T[:][col]   per unit (fp16 products, fp32 sums)
@@ -81,10 +84,9 @@ __device__ __forceinline__ int piece_order(int q, bool k) {
   return p;
 }
 
-template <bool I8, int D, int G, int QT, int NTW>
-__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+template <bool I8, int D, int G, int QT, int NTW, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(const PrefillLaunch a) {
-  constexpr int NW = kPrefillWaves;
   constexpr int NT = 64 * NW;               // threads
   constexpr int TQ = 16 / G;                // query tokens per tile
   constexpr int WQ = NW * NTW * TQ;         // query tokens per workgroup
@@ -635,17 +637,25 @@ void prefill_kernel(const PrefillLaunch a) {
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool I8, int D, int G, int QT, int NTW>
+template <bool I8, int D, int G, int QT, int NTW, int NW>
 hipError_t launch_prefill_t(const PrefillLaunch& p, hipStream_t stream) {
-  constexpr int WQ = kPrefillWaves * NTW * (16 / G);
+  constexpr int WQ = NW * NTW * (16 / G);
   const int64_t ngroups = (p.max_query_len + WQ - 1) / WQ;
   const int64_t nwg = ngroups * p.pieces * p.lv.num_kv_heads * p.num_seqs;
-  if (nwg * 64 * kPrefillWaves >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
+  if (nwg * 64 * NW >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;  // grid size in threads
   if (p.pieces > 1 && ngroups * p.lv.num_kv_heads * p.num_seqs > kMergeCounters)  // one counter per tile group
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<I8, D, G, QT, NTW>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, stream,
-                     p);
+  hipLaunchKernelGGL((prefill_kernel<I8, D, G, QT, NTW, NW>), dim3((unsigned)nwg), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool I8, int D, int G, int QT, int NTW>
+hipError_t launch_prefill_w(const PrefillLaunch& p, hipStream_t stream) {
+  switch (p.waves) {
+    case kPrefillWaves: return launch_prefill_t<I8, D, G, QT, NTW, kPrefillWaves>(p, stream);
+    case kPrefillWavesLong: return launch_prefill_t<I8, D, G, QT, NTW, kPrefillWavesLong>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Tiles per wavefront: two share each K and V operand read from LDS, except
@@ -655,9 +665,9 @@ template <bool I8, int D, int G>
 hipError_t launch_prefill_q(const PrefillLaunch& p, hipStream_t stream) {
   constexpr int NTW = I8 || D == 64 ? 2 : 1;
   switch (p.q_dtype) {
-    case kF32: return launch_prefill_t<I8, D, G, kF32, 1>(p, stream);
-    case kF16: return launch_prefill_t<I8, D, G, kF16, NTW>(p, stream);
-    case kBF16: return launch_prefill_t<I8, D, G, kBF16, NTW>(p, stream);
+    case kF32: return launch_prefill_w<I8, D, G, kF32, 1>(p, stream);
+    case kF16: return launch_prefill_w<I8, D, G, kF16, NTW>(p, stream);
+    case kBF16: return launch_prefill_w<I8, D, G, kBF16, NTW>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -117,7 +117,7 @@ SIGNATURES = {
     "pkv_read_tail_blocks": (C.c_int, [_vp, _i32, _vp, _i32, _vp]),
     "pkv_prefill_attention": (C.c_int, [_vp, _i32, _vp, C.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                         _f32, _i32, _vp, _vp, _sz, _vp]),
-    "pkv_prefill_plan": (C.c_int, [_vp, C.c_int, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "pkv_prefill_plan": (C.c_int, [_vp, C.c_int, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "pkv_kv_bytes": (_u64, [_u64] * 6),
     "pkv_last_error": (C.c_char_p, []),
 }
@@ -476,13 +476,15 @@ class Pool:
                                 softmax_scale, out, partition_tokens, stream, flags)
         return out
 
-    def prefill_plan(self, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens=0):
-        """(piece tokens, pieces, workspace bytes) of pkv_prefill_attention for these sizes."""
-        T, n, nb = _i32(), _i32(), _sz()
+    def prefill_plan(self, q_dtype, num_q_heads, num_seqs, max_query_len, max_context_len, piece_tokens=0,
+                     waves=False):
+        """(piece tokens, pieces, workspace bytes) of pkv_prefill_attention for these sizes,
+        and the wavefronts per workgroup as a fourth entry with waves=True."""
+        T, n, nb, w = _i32(), _i32(), _sz(), _i32()
         _check(lib().pkv_prefill_plan(self.h, int(q_dtype), int(num_q_heads), int(num_seqs), int(max_query_len),
                                       int(max_context_len), int(piece_tokens), C.byref(T), C.byref(n),
-                                      C.byref(nb)))
-        return T.value, n.value, nb.value
+                                      C.byref(nb), C.byref(w)))
+        return (T.value, n.value, nb.value, w.value) if waves else (T.value, n.value, nb.value)
 
     def prefill(self, layer, q, query_start, max_query_len, block_tables, context_lens, softmax_scale,
                 max_context_len, out=None, workspace=None, piece_tokens=0, stream=None):

@@ -210,23 +210,31 @@ def test_graft_entry_build_calls_the_library_build(monkeypatch):
 
 
 @pytest.mark.parametrize("args,plan", [
-    # (q dtype, Hq, B, max_query_len, max_context_len, piece_tokens) -> (piece tokens, pieces, workspace bytes);
+    # (q dtype, Hq, B, max_query_len, max_context_len, piece_tokens) ->
+    # (piece tokens, pieces, workspace bytes, wavefronts per workgroup);
     # the workspace holds the 64 KiB counter prefix, then the partials
-    (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 65536 + 4 * 512 * 16 * 2 * 130 * 4)),  # 256 workgroups: split
-    (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0)),                         # 1024 workgroups: one piece
-    (("F32", 16, 4, 512, 8000, 0), (8000, 1, 0)),                           # one tile per wavefront: 512
-    (("BF16", 16, 1, 64, 900, 0), (960, 1, 0)),                              # under 1024 tokens: never cut
-    (("BF16", 16, 2, 64, 455, 64), (64, 8, 65536 + 2 * 64 * 16 * 8 * 130 * 4)),  # explicit pieces
-    (("BF16", 16, 2, 64, 455, 512), (512, 1, 0)),
+    (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 65536 + 4 * 512 * 16 * 2 * 130 * 4, 8)),  # 256 workgroups: split
+    (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0, 4)),                        # 1024 workgroups: one piece
+    (("F32", 16, 4, 512, 8000, 0), (8000, 1, 0, 4)),                          # one tile per wavefront: 512
+    (("BF16", 16, 1, 64, 900, 0), (960, 1, 0, 4)),                             # under 1024 tokens: never cut
+    (("BF16", 16, 2, 64, 455, 64), (64, 8, 65536 + 2 * 64 * 16 * 8 * 130 * 4, 4)),  # explicit pieces
+    (("BF16", 16, 2, 64, 455, 512), (512, 1, 0, 4)),
+    # one tile group of 64 queries: cut into 15 pieces, four wavefronts (eight would idle half)
+    (("BF16", 16, 1, 64, 16000, 0), (1088, 15, 65536 + 64 * 16 * 15 * 130 * 4, 4)),
+    (("BF16", 16, 1, 128, 16000, 0), (1088, 15, 65536 + 128 * 16 * 15 * 130 * 4, 8)),
+    (("BF16", 16, 4, 512, 8000, 8000), (8000, 1, 0, 8)),  # the automatic plan would cut: eight wavefronts
 ])
 def test_prefill_plan(args, plan):
-    """The context split pkv_prefill_attention makes (a 256-CU planning
-    figure on a host-only pool): pieces only when the query tiles leave
-    compute units idle, never under 1024 tokens, workspace for the partials."""
+    """The launch pkv_prefill_attention makes (a 256-CU planning figure on a
+    host-only pool): pieces only when the query tiles leave compute units
+    idle, never under 1024 tokens, workspace for the partials, eight
+    wavefronts per workgroup where the automatic plan cuts and the tile
+    groups pair up."""
     from paged_kv_cache_62_amd import pkv
     p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
     qd, hq, B, mq, mctx, T = args
-    assert p.prefill_plan(getattr(pkv, "PKV_" + qd), hq, B, mq, mctx, T) == plan
+    assert p.prefill_plan(getattr(pkv, "PKV_" + qd), hq, B, mq, mctx, T, waves=True) == plan
+    assert p.prefill_plan(getattr(pkv, "PKV_" + qd), hq, B, mq, mctx, T) == plan[:3]
 
 
 def test_prefill_plan_rejects_bad_arguments():

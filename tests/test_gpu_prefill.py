@@ -169,3 +169,28 @@ def test_prefill_workspace_reused(gpu):
         print(f"prefill reused workspace qlens={qlens}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
         H.assert_attention_close(got, ref)
         assert int(torch.count_nonzero(ws[:pkv.MERGE_COUNTER_BYTES])) == 0, "arrival counters not left at zero"
+
+
+@pytest.mark.parametrize("kv,hq,hkv,dim,bs,q_dtype,lens,qlens,piece_tokens", [
+    (orc.I8, 16, 8, 128, 16, "bf16", [2100, 2600], [128, 100], 0),
+    (orc.I8, 16, 8, 128, 16, "bf16", [2100, 2600], [128, 100], 512),
+    (orc.F16, 8, 2, 64, 32, "f32", [2200, 3000], [64, 40], 0),
+    (orc.I8, 4, 4, 128, 64, "f16", [2500, 2048], [256, 200], 0),
+    (orc.F16, 16, 8, 128, 16, "bf16", [2300, 2050], [128, 70], 0),
+])
+def test_prefill_eight_wavefronts(gpu, kv, hq, hkv, dim, bs, q_dtype, lens, qlens, piece_tokens):
+    """Few query tiles over long contexts: the automatic plan cuts the
+    context, and the launch runs eight wavefronts per workgroup (twice the
+    tiles per staged step; some of them past the chunk), merged over ragged
+    piece counts. INT8 and FP16, head_dim 64 and 128, G 1/2/4, fp32, fp16
+    and bf16 queries, automatic and explicit pieces."""
+    from paged_kv_cache_62_amd import pkv
+    c = _case(kv, hq, hkv, dim, bs, lens, 64600 + hq + dim + bs + kv, in_dtype=q_dtype)
+    pool = H.make_gpu_pool(c)
+    qcode = {"f32": pkv.PKV_F32, "f16": pkv.PKV_F16, "bf16": pkv.PKV_BF16}[q_dtype]
+    T, n, _, waves = pool.prefill_plan(qcode, hq, len(lens), max(qlens), max(lens), piece_tokens, waves=True)
+    assert waves == 8 and n > 1, (T, n, waves)
+    got, ref, ma, mr = _prefill(c, qlens, q_dtype, piece_tokens)
+    print(f"prefill eight wavefronts kv={kv} hq={hq}/{hkv} d={dim} q={q_dtype} pieces {n} x {T}: "
+          f"max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+    H.assert_attention_close(got, ref)
