@@ -58,10 +58,13 @@ namespace {
 // the group's pieces (log-sum-exp) and writes the output. With one piece the
 // workgroup writes the output itself.
 //
-// Workgroups are numbered so that those of one (sequence, KV head, piece)
-// run on one XCD, whose L2 then serves that context range to all of them
-// (consecutive workgroup ids go to the eight XCDs in turn), and so that on
-// each XCD the tiles with the longest context start first.
+// Workgroups are numbered so that each XCD takes a contiguous stretch of the
+// (sequence, KV head, piece) units' tile groups (consecutive workgroup ids go
+// to the eight XCDs in turn), whose L2 then serves those context ranges to
+// all of them. With one piece it runs them longest context first across its
+// units: list scheduling in that order keeps its compute units busy to the
+// end, where unit after unit left the long tile groups of the last units to
+// run alone.
 // ---------------------------------------------------------------------------
 constexpr float kMaxFloor = -1e30f;  // running max before any visible token (finite: no inf - inf)
 
@@ -109,15 +112,34 @@ void prefill_kernel(const PrefillLaunch a) {
   const int n16 = lane & 15, gq = lane >> 4;
   const int hq = a.num_q_heads, hkv = a.lv.num_kv_heads, bs = a.lv.block_size;
 
-  // workgroup -> (pair, piece, tile group); XCD x runs ids x, x + 8, ... and
-  // takes the x-th contiguous stretch of (pair, piece)-major, longest-first
-  // order
+  // workgroup -> (pair, piece, tile group). Work item jo = unit * ngroups + r
+  // is tile group ngroups - 1 - r (r = 0 the one with the longest context) of
+  // unit (pair, piece). XCD x runs ids x, x + 8, ... and takes the x-th
+  // contiguous stretch of items, so its units' context stays in its L2. With
+  // one piece (a grid that may take several rounds) it runs them in the order
+  // r = 0, 1, ... across those units, longest first: the k-th id of the XCD
+  // is the k-th item of the stretch in that order. A context cut into pieces
+  // (planned only for grids that fit at once) runs unit after unit instead,
+  // which measured faster there.
   const int ngroups = (a.max_query_len + WQ - 1) / WQ;
   const int npc = a.pieces;
   const int nwg = gridDim.x, xcd = blockIdx.x & 7, base = nwg >> 3, rem = nwg & 7;
-  const int jo = xcd * base + min(xcd, rem) + (blockIdx.x >> 3);
-  const int pair = jo / (ngroups * npc), rr = jo % (ngroups * npc);
-  const int piece = rr / ngroups, grp = ngroups - 1 - rr % ngroups;
+  const int jstart = xcd * base + min(xcd, rem), jend = jstart + base + (xcd < rem ? 1 : 0);
+  int k = blockIdx.x >> 3, r = 0, unit = 0;
+  if (npc > 1) {
+    unit = (jstart + k) / ngroups;
+    r = (jstart + k) % ngroups;
+  } else {
+    for (; r < ngroups; ++r) {  // the units holding item r in [jstart, jend): [lo, hi)
+      const int lo = (jstart - r + ngroups - 1) / ngroups, hi = (jend - r + ngroups - 1) / ngroups;
+      if (k < hi - lo) {
+        unit = lo + k;
+        break;
+      }
+      k -= hi - lo;
+    }
+  }
+  const int pair = unit / npc, piece = unit % npc, grp = ngroups - 1 - r;
   const int g = pair % hkv, s = pair / hkv;
 
   const int lupb = __builtin_ctz(bs / kUnit);
