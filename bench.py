@@ -273,6 +273,11 @@ class Workload:
                 slots = self.pool.allocate(s, int(lens0[s]))
                 self._append_all(kv_fill, slots)
         torch.cuda.synchronize()
+        # the batch in pkv_seq_order_longest_first's order (longest context
+        # first; equal lengths keep their order): with one partition per
+        # sequence each compute unit then gets sequences from every part of
+        # the length range
+        self.seqs = self.pool.order_longest_first(self.seqs)
         # per-step inputs: one query and one new K/V row per sequence and layer
         self.q = [torch.randn(self.B, self.hq, self.dim, generator=gen, device=self.dev).to(tdt[c["q"]])
                   for _ in range(self.L)]
@@ -669,6 +674,7 @@ def run(args, stream):
                    "merge": "none (one partition)" if plan[1] == 1 else
                             "last workgroup" if plan[2] else "separate launch",
                    "hip_graph": not args.no_graph,
+                   "batch_order": "longest context first",
                    "contraction": "vector ALU (comparison)" if valu_flag else "matrix cores",
                    "launches_per_layer": 1 if w.fused else 2,
                    "kv_read_GBps_whole_step": kv_gbs_step,
@@ -737,7 +743,7 @@ class ServeWorkload:
         d = torch.from_numpy(slots).to(dev)
         for layer in range(L):
             pool.append_kv(layer, self.ksrc[: len(slots)], self.vsrc[: len(slots)], d)
-        self.sched = pkv.Scheduler(pool, mb, mml, reserve_blocks=1)
+        self.sched = pkv.Scheduler(pool, mb, mml, reserve_blocks=1, batch_order=pkv.PKV_BATCH_LONGEST_FIRST)
         suffix = np.minimum(mix_suffix_lengths(seed, R), mml - c["prefix"] - 1)
         z = synth.normal(synth.stream_seed(seed, 4343), R)
         self.eos_at = np.maximum(np.rint(np.exp(math.log(300.0) - 0.32 + 0.8 * z)), 1).astype(np.int64)
@@ -871,6 +877,7 @@ def run_serve(args, stream):
             "last_batch": {"seqs": n, "max_context_len": mctx, "partition_tokens": plan[0],
                            "partitions": plan[1]},
             "launches_per_layer": "pkv_decode_step, plus pkv_append_kv on steps that admit",
+            "batch_order": "longest context first (scheduler option)",
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,

@@ -152,6 +152,16 @@ pkv_status pkv_seq_block_table(const pkv_pool* pool, const int64_t* seqs, int32_
 /* Length in tokens of a live sequence (host). */
 pkv_status pkv_seq_length(const pkv_pool* pool, int64_t seq, int64_t* len_out);
 
+/* A decode batch in the order that spreads its work evenly over the device:
+ * seqs_out (host) [n] = seqs sorted by current length, longest first (equal
+ * lengths keep their order; seqs_out may be seqs). Consecutive workgroups of
+ * a decode launch go to different compute units, so when the whole grid is
+ * resident at once (one partition per sequence) each compute unit then gets
+ * sequences from every part of the length range instead of a random draw;
+ * results do not depend on the order. PKV_ERR_UNKNOWN_SEQ for an unknown
+ * id (seqs_out unchanged). */
+pkv_status pkv_seq_order_longest_first(const pkv_pool* pool, const int64_t* seqs, int32_t n, int64_t* seqs_out);
+
 pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out);
 
 /* Host copy of the free queue, front first (for checks). cap >= N. *n_out =
@@ -388,7 +398,14 @@ typedef struct {
                              a request that reaches it ends with PKV_EV_MAX_LENGTH */
   int32_t reserve_blocks; /* admission needs this many free blocks beyond those of the
                              prompt (>= 0; 1 leaves room for the first decode token) */
+  int32_t batch_order;    /* order of a plan's decode rows: PKV_BATCH_ADMISSION or
+                             PKV_BATCH_LONGEST_FIRST (as pkv_seq_order_longest_first,
+                             equal lengths in admission order); the step's decisions and
+                             allocations are the same either way */
 } pkv_sched_config;
+
+#define PKV_BATCH_ADMISSION 0
+#define PKV_BATCH_LONGEST_FIRST 1
 
 /* event kinds (2 and 3 as in "无 vLLM 环境下的 Paged-KV 与连续批处理调度" §3.1) */
 #define PKV_EV_ADMIT 1      /* admitted: its prompt is in this step's prefill list */
@@ -408,7 +425,7 @@ typedef struct {
 /* A step's plan. The arrays are host memory owned by the scheduler, valid
  * until the next pkv_sched_step or pkv_sched_destroy. */
 typedef struct {
-  int32_t num_seqs;             /* requests decoded this step, in admission order */
+  int32_t num_seqs;             /* requests decoded this step, in the configured batch order */
   int32_t max_blocks;           /* width of block_tables rows: ceil(max_model_len / bs) */
   int32_t max_context_len;      /* max of context_lens (0 when num_seqs is 0) */
   int32_t num_prefill;          /* requests admitted this step */

@@ -455,6 +455,23 @@ pkv_status pkv_seq_length(const pkv_pool* pool, int64_t seq, int64_t* len_out) {
   return ok();
 }
 
+pkv_status pkv_seq_order_longest_first(const pkv_pool* pool, const int64_t* seqs, int32_t n, int64_t* seqs_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0 || (n > 0 && (!seqs || !seqs_out))) return fail(PKV_ERR_INVALID_ARG, "bad arguments");
+  std::vector<std::pair<int64_t, int64_t>> by_len(n);  // (length, id), in the given order
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seqs[i]);
+    by_len[i] = {it->second.len, seqs[i]};
+  }
+  std::stable_sort(by_len.begin(), by_len.end(),
+                   [](const std::pair<int64_t, int64_t>& x, const std::pair<int64_t, int64_t>& y) {
+                     return x.first > y.first;
+                   });
+  for (int32_t i = 0; i < n; ++i) seqs_out[i] = by_len[i].second;
+  return ok();
+}
+
 pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
   if (!pool || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
   // every block is either in the free queue or referenced (conservation)

@@ -93,6 +93,8 @@ pkv_status pkv_sched_create(pkv_pool* pool, const pkv_sched_config* cfg, pkv_sch
   if (cfg->max_batch < 1 || cfg->max_model_len < 2 || cfg->reserve_blocks < 0)
     return sfail(PKV_ERR_INVALID_ARG, "max_batch %d >= 1, max_model_len %d >= 2, reserve_blocks %d >= 0",
                  cfg->max_batch, cfg->max_model_len, cfg->reserve_blocks);
+  if (cfg->batch_order != PKV_BATCH_ADMISSION && cfg->batch_order != PKV_BATCH_LONGEST_FIRST)
+    return sfail(PKV_ERR_INVALID_ARG, "batch_order %d", cfg->batch_order);
   pkv_stats ps{};
   pkv_status e = pkv_pool_stats(pool, &ps);
   if (e != PKV_OK) return e;
@@ -260,6 +262,27 @@ pkv_status pkv_sched_step(pkv_sched* s, const int64_t* eos, int32_t n_eos, pkv_s
     const pkv_status e =
         pkv_seq_block_table(s->pool, s->seqs.data(), nb, s->max_blocks, s->tables.data(), s->lens.data());
     if (e != PKV_OK) return e;
+  }
+  if (s->cfg.batch_order == PKV_BATCH_LONGEST_FIRST && nb > 1) {
+    // the rows permuted, longest context first (stable): decisions and
+    // allocations above are those of admission order
+    std::vector<int32_t> perm(nb);
+    for (int32_t i = 0; i < nb; ++i) perm[i] = i;
+    std::stable_sort(perm.begin(), perm.end(), [&](int32_t x, int32_t y) { return s->lens[x] > s->lens[y]; });
+    std::vector<int64_t> seqs(nb), slots(nb);
+    std::vector<int32_t> tables((size_t)nb * s->max_blocks), lens(nb);
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t j = perm[i];
+      seqs[i] = s->seqs[j];
+      slots[i] = s->slots[j];
+      lens[i] = s->lens[j];
+      std::copy(s->tables.begin() + (size_t)j * s->max_blocks, s->tables.begin() + (size_t)(j + 1) * s->max_blocks,
+                tables.begin() + (size_t)i * s->max_blocks);
+    }
+    s->seqs.swap(seqs);
+    s->slots.swap(slots);
+    s->tables.swap(tables);
+    s->lens.swap(lens);
   }
   std::unordered_set<int64_t> in_batch(s->seqs.begin(), s->seqs.end());
   for (Request& r : s->running) {

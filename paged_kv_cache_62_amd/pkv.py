@@ -38,6 +38,7 @@ PKV_DECODE_SEPARATE_MERGE = 1
 PKV_DECODE_FUSED_MERGE = 2
 PKV_DECODE_VALU_CONTRACTION = 4  # comparison variant: both contractions on the vector ALUs
 MERGE_COUNTER_BYTES = 65536  # PKV_MERGE_COUNTER_BYTES: the arrival-counter prefix of every workspace
+PKV_BATCH_ADMISSION, PKV_BATCH_LONGEST_FIRST = 0, 1
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _u64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float, C.c_void_p
@@ -61,7 +62,7 @@ PKV_EV_ADMIT, PKV_EV_EOS, PKV_EV_MAX_LENGTH, PKV_EV_PREEMPT, PKV_EV_WAIT = 1, 2,
 
 
 class pkv_sched_config(C.Structure):
-    _fields_ = [("max_batch", _i32), ("max_model_len", _i32), ("reserve_blocks", _i32)]
+    _fields_ = [("max_batch", _i32), ("max_model_len", _i32), ("reserve_blocks", _i32), ("batch_order", _i32)]
 
 
 class pkv_event(C.Structure):
@@ -95,6 +96,7 @@ SIGNATURES = {
     "pkv_seq_free": (C.c_int, [_vp, _i64]),
     "pkv_seq_block_table": (C.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pkv_seq_length": (C.c_int, [_vp, _i64, _vp]),
+    "pkv_seq_order_longest_first": (C.c_int, [_vp, _vp, _i32, _vp]),
     "pkv_pool_stats": (C.c_int, [_vp, _vp]),
     "pkv_pool_free_queue": (C.c_int, [_vp, _vp, _i32, _vp]),
     "pkv_append_kv": (C.c_int, [_vp, _i32, _vp, _vp, C.c_int, _vp, _i32, _vp]),
@@ -232,6 +234,14 @@ def pkv_seq_length(h, seq: int) -> int:
     out = C.c_int64()
     _check(lib().pkv_seq_length(h, seq, C.byref(out)))
     return int(out.value)
+
+
+def pkv_seq_order_longest_first(h, seqs) -> np.ndarray:
+    """The sequence ids sorted by current length, longest first (stable)."""
+    seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+    out = np.empty_like(seqs)
+    _check(lib().pkv_seq_order_longest_first(h, _np_ptr(seqs), len(seqs), _np_ptr(out)))
+    return out
 
 
 def pkv_pool_stats(h) -> dict:
@@ -423,6 +433,9 @@ class Pool:
     def length(self, seq):
         return pkv_seq_length(self.h, seq)
 
+    def order_longest_first(self, seqs):
+        return pkv_seq_order_longest_first(self.h, seqs)
+
     def stats(self):
         return pkv_pool_stats(self.h)
 
@@ -535,9 +548,10 @@ class Scheduler:
     """Continuous-batching step scheduler over a Pool (pkv_sched_* in
     include/pkv.h). step() returns the plan as numpy copies."""
 
-    def __init__(self, pool: Pool, max_batch: int, max_model_len: int, reserve_blocks: int = 1):
+    def __init__(self, pool: Pool, max_batch: int, max_model_len: int, reserve_blocks: int = 1,
+                 batch_order: int = 0):
         self.pool = pool
-        cfg = pkv_sched_config(max_batch, max_model_len, reserve_blocks)
+        cfg = pkv_sched_config(max_batch, max_model_len, reserve_blocks, batch_order)
         h = _vp()
         _check(lib().pkv_sched_create(pool.h, C.byref(cfg), C.byref(h)))
         self.h = h

@@ -145,6 +145,51 @@ def test_random_scripts_match_the_oracle(seed):
         prev = a
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_longest_first_batch_order_permutes_rows_only(seed):
+    """batch_order = PKV_BATCH_LONGEST_FIRST: every step's decode rows (ids,
+    new-token slots, tables, lengths) are those of admission order sorted by
+    context length, longest first, equal lengths in admission order; the
+    events, the admitted prompts and the pool (free queue, counts) are the
+    same as with admission order, step after step."""
+    rng = np.random.default_rng(62900 + seed)
+    bs = [16, 32][seed % 2]
+    max_model_len = int(rng.integers(4, 9)) * bs
+    nblocks = max_model_len // bs + 4 + int(rng.integers(0, 16))
+    max_batch = int(rng.integers(2, 9))
+    order = synth.permutation(synth.stream_seed(seed, 1), nblocks)
+    pools = [pkv.Pool(1, 2, 64, bs, nblocks, pkv.PKV_I8, initial_free_order=order, host_only=True)
+             for _ in range(2)]
+    fifo = pkv.Scheduler(pools[0], max_batch, max_model_len, 1)
+    longest = pkv.Scheduler(pools[1], max_batch, max_model_len, 1, batch_order=pkv.PKV_BATCH_LONGEST_FIRST)
+    next_id, prev, reordered = 0, None, 0
+    for step in range(150):
+        for _ in range(int(rng.poisson(0.6))):
+            prompt, max_new = int(rng.integers(1, max_model_len)), int(rng.integers(1, 4 * bs))
+            fifo.submit(next_id, prompt, max_new)
+            longest.submit(next_id, prompt, max_new)
+            next_id += 1
+        eos = [int(s) for s in prev["seqs"] if rng.random() < 0.03] if prev is not None else []
+        a, b = fifo.step(eos), longest.step(eos)
+        perm = sorted(range(len(a["seqs"])), key=lambda i: (-int(a["context_lens"][i]), i))
+        for k in ("seqs", "slots", "block_tables", "context_lens"):
+            np.testing.assert_array_equal(b[k], a[k][perm], err_msg=f"{k} at step {step}")
+        for k in ("prefill_seqs", "prefill_first", "prefill_tokens", "prefill_slots"):
+            np.testing.assert_array_equal(b[k], a[k], err_msg=f"{k} at step {step}")
+        assert a["events"] == b["events"] and a["max_context_len"] == b["max_context_len"]
+        assert fifo.stats() == longest.stats()
+        assert pools[0].free_queue().tolist() == pools[1].free_queue().tolist()
+        reordered += perm != sorted(perm)
+        prev = a
+    assert reordered > 0, "no step had rows to reorder"
+
+
+def test_batch_order_must_be_known():
+    pool = pkv.Pool(1, 2, 64, 16, 8, pkv.PKV_I8, host_only=True)
+    with pytest.raises(pkv.PkvError):
+        pkv.Scheduler(pool, 2, 64, 1, batch_order=2)
+
+
 @pytest.mark.parametrize("side", sorted(SIDES))
 def test_b_finishes_c_joins_a_continues(side):
     """"无 vLLM 环境下的 Paged-KV 与连续批处理调度" §3.1: with no room for C while A and
