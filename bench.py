@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # the hash they record.
 TRAFFIC_PROFILES = {"qwen": "profiles/decode_kernel_qwen3_tts_int8.md",
                     "llama29": "profiles/decode_kernel_llama2_7b_29x4096_fp16.md",
+                    "llama128": "profiles/decode_kernel_llama2_7b_128x1024_fp16.md",
                     "mix16": "profiles/decode_kernel_mix_bs16_int8.md",
                     "long_i8": "profiles/decode_kernel_long_context_int8.md",
                     "prefill512": "profiles/prefill_kernel_qwen3_tts_chunk512_int8.md",
