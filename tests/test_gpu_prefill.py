@@ -194,3 +194,27 @@ def test_prefill_eight_wavefronts(gpu, kv, hq, hkv, dim, bs, q_dtype, lens, qlen
     print(f"prefill eight wavefronts kv={kv} hq={hq}/{hkv} d={dim} q={q_dtype} pieces {n} x {T}: "
           f"max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
     H.assert_attention_close(got, ref)
+
+
+def test_prefill_workspace_shared_by_four_and_eight_wavefront_launches(gpu):
+    """One workspace for launches whose arrival counters are laid out
+    differently (an eight-wavefront launch over long contexts, then a
+    four-wavefront launch cut into explicit pieces, then the first again):
+    each leaves the counter prefix at zero and matches the oracle."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    long_case = _case(orc.I8, 16, 8, 128, 16, [2100, 2600], 64700)
+    short_case = _case(orc.I8, 16, 8, 128, 16, [600, 620, 545, 700], 64701)
+    pool = H.make_gpu_pool(long_case)
+    assert pool.prefill_plan(pkv.PKV_BF16, 16, 2, 128, 2600, 0, waves=True)[3] == 8
+    assert pool.prefill_plan(pkv.PKV_BF16, 16, 4, 600, 700, 192, waves=True)[3] == 4
+    nb = max(pool.prefill_plan(pkv.PKV_BF16, 16, 2, 128, 2600, 0)[2],
+             pool.prefill_plan(pkv.PKV_BF16, 16, 4, 600, 700, 192)[2])
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    for case, qlens, T in ((long_case, [128, 100], 0), (short_case, [600, 530, 545, 580], 192),
+                           (long_case, [128, 100], 0)):
+        got, ref, ma, mr = _prefill(case, qlens, "bf16", piece_tokens=T, workspace=ws)
+        print(f"prefill shared workspace qlens={qlens} pieces of {T}: max_abs={ma:.3e} max_rel={mr:.3e}",
+              flush=True)
+        H.assert_attention_close(got, ref)
+        assert int(torch.count_nonzero(ws[:pkv.MERGE_COUNTER_BYTES])) == 0, "arrival counters not left at zero"
