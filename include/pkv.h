@@ -359,10 +359,11 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, const void* q, p
 /* The launch plan pkv_prefill_attention follows for these sizes: the piece
  * size in tokens, the number of pieces per sequence, the workspace bytes it
  * needs (0 for one piece) and the wavefronts per workgroup (4; 8 when the
- * automatic split cuts the context and the query tiles fill the larger
- * workgroups, which then share each staged step of the context among twice
- * the tiles). Output pointers may be NULL. Host only, synchronous; the same
- * argument checks as pkv_prefill_attention. */
+ * query tiles fill the larger workgroups and either the automatic split cuts
+ * the context or four-wavefront workgroups would take two or more rounds of
+ * the device: the larger workgroups share each staged step of the context
+ * among twice the tiles). Output pointers may be NULL. Host only,
+ * synchronous; the same argument checks as pkv_prefill_attention. */
 pkv_status pkv_prefill_plan(const pkv_pool* pool, pkv_dtype q_dtype, int32_t num_q_heads, int32_t num_seqs,
                             int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens,
                             int32_t* piece_tokens_out, int32_t* pieces_out, size_t* workspace_bytes_out,

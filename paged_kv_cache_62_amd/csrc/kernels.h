@@ -113,10 +113,12 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 // workgroup takes for planning: two 16-column tiles per wavefront (one for an
 // fp32 query), a tile being 16 / group query tokens. (A binary16 cache at
 // head_dim 128 runs one tile per wavefront; the plan does not depend on the
-// layer.) Launches whose context the automatic plan cuts into pieces run
-// eight wavefronts per workgroup instead: twice the query tiles share each
-// staged step of the context, in half as many workgroups (one per compute
-// unit at two wavefronts per SIMD); the piece count comes out the same.
+// layer.) Launches whose context the automatic plan cuts into pieces, or
+// whose four-wavefront grid would take two or more rounds (at two workgroups
+// per compute unit), run eight wavefronts per workgroup instead: twice the
+// query tiles share each staged step of the context, in half as many
+// workgroups (one per compute unit at two wavefronts per SIMD); the piece
+// count comes out the same.
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillWavesLong = 8;
 constexpr int prefill_query_tokens_per_workgroup(int group, int q_dtype) {
@@ -128,10 +130,11 @@ constexpr int prefill_query_tokens_per_workgroup(int group, int q_dtype) {
 // wavefronts per workgroup. The automatic split cuts the context only when
 // the query tiles alone give fewer than two four-wavefront workgroups per
 // compute unit (cus of them), and keeps pieces of at least 1024 tokens. The
-// launch runs kPrefillWavesLong wavefronts per workgroup when the automatic
-// split cuts (whatever piece_tokens is) and the four-wavefront workgroups of
-// a sequence and KV head come in an even number (so the larger ones leave no
-// more query slots idle).
+// launch runs kPrefillWavesLong wavefronts per workgroup when the
+// four-wavefront workgroups of a sequence and KV head come in an even number
+// (so the larger ones leave no more query slots idle) and either the
+// automatic split cuts (whatever piece_tokens is) or those workgroups make
+// two or more rounds of two per compute unit.
 void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t group, int q_dtype,
                   int32_t max_query_len, int32_t max_context_len, int32_t piece_tokens, int32_t* piece_out,
                   int32_t* pieces_out, int32_t* waves_out);

@@ -50,8 +50,11 @@ void prefill_plan(int32_t cus, int32_t num_seqs, int32_t num_kv_heads, int32_t g
   const int32_t n = (int32_t)(((int64_t)ctx + t - 1) / t);
   *piece_out = n > 1 ? t : std::max(t, ((ctx + 63) / 64) * 64);
   *pieces_out = n;
-  // eight wavefronts only where they leave no more query slots idle than four
-  *waves_out = na > 1 && groups % 2 == 0 ? kPrefillWavesLong : kPrefillWaves;
+  // eight wavefronts only where they leave no more query slots idle than four,
+  // and where their grid still has a workgroup for every compute unit
+  // through its rounds: a cut context, or two or more rounds of four
+  const bool many = items >= 4 * (int64_t)cus;
+  *waves_out = groups % 2 == 0 && (na > 1 || many) ? kPrefillWavesLong : kPrefillWaves;
 }
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads, int32_t head_dim,

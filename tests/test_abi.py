@@ -214,8 +214,10 @@ def test_graft_entry_build_calls_the_library_build(monkeypatch):
     # (piece tokens, pieces, workspace bytes, wavefronts per workgroup);
     # the workspace holds the 64 KiB counter prefix, then the partials
     (("BF16", 16, 4, 512, 8000, 0), (4032, 2, 65536 + 4 * 512 * 16 * 2 * 130 * 4, 8)),  # 256 workgroups: split
-    (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0, 4)),                        # 1024 workgroups: one piece
+    (("BF16", 16, 4, 2048, 2048, 0), (2048, 1, 0, 8)),   # 1024 workgroups, two rounds: one piece, eight waves
+    (("BF16", 16, 2, 2048, 2048, 0), (2048, 1, 0, 4)),   # 512 workgroups, one round: four waves
     (("F32", 16, 4, 512, 8000, 0), (8000, 1, 0, 4)),                          # one tile per wavefront: 512
+    (("F32", 16, 4, 2048, 2048, 0), (2048, 1, 0, 8)),                         # 2048 of them
     (("BF16", 16, 1, 64, 900, 0), (960, 1, 0, 4)),                             # under 1024 tokens: never cut
     (("BF16", 16, 2, 64, 455, 64), (64, 8, 65536 + 2 * 64 * 16 * 8 * 130 * 4, 4)),  # explicit pieces
     (("BF16", 16, 2, 64, 455, 512), (512, 1, 0, 4)),
@@ -228,8 +230,8 @@ def test_prefill_plan(args, plan):
     """The launch pkv_prefill_attention makes (a 256-CU planning figure on a
     host-only pool): pieces only when the query tiles leave compute units
     idle, never under 1024 tokens, workspace for the partials, eight
-    wavefronts per workgroup where the automatic plan cuts and the tile
-    groups pair up."""
+    wavefronts per workgroup where the tile groups pair up and the automatic
+    plan cuts or they make two or more rounds."""
     from paged_kv_cache_62_amd import pkv
     p = pkv.Pool(1, 8, 128, 16, 64, pkv.PKV_I8, host_only=True)
     qd, hq, B, mq, mctx, T = args

@@ -218,3 +218,20 @@ def test_prefill_workspace_shared_by_four_and_eight_wavefront_launches(gpu):
               flush=True)
         H.assert_attention_close(got, ref)
         assert int(torch.count_nonzero(ws[:pkv.MERGE_COUNTER_BYTES])) == 0, "arrival counters not left at zero"
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_prefill_eight_wavefronts_over_rounds(gpu, ragged):
+    """Whole prompts whose four-wavefront grid would take two rounds: the
+    plan runs eight wavefronts per workgroup with one piece (G = 4 so that
+    eight 512-token prompts reach that size; ragged lengths leave some
+    workgroups' second half past the chunk)."""
+    from paged_kv_cache_62_amd import pkv
+    lens = [512 - (37 * i) % 200 if ragged else 512 for i in range(8)]
+    c = _case(orc.I8, 32, 8, 64, 16, lens, 64800 + int(ragged))
+    pool = H.make_gpu_pool(c)
+    plan = pool.prefill_plan(pkv.PKV_BF16, 32, 8, max(lens), max(lens), 0, waves=True)
+    assert plan[1] == 1 and plan[3] == 8, plan
+    got, ref, ma, mr = _prefill(c, lens, "bf16")
+    print(f"prefill eight wavefronts over rounds ragged={ragged}: max_abs={ma:.3e} max_rel={mr:.3e}", flush=True)
+    H.assert_attention_close(got, ref)
