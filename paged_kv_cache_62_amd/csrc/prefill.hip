@@ -395,7 +395,13 @@ void prefill_kernel(const PrefillLaunch a) {
       sc[t] = sa[t];
       sd[t] = sb[t];
     }
-    qk(nslot, sa, sb);  // first, so that the matrix cores work through what follows
+    // first, so that the matrix cores work through what follows; at raised
+    // priority, so that the other wavefront of the SIMD, at its exponentials,
+    // does not hold back their issue (s_setprio around the PV products
+    // instead measured slower)
+    __builtin_amdgcn_s_setprio(1);
+    qk(nslot, sa, sb);
+    __builtin_amdgcn_s_setprio(0);
     const int evn = I8 ? max(ev, esv[slot]) : ev;
     // some column does not see the whole step (wave-uniform; the first tile
     // has the earliest queries, so it decides for all)
