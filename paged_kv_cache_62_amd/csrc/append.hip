@@ -59,22 +59,23 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
 }
 
 // ---------------------------------------------------------------------------
-// H1 (int8 cache): one wavefront per (run, head, K|V), where a run is the
-// maximal group of consecutive tokens that land in one block. Only the
-// wavefront of a run's first token works, so every (block, head, K|V) tile
-// has a single writer and no atomics are needed.
+// H1 (int8 cache): a run is the maximal group of consecutive tokens that
+// land in one block. Workgroups of (window of 64 tokens, split, K|V, head)
+// find the runs that start in their window and deal them to their
+// wavefronts; a wavefront appends each of its runs alone. Every
+// (block, head, K|V) tile has a single writer, so no atomics are needed.
 // ---------------------------------------------------------------------------
 
 // One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
 // head h, K (kv 0) or V (kv 1), at rows row0 .. row0+nr-1 of block blk:
 // grow-only scale, old rows re-encoded when it grows (P5 section 3 plus the
-// rule for partly filled blocks). issue() sends every load without waiting
-// (the block's old codes, rows < row0, 16 bytes per load; its scale; up to
-// kPre new values per lane), so a wavefront can have the K and the V append
-// in flight together; finish() does the rest and returns the new scale.
-// Old rows of a K tile are its first row0*D bytes; those of a V tile lie in
-// its first ceil(row0/16) 16-token sub-tiles, where each byte's token is
-// decoded from its offset.
+// rule for partly filled blocks). issue() sends its loads without waiting
+// (the block's scale and the largest |code| of its old rows; up to kPre new
+// values per lane), so a wavefront can have two appends in flight;
+// finish() does the rest and returns the new scale. The old codes are read,
+// 16 bytes per load, only when the max grows. Old rows of a K tile are its
+// first row0*D bytes; those of a V tile lie in its first ceil(row0/16)
+// 16-token sub-tiles, where each byte's token is decoded from its offset.
 template <int IN>
 struct I8Append {
   static constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
@@ -87,8 +88,8 @@ struct I8Append {
   float* sp;
   int32_t* qp;
   int old_bytes;
-  uint4 oc[kMaxChunks];
   float s_old;
+  int q_old;
   float pre[kPre];
 
   __device__ __forceinline__ void issue(const LayerView& lv_, int kv_, int h_, int64_t blk, int row0_, int nr_,
@@ -100,12 +101,8 @@ struct I8Append {
     sp = (kv ? lv_.v_scales : lv_.k_scales) + (size_t)blk * hkv + h;
     qp = (kv ? lv_.v_qmax : lv_.k_qmax) + (size_t)blk * hkv + h;
     old_bytes = kv ? ((row0 + 15) >> 4) * 16 * D : row0 * D;  // <= 63*128 = 504 chunks
-#pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) {
-      const int c = lane + 64 * k;
-      oc[k] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
     s_old = row0 > 0 ? *sp : 1.f;
+    q_old = row0 > 0 ? *qp : 0;
     if (nr * D <= 64 * kPre) {
 #pragma unroll
       for (int k = 0; k < kPre; ++k) {
@@ -138,18 +135,6 @@ struct I8Append {
       return load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1)));
     };
     const bool held = nr * D <= 64 * kPre;
-    int qm = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) {
-      const uint32_t wm = word_mask(k);
-      const uint32_t ws[4] = {oc[k].x, oc[k].y, oc[k].z, oc[k].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = (ws[w] ^ bias4) & wm;  // signed codes; other rows read as 0
-#pragma unroll
-        for (int b = 0; b < 4; ++b) qm = max(qm, abs((int)(int8_t)(x >> (8 * b))));
-      }
-    }
     float mx = 0.f;
     if (held) {
 #pragma unroll
@@ -164,16 +149,23 @@ struct I8Append {
     if (row0 == 0) {
       sc = scale_of(mx);
     } else {
-      qm = wave_max_int(qm);
-      const float m_old = (float)qm * s_old;
+      // the old rows' largest |code| is kept beside the scale, so the old
+      // codes are read only when the max grows
+      const float m_old = (float)q_old * s_old;
       if (mx <= m_old) {
         sc = s_old;
-        qold = qm;
+        qold = q_old;
       } else {
-        // the max grew: re-encode the old codes from their dequantised values,
-        // in the registers they were read into, and store whole chunks back
-        // (bytes of rows >= row0 are written back unchanged)
+        // the max grew: re-encode the old codes from their dequantised values
+        // and store whole chunks back (bytes of rows >= row0 are written back
+        // unchanged)
         sc = scale_of(mx);
+        uint4 oc[kMaxChunks];
+#pragma unroll
+        for (int k = 0; k < kMaxChunks; ++k) {
+          const int c = lane + 64 * k;
+          oc[k] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int k = 0; k < kMaxChunks; ++k) {
           const int c = lane + 64 * k;
@@ -225,40 +217,333 @@ struct I8Append {
   }
 };
 
+// A run that starts at row 0 and fills whole 16-token sub-tiles (a prompt's
+// full blocks, and its last block's whole sub-tiles) has no old rows: one
+// wavefront reads its nr x D values with 16-byte loads, a row's chunks in
+// consecutive lanes, keeping the first four loads per lane in registers for
+// the encode pass (runs of up to 16 x 128 bf16 values fit; longer ones are
+// read again from L2). Scale max|x| / 127 and codes as in I8Append. K codes go
+// straight to their row-major place; V codes are gathered in the wavefront's
+// LDS stage in tile order and stored as 16-byte chunks. src must be 16-byte
+// aligned.
+constexpr int kStageBytes = 64 * 128;  // the largest tile: bs 64 x d 128 codes
+
+template <int IN>
+__device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int h, int64_t blk, int nr,
+                                                const void* src, int64_t i, uint8_t* stage) {
+  constexpr int EPV = IN == kF32 ? 4 : 8;  // elements per 16-byte load
+  constexpr int G = 4;                     // loads per lane in flight
+  const int lane = threadIdx.x & 63;
+  const int hkv = lv.num_kv_heads, D = lv.head_dim, ld = __builtin_ctz(D);
+  const int per = (nr * D / EPV) >> 6;  // loads per lane: nr*D is a multiple of 1024
+  auto addr = [&](int q) {  // vector q of the run: row (q*EPV) / D, dims (q*EPV) % D ..
+    const int e = q * EPV;
+    return (const uint4*)src + ((((size_t)(i + (e >> ld)) * hkv + h) << ld) + (e & (D - 1))) / EPV;
+  };
+  auto unpack = [&](const uint4& r, float* x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (IN == kF32) {
+        x[j] = __uint_as_float(w[j]);
+      } else if constexpr (IN == kF16) {
+        x[2 * j] = f16_to_f32(w[j] & 0xFFFFu);
+        x[2 * j + 1] = f16_to_f32(w[j] >> 16);
+      } else {
+        x[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+        x[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+      }
+    }
+  };
+  auto absmax = [&](const uint4& r, float m) {
+    float x[EPV];
+    unpack(r, x);
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) m = fmaxf(m, fabsf(x[j]));
+    return m;
+  };
+  uint4 r0[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) r0[u] = u < per ? *addr(u * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+  float mx = 0.f;
+  for (int g = G; g < per; g += G) {
+    uint4 r[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) r[u] = g + u < per ? *addr((g + u) * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < G; ++u) mx = absmax(r[u], mx);
+  }
+#pragma unroll
+  for (int u = 0; u < G; ++u) mx = absmax(r0[u], mx);  // zero padding leaves the max unchanged
+  const float sc = uniform_f(scale_of(wave_max(mx)));
+
+  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * lv.block_size * D;
+  int qm = 0;
+  if (kv) {  // the stage may still be read by this wavefront's previous run
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  auto encode_vec = [&](const uint4& r, int q) {
+    float x[EPV];
+    unpack(r, x);
+    const int e = q * EPV, t = e >> ld, d0 = e & (D - 1);
+    uint32_t w[EPV / 4] = {};
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      const int8_t c = encode(x[j], sc);
+      qm = max(qm, abs((int)c));
+      if (kv) {
+        // V byte (t, d0 + j): consecutive dims are d/4 bytes apart in a lane slice
+        stage[v_tile_offset(t, d0, D) + j * (D >> 2)] = (uint8_t)(c ^ (int8_t)0x80);
+      } else {
+        w[j >> 2] |= (uint32_t)(uint8_t)c << (8 * (j & 3));
+      }
+    }
+    if (!kv) {
+      if constexpr (EPV == 8) *(uint2*)(tile + k_tile_offset(t, d0, D)) = make_uint2(w[0], w[1]);
+      else *(uint32_t*)(tile + k_tile_offset(t, d0, D)) = w[0];
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < G; ++u)
+    if (u < per) encode_vec(r0[u], u * 64 + lane);
+  for (int g = G; g < per; g += G) {
+    uint4 r[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) r[u] = g + u < per ? *addr((g + u) * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (g + u < per) encode_vec(r[u], (g + u) * 64 + lane);
+  }
+  if (kv) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int c = lane; c < (nr * D) >> 4; c += 64) *(uint4*)(tile + 16 * c) = *(const uint4*)(stage + 16 * c);
+  }
+  qm = wave_max_int(qm);
+  if (lane == 0) {
+    (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
+    (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
+  }
+}
+
+// The runs of a call -- maximal groups of consecutive tokens whose slots lie
+// in one block -- that start among tokens [base, base + 64), each as its
+// first token i, its block, first row and length. The window's positions are
+// dealt in equal stretches to the 4 * splits wavefronts of its `splits`
+// workgroups (wavefront w of split s takes stretch 4 s + w), and a wavefront
+// appends the runs that start in its stretch: one run per 16 positions for a
+// prompt in 16-token blocks, four single-token runs per wavefront when
+// splits is 4. A token whose slot is not in the pool starts no run; a run
+// stops at the end of its block and is at most 64 tokens long (the slots of
+// base .. base + 127 cover every run that starts in the window).
+constexpr int64_t kAppendGroups = 512;      // workgroups a launch aims for before splitting stops
+constexpr int64_t kAppendMaxGrid = 1 << 22;  // workgroups per launch (grids stay far below 2^32 threads)
+
+struct Run {
+  int64_t i, blk;
+  int row0, nr;
+};
+
+struct WindowRuns {
+  int64_t sa, sb, base;
+  int lbs, bs;
+  uint64_t mine;  // window positions that start this wavefront's runs
+
+  __device__ __forceinline__ void init(const LayerView& lv, const int64_t* slots, int32_t n, int64_t base_,
+                                       int split, int splits) {
+    const int lane = threadIdx.x & 63;
+    const int wave = split * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // of 4 * splits
+    const int ways = 4 * splits;
+    base = base_;
+    bs = lv.block_size;
+    lbs = __builtin_ctz(bs);  // block sizes are powers of two
+    sa = base + lane < n ? slots[base + lane] : -1;
+    sb = base + 64 + lane < n ? slots[base + 64 + lane] : -1;
+    const int64_t sprev = base > 0 ? slots[base - 1] : -1;
+    // lane j: the slot of the token before base + j
+    const int64_t up = ((int64_t)__shfl_up((int)(sa >> 32), 1) << 32) | (uint32_t)__shfl_up((int)sa, 1);
+    const int64_t pa = lane == 0 ? sprev : up;
+    const bool in_pool = sa >= 0 && (sa >> lbs) < lv.num_blocks;
+    const uint64_t starts = __ballot(in_pool && (base + lane == 0 || (pa >> lbs) != (sa >> lbs)));
+    const int per = 64 / ways;  // window positions per wavefront (ways is a power of two)
+    mine = starts & (((uint64_t(1) << per) - 1) << (wave * per));  // per <= 16
+  }
+
+  // The next of this wavefront's runs, in token order; false when none is left.
+  __device__ __forceinline__ bool next(Run& run) {
+    if (mine == 0) return false;
+    const int j = __builtin_ctzll(mine);
+    mine &= mine - 1;
+    const int64_t slot0 = ((int64_t)__builtin_amdgcn_readlane((int)(sa >> 32), j) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)sa, j);
+    const int64_t blk = slot0 >> lbs;
+    // tokens base + j, base + j + 1, ... while their slots stay in blk
+    const uint64_t ma = __ballot(sa >= 0 && (sa >> lbs) == blk);
+    const uint64_t mb = __ballot(sb >= 0 && (sb >> lbs) == blk);
+    const uint64_t from = j == 0 ? ma : (ma >> j) | (mb << (64 - j));
+    const int len = ~from == 0 ? 64 : __builtin_ctzll(~from);
+    run.i = base + j;
+    run.blk = blk;
+    run.row0 = (int)(slot0 & (bs - 1));
+    run.nr = min(len, bs - run.row0);  // rows stay inside the tile even for malformed slots
+    return true;
+  }
+};
+
+// Maximum over each 16-lane row of the wavefront, in every lane of the row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kHalfMirror>(x));
+  return fmaxf(x, dpp_f<kMirror>(x));
+}
+__device__ __forceinline__ int row16_max_int(int x) {  // x >= 0
+  x = max(x, dpp_i<kQuadXor1>(x));
+  x = max(x, dpp_i<kQuadXor2>(x));
+  x = max(x, dpp_i<kHalfMirror>(x));
+  return max(x, dpp_i<kMirror>(x));
+}
+
+// Up to four single-token runs q0 .. q{cnt-1} at once (a decode step's new
+// tokens), one per 16-lane row of the wavefront: each lane holds d/16 values
+// of its run's row. The rule is I8Append's; a run whose max grows past the
+// block's old max (which needs its old codes re-encoded) is not written here:
+// its bit is set in the returned mask and I8Append does it whole.
+template <int IN>
+__device__ __forceinline__ unsigned append_i8_rows(const LayerView& lv, int kv, int h, const Run& q0, const Run& q1,
+                                                   const Run& q2, const Run& q3, int cnt, const void* src) {
+  constexpr int kMaxE = 8;  // d / 16 for d <= 128
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  const int hkv = lv.num_kv_heads, D = lv.head_dim, E = D >> 4;
+  const int64_t i = g == 0 ? q0.i : g == 1 ? q1.i : g == 2 ? q2.i : q3.i;
+  const int64_t blk = g == 0 ? q0.blk : g == 1 ? q1.blk : g == 2 ? q2.blk : q3.blk;
+  const int row0 = g == 0 ? q0.row0 : g == 1 ? q1.row0 : g == 2 ? q2.row0 : q3.row0;
+  const bool act = g < cnt;
+  const size_t at = (size_t)blk * hkv + h;
+  float* sp = (kv ? lv.v_scales : lv.k_scales) + at;
+  int32_t* qp = (kv ? lv.v_qmax : lv.k_qmax) + at;
+  const float s_old = act && row0 > 0 ? *sp : 1.f;
+  const int q_old = act && row0 > 0 ? *qp : 0;
+  const int d0 = (lane & 15) * E;
+  float x[kMaxE];
+#pragma unroll
+  for (int e = 0; e < kMaxE; ++e)
+    x[e] = act && e < E ? load_elem<IN>(src, ((size_t)i * hkv + h) * D + d0 + e) : 0.f;
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < kMaxE; ++e) mx = fmaxf(mx, fabsf(x[e]));
+  mx = row16_max(mx);
+  const bool grow = act && row0 > 0 && mx > (float)q_old * s_old;
+  const uint64_t gb = __ballot(grow);
+  const unsigned grows = (unsigned)((gb & 1u) | ((gb >> 15) & 2u) | ((gb >> 30) & 4u) | ((gb >> 45) & 8u));
+  if (act && !grow) {
+    const float sc = row0 == 0 ? scale_of(mx) : s_old;
+    int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + at * lv.block_size * D;
+    uint32_t w[kMaxE / 4] = {};
+    int qn = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxE; ++e) {
+      if (e < E) {
+        const int8_t c = encode(x[e], sc);
+        qn = max(qn, abs((int)c));
+        if (kv) {
+          // V byte (row0, d0 + e): consecutive dims are d/4 bytes apart in a lane slice
+          tile[v_tile_offset(row0, d0, D) + e * (D >> 2)] = (int8_t)(c ^ (int8_t)0x80);
+        } else {
+          w[e >> 2] |= (uint32_t)(uint8_t)c << (8 * (e & 3));
+        }
+      }
+    }
+    if (!kv) {
+      if (E == 8) *(uint2*)(tile + k_tile_offset(row0, d0, D)) = make_uint2(w[0], w[1]);
+      else *(uint32_t*)(tile + k_tile_offset(row0, d0, D)) = w[0];
+    }
+    qn = row16_max_int(qn);
+    if ((lane & 15) == 0) {
+      *sp = sc;
+      *qp = row0 == 0 ? qn : max(q_old, qn);
+    }
+  }
+  return grows;
+}
+
 template <int IN>
 __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, const void* k,
                                                         const void* v, const int64_t* slots,
-                                                        int32_t n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                                        int32_t n, int64_t w0, int splits, int vec) {
+  // workgroup: (window w0 + .. of 64 tokens, split, K|V, head)
+  __shared__ __align__(16) uint8_t stage[4][kStageBytes];
   const int hkv = lv.num_kv_heads;
-  if (wid >= (int64_t)n * hkv * 2) return;
-  const int h = (int)(wid % hkv);
-  const int kv = (int)((wid / hkv) & 1);
-  const int64_t i = wid / hkv / 2;
-  const int bs = lv.block_size;
-  const int lbs = __builtin_ctz(bs);  // block sizes are powers of two
-
-  // The slots of tokens i .. i+63, one per lane, and of token i-1: the run
-  // starting at i is the leading lanes whose slot lies in the same block.
-  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
-  const int64_t blk = slot0 >> lbs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
-  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
-  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
-  const int row0 = (int)(slot0 & (bs - 1));
-  const int nr = min(run, bs - row0);  // rows stay inside the tile even for malformed slots
-  I8Append<IN> ap;
-  ap.issue(lv, kv, h, blk, row0, nr, kv ? v : k, i);
-  (void)ap.finish();
+  const int h = (int)(blockIdx.x % hkv);
+  const int kv = (int)((blockIdx.x / hkv) & 1);
+  const int split = (int)((blockIdx.x / hkv / 2) % splits);
+  const int64_t base = (w0 + (int64_t)(blockIdx.x / hkv / 2 / splits)) * 64;
+  WindowRuns wr;
+  wr.init(lv, slots, n, base, split, splits);
+  const void* src = kv ? v : k;
+  auto whole = [&](const Run& r) { return vec && r.row0 == 0 && (r.nr & 15) == 0; };
+  Run a, b;
+  bool have = wr.next(a);
+  while (have) {
+    if (whole(a)) {
+      append_i8_whole<IN>(lv, kv, h, a.blk, a.nr, src, a.i, stage[threadIdx.x >> 6]);
+      have = wr.next(a);
+      continue;
+    }
+    if (a.nr == 1) {  // up to four consecutive single-token runs together
+      const Run q0 = a;
+      Run q1 = a, q2 = a, q3 = a;
+      int cnt = 1;
+      have = wr.next(a);
+      if (have && a.nr == 1) {
+        q1 = a;
+        cnt = 2;
+        have = wr.next(a);
+        if (have && a.nr == 1) {
+          q2 = a;
+          cnt = 3;
+          have = wr.next(a);
+          if (have && a.nr == 1) {
+            q3 = a;
+            cnt = 4;
+            have = wr.next(a);
+          }
+        }
+      }
+      for (unsigned m = append_i8_rows<IN>(lv, kv, h, q0, q1, q2, q3, cnt, src); m != 0; m &= m - 1) {
+        const int g = __builtin_ctz(m);
+        const Run r = g == 0 ? q0 : g == 1 ? q1 : g == 2 ? q2 : q3;
+        I8Append<IN> p;
+        p.issue(lv, kv, h, r.blk, r.row0, r.nr, src, r.i);
+        (void)p.finish();
+      }
+      continue;
+    }
+    // two short runs at a time: the second's loads are in flight while the
+    // first finishes
+    I8Append<IN> p0;
+    p0.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
+    have = wr.next(b);
+    if (have && !whole(b)) {
+      I8Append<IN> p1;
+      p1.issue(lv, kv, h, b.blk, b.row0, b.nr, src, b.i);
+      (void)p0.finish();
+      (void)p1.finish();
+      have = wr.next(a);
+    } else {
+      (void)p0.finish();
+      a = b;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // H1 for a seal-on-full INT8 layer (lazy quantization, "轻量级推理引擎实战"
-// §三, third design note): one wavefront per (run, head, K|V), runs found as
-// above. A run that leaves its block partly filled is stored as binary16
+// §三, third design note): runs found and dealt to wavefronts as above, one
+// run at a time per wavefront. A run that leaves its block partly filled is stored as binary16
 // rows in the block's FP16 staging tile. The run that writes the block's last
 // row quantizes the whole block -- its staged rows and the run's own, all as
 // binary16 values -- with the section's quantize_block: one scale max|x|/127
@@ -268,59 +553,54 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
 template <int IN>
 __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, const void* k,
                                                           const void* v, const int64_t* slots,
-                                                          int32_t n) {
+                                                          int32_t n, int64_t w0, int splits) {
+  // workgroup: (window w0 + .. of 64 tokens, split, K|V, head)
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = lv.num_kv_heads;
-  if (wid >= (int64_t)n * hkv * 2) return;
-  const int h = (int)(wid % hkv);
-  const int kv = (int)((wid / hkv) & 1);
-  const int64_t i = wid / hkv / 2;
+  const int h = (int)(blockIdx.x % hkv);
+  const int kv = (int)((blockIdx.x / hkv) & 1);
+  const int split = (int)((blockIdx.x / hkv / 2) % splits);
+  const int64_t base = (w0 + (int64_t)(blockIdx.x / hkv / 2 / splits)) * 64;
   const int bs = lv.block_size;
-  const int lbs = __builtin_ctz(bs);
-  const int64_t sj = i + lane < n ? slots[i + lane] : -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)sj) | ((int64_t)__builtin_amdgcn_readfirstlane((int)(sj >> 32)) << 32);
-  const int64_t blk = slot0 >> lbs;
-  if (slot0 < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  if (i > 0 && (slots[i - 1] >> lbs) == blk) return;  // not the first token of its run
-  const uint64_t same = __ballot(sj >= 0 && (sj >> lbs) == blk);
-  const int run = ~same == 0 ? 64 : __builtin_ctzll(~same);
-  const int row0 = (int)(slot0 & (bs - 1));
-  const int nr = min(run, bs - row0);
-
-  const int D = lv.head_dim, ld = __builtin_ctz(D);
-  const void* src = kv ? v : k;
-  uint16_t* t16 = (uint16_t*)(kv ? lv.tail_v : lv.tail_k) + ((size_t)blk * hkv + h) * bs * D;
-  auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
-  // element e of the run (row e >> ld, dim e % D) as binary16 bits
-  auto run_bits = [&](int e) {
-    return __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))));
-  };
-  if (row0 + nr < bs) {  // the block stays partly filled: stage the rows
-    for (int e = lane; e < nr * D; e += 64) t16[off(row0 + (e >> ld), e & (D - 1))] = run_bits(e);
-    return;
-  }
-  // the block is complete: its bs rows as binary16 values, staged or new
-  auto value = [&](int e) {  // element e of the block (row e >> ld)
-    const int t = e >> ld, dd = e & (D - 1);
-    return f16_to_f32(t < row0 ? t16[off(t, dd)] : run_bits(((t - row0) << ld) | dd));
-  };
-  float mx = 0.f;
-  for (int e = lane; e < bs * D; e += 64) mx = fmaxf(mx, fabsf(value(e)));
-  mx = wave_max(mx);
-  const float sc = scale_of(mx);
-  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
-  const int8_t bias = kv ? (int8_t)0x80 : 0;  // V codes are stored biased by 128
-  int qm = 0;
-  for (int e = lane; e < bs * D; e += 64) {
-    const int8_t q = encode(value(e), sc);
-    qm = max(qm, abs((int)q));
-    tile[off(e >> ld, e & (D - 1))] = (int8_t)(q ^ bias);
-  }
-  qm = wave_max_int(qm);
-  if (lane == 0) {
-    (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
-    (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
+  WindowRuns wr;
+  wr.init(lv, slots, n, base, split, splits);
+  for (Run r; wr.next(r);) {
+    const int64_t i = r.i, blk = r.blk;
+    const int row0 = r.row0, nr = r.nr;
+    const int D = lv.head_dim, ld = __builtin_ctz(D);
+    const void* src = kv ? v : k;
+    uint16_t* t16 = (uint16_t*)(kv ? lv.tail_v : lv.tail_k) + ((size_t)blk * hkv + h) * bs * D;
+    auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
+    // element e of the run (row e >> ld, dim e % D) as binary16 bits
+    auto run_bits = [&](int e) {
+      return __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, ((size_t)(i + (e >> ld)) * hkv + h) * D + (e & (D - 1))));
+    };
+    if (row0 + nr < bs) {  // the block stays partly filled: stage the rows
+      for (int e = lane; e < nr * D; e += 64) t16[off(row0 + (e >> ld), e & (D - 1))] = run_bits(e);
+      continue;
+    }
+    // the block is complete: its bs rows as binary16 values, staged or new
+    auto value = [&](int e) {  // element e of the block (row e >> ld)
+      const int t = e >> ld, dd = e & (D - 1);
+      return f16_to_f32(t < row0 ? t16[off(t, dd)] : run_bits(((t - row0) << ld) | dd));
+    };
+    float mx = 0.f;
+    for (int e = lane; e < bs * D; e += 64) mx = fmaxf(mx, fabsf(value(e)));
+    mx = wave_max(mx);
+    const float sc = scale_of(mx);
+    int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * bs * D;
+    const int8_t bias = kv ? (int8_t)0x80 : 0;  // V codes are stored biased by 128
+    int qm = 0;
+    for (int e = lane; e < bs * D; e += 64) {
+      const int8_t q = encode(value(e), sc);
+      qm = max(qm, abs((int)q));
+      tile[off(e >> ld, e & (D - 1))] = (int8_t)(q ^ bias);
+    }
+    qm = wave_max_int(qm);
+    if (lane == 0) {
+      (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
+      (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
+    }
   }
 }
 
@@ -338,23 +618,33 @@ hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int 
       case kBF16: hipLaunchKernelGGL(append_f16_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
       default: return hipErrorInvalidValue;
     }
-  } else if (lv.seal) {
-    const int64_t waves = (int64_t)n * lv.num_kv_heads * 2;
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      default: return hipErrorInvalidValue;
-    }
   } else {
-    const int64_t waves = (int64_t)n * lv.num_kv_heads * 2;
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_i8_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_i8_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_i8_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      default: return hipErrorInvalidValue;
+    // A window's runs are dealt to the 4 wavefronts of `splits` workgroups:
+    // few windows (a decode step's single tokens) get up to 16 wavefronts,
+    // four runs each; many windows one workgroup each.
+    const int64_t windows = ((int64_t)n + 63) / 64;
+    const int64_t per_window = 2 * (int64_t)lv.num_kv_heads;
+    int splits = 1;  // 1, 2 or 4
+    while (splits < 4 && 2 * splits * windows * per_window <= kAppendGroups) splits *= 2;
+    const int64_t chunk = std::max<int64_t>(1, kAppendMaxGrid / (splits * per_window));
+    const int vec = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;  // 16-byte loads of whole runs
+    for (int64_t w0 = 0; w0 < windows; w0 += chunk) {
+      const dim3 grid((unsigned)(std::min(chunk, windows - w0) * splits * per_window));
+      if (lv.seal) {
+        switch (in_dtype) {
+          case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
+          case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
+          case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
+          default: return hipErrorInvalidValue;
+        }
+      } else {
+        switch (in_dtype) {
+          case kF32: hipLaunchKernelGGL(append_i8_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
+          case kF16: hipLaunchKernelGGL(append_i8_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
+          case kBF16: hipLaunchKernelGGL(append_i8_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
+          default: return hipErrorInvalidValue;
+        }
+      }
     }
   }
   return hipGetLastError();

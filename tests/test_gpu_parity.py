@@ -109,6 +109,51 @@ def test_input_dtypes(gpu, kv, in_dtype, q_dtype):
     H.assert_attention_close(res["gpu"], res["ref"])
 
 
+class _OffsetInputs:
+    """A pool whose pkv_append_kv gets K and V starting 4 bytes past a 16-byte
+    boundary (contiguous views into a larger buffer), so the appends take the
+    element-wise loads instead of the 16-byte ones."""
+
+    def __init__(self, pool):
+        self._pool = pool
+
+    def __getattr__(self, name):
+        return getattr(self._pool, name)
+
+    def append_kv(self, layer, k, v, slot_mapping, stream=None):
+        import torch
+
+        def shifted(x):
+            flat = x.reshape(-1)
+            off = 4 // x.element_size()
+            buf = torch.zeros(flat.numel() + 16, dtype=x.dtype, device=x.device)
+            buf[off:off + flat.numel()] = flat
+            out = buf[off:off + flat.numel()].view(x.shape)
+            assert out.data_ptr() % 16 == 4
+            return out
+
+        self._pool.append_kv(layer, shifted(k), shifted(v), slot_mapping, stream)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_append_offset_inputs(gpu, in_dtype, bs):
+    """Prompt appends (whole blocks from row 0, a partial last block) with K/V
+    that are not 16-byte aligned: codes and scales bit-exact with the oracle."""
+    import torch
+    lens = [1, 33, 300, 129]
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + 3,
+                 kv_dtype=orc.I8, in_dtype=in_dtype, q_dtype="f32", sigma_kv="per_head", outlier_p=0.01)
+    case = H.Case(sh, 62190 + bs, [("allocate", s, n) for s, n in enumerate(lens)] + [("append", [1, 3], [40, 17])],
+                  decode_seqs=list(range(len(lens))))
+    pool = H.make_gpu_pool(case)
+    o = H.replay(case, _OffsetInputs(pool))
+    torch.cuda.synchronize()
+    maxb = max((int(pool.length(s)) + bs - 1) // bs for s in case.decode_seqs)
+    H.compare_caches(case, o, pool, case.decode_seqs, maxb)
+    pool.close()
+
+
 SHAPES = [
     # (hq, hkv, dim, bs, lens)
     (2, 2, 128, 16, [1, 33, 300, 1000]),
