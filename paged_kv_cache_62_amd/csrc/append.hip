@@ -62,8 +62,9 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
 // H1 (int8 cache): a run is the maximal group of consecutive tokens that
 // land in one block. Workgroups of (window of 64 tokens, split, K|V, head)
 // find the runs that start in their window and deal them to their
-// wavefronts; a wavefront appends each of its runs alone. Every
-// (block, head, K|V) tile has a single writer, so no atomics are needed.
+// wavefronts; a wavefront appends its runs one after another, single-token
+// runs four at a time. Every (block, head, K|V) tile has a single writer, so
+// no atomics are needed.
 // ---------------------------------------------------------------------------
 
 // One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
@@ -71,14 +72,14 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
 // grow-only scale, old rows re-encoded when it grows (P5 section 3 plus the
 // rule for partly filled blocks). issue() sends its loads without waiting
 // (the block's scale and the largest |code| of its old rows; up to kPre new
-// values per lane), so a wavefront can have two appends in flight;
-// finish() does the rest and returns the new scale. The old codes are read,
-// 16 bytes per load, only when the max grows. Old rows of a K tile are its
-// first row0*D bytes; those of a V tile lie in its first ceil(row0/16)
-// 16-token sub-tiles, where each byte's token is decoded from its offset.
+// values per lane); finish() does the rest and returns the new scale. The old
+// codes are read only when the max grows, 16 bytes per load and kOcBatch
+// loads per lane at a time. Old rows of a K tile are its first row0*D bytes;
+// those of a V tile lie in its first ceil(row0/16) 16-token sub-tiles, where
+// each byte's token is decoded from its offset.
 template <int IN>
 struct I8Append {
-  static constexpr int kMaxChunks = 8;  // per lane: 64 lanes x 8 x 16 bytes covers any tile
+  static constexpr int kOcBatch = 2;  // old-code chunks per lane in flight (a tile is at most 8 per lane)
   static constexpr int kPre = 2;        // new values held per lane (one row of d <= 128)
   const LayerView* lv;
   int kv, h, row0, nr;
@@ -160,31 +161,33 @@ struct I8Append {
         // and store whole chunks back (bytes of rows >= row0 are written back
         // unchanged)
         sc = scale_of(mx);
-        uint4 oc[kMaxChunks];
+        for (int k0 = 0; k0 * 1024 < old_bytes; k0 += kOcBatch) {  // kOcBatch chunks per lane at a time
+          uint4 oc[kOcBatch];
 #pragma unroll
-        for (int k = 0; k < kMaxChunks; ++k) {
-          const int c = lane + 64 * k;
-          oc[k] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
-        }
+          for (int u = 0; u < kOcBatch; ++u) {
+            const int c = lane + 64 * (k0 + u);
+            oc[u] = c * 16 < old_bytes ? *(const uint4*)(tile + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
+          }
 #pragma unroll
-        for (int k = 0; k < kMaxChunks; ++k) {
-          const int c = lane + 64 * k;
-          if (c * 16 < old_bytes) {
-            const uint32_t wm = word_mask(k);
-            uint32_t ws[4] = {oc[k].x ^ bias4, oc[k].y ^ bias4, oc[k].z ^ bias4, oc[k].w ^ bias4};
+          for (int u = 0; u < kOcBatch; ++u) {
+            const int c = lane + 64 * (k0 + u);
+            if (c * 16 < old_bytes) {
+              const uint32_t wm = word_mask(k0 + u);
+              uint32_t ws[4] = {oc[u].x ^ bias4, oc[u].y ^ bias4, oc[u].z ^ bias4, oc[u].w ^ bias4};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+              for (int w = 0; w < 4; ++w) {
 #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                if (wm & (0xFFu << (8 * b))) {
-                  const int code = (int)(int8_t)(ws[w] >> (8 * b));
-                  const int8_t qn = encode((float)code * s_old, sc);
-                  qold = max(qold, abs((int)qn));
-                  ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | ((uint32_t)(uint8_t)qn << (8 * b));
+                for (int b = 0; b < 4; ++b) {
+                  if (wm & (0xFFu << (8 * b))) {
+                    const int code = (int)(int8_t)(ws[w] >> (8 * b));
+                    const int8_t qn = encode((float)code * s_old, sc);
+                    qold = max(qold, abs((int)qn));
+                    ws[w] = (ws[w] & ~(0xFFu << (8 * b))) | ((uint32_t)(uint8_t)qn << (8 * b));
+                  }
                 }
               }
+              *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
             }
-            *(uint4*)(tile + (size_t)c * 16) = make_uint4(ws[0] ^ bias4, ws[1] ^ bias4, ws[2] ^ bias4, ws[3] ^ bias4);
           }
         }
         qold = wave_max_int(qold);
@@ -217,29 +220,39 @@ struct I8Append {
   }
 };
 
-// A run that starts at row 0 and fills whole 16-token sub-tiles (a prompt's
-// full blocks, and its last block's whole sub-tiles) has no old rows: one
-// wavefront reads its nr x D values with 16-byte loads, a row's chunks in
+// A run of several tokens with 16-byte aligned K/V (a prompt's runs): one
+// wavefront reads its nr x D new values with 16-byte loads, a row's chunks in
 // consecutive lanes, keeping the first four loads per lane in registers for
 // the encode pass (runs of up to 16 x 128 bf16 values fit; longer ones are
-// read again from L2). Scale max|x| / 127 and codes as in I8Append. K codes go
-// straight to their row-major place; V codes are gathered in the wavefront's
-// LDS stage in tile order and stored as 16-byte chunks. src must be 16-byte
-// aligned.
+// read again from L2). The scale follows I8Append: max|x| / 127 for a fresh
+// block; kept when the block's old max (its stored largest |code| times its
+// scale) covers the new values. When it does not, nothing is written and the
+// call returns false: the old codes must be re-encoded, which I8Append does.
+// K codes go straight to their row-major places. V codes of a run from row 0
+// that fills whole 16-token sub-tiles are gathered in the wavefront's LDS
+// stage in tile order and stored as 16-byte chunks; other V codes are stored
+// byte by byte.
 constexpr int kStageBytes = 64 * 128;  // the largest tile: bs 64 x d 128 codes
 
-template <int IN>
-__device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int h, int64_t blk, int nr,
-                                                const void* src, int64_t i, uint8_t* stage) {
+template <int IN, bool WHOLE>  // WHOLE: row0 == 0 and nr a multiple of 16
+__device__ __forceinline__ bool append_i8_vec(const LayerView& lv, int kv, int h, int64_t blk, int row0, int nr,
+                                              const void* src, int64_t i, uint8_t* stage) {
   constexpr int EPV = IN == kF32 ? 4 : 8;  // elements per 16-byte load
   constexpr int G = 4;                     // loads per lane in flight
   const int lane = threadIdx.x & 63;
   const int hkv = lv.num_kv_heads, D = lv.head_dim, ld = __builtin_ctz(D);
-  const int per = (nr * D / EPV) >> 6;  // loads per lane: nr*D is a multiple of 1024
+  const size_t at = (size_t)blk * hkv + h;
+  float* sp = (kv ? lv.v_scales : lv.k_scales) + at;
+  int32_t* qp = (kv ? lv.v_qmax : lv.k_qmax) + at;
+  if constexpr (WHOLE) row0 = 0;
+  const int nvec = nr * D / EPV;      // a multiple of 8 (d >= 64); of 64 for WHOLE
+  const int per = (nvec + 63) >> 6;  // loads per lane, the last one masked
   auto addr = [&](int q) {  // vector q of the run: row (q*EPV) / D, dims (q*EPV) % D ..
     const int e = q * EPV;
     return (const uint4*)src + ((((size_t)(i + (e >> ld)) * hkv + h) << ld) + (e & (D - 1))) / EPV;
   };
+  auto in_run = [&](int q) { return q < nvec; };
+  auto load = [&](int q) { return in_run(q) ? *addr(q) : make_uint4(0u, 0u, 0u, 0u); };
   auto unpack = [&](const uint4& r, float* x) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -264,22 +277,31 @@ __device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int
   };
   uint4 r0[G];
 #pragma unroll
-  for (int u = 0; u < G; ++u) r0[u] = u < per ? *addr(u * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+  for (int u = 0; u < G; ++u) r0[u] = load(u * 64 + lane);
+  float s_old = 1.f;
+  int q_old = 0;
+  if (!WHOLE && row0 > 0) {
+    s_old = *sp;
+    q_old = *qp;
+  }
   float mx = 0.f;
   for (int g = G; g < per; g += G) {
     uint4 r[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) r[u] = g + u < per ? *addr((g + u) * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < G; ++u) r[u] = load((g + u) * 64 + lane);
 #pragma unroll
     for (int u = 0; u < G; ++u) mx = absmax(r[u], mx);
   }
 #pragma unroll
   for (int u = 0; u < G; ++u) mx = absmax(r0[u], mx);  // zero padding leaves the max unchanged
-  const float sc = uniform_f(scale_of(wave_max(mx)));
+  mx = uniform_f(wave_max(mx));
+  if (!WHOLE && row0 > 0 && mx > (float)q_old * s_old) return false;  // the max grows
+  const float sc = row0 == 0 ? scale_of(mx) : s_old;
 
-  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + ((size_t)blk * hkv + h) * lv.block_size * D;
+  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + at * lv.block_size * D;
+  const bool staged = WHOLE && kv;
   int qm = 0;
-  if (kv) {  // the stage may still be read by this wavefront's previous run
+  if (staged) {  // the stage may still be read by this wavefront's previous run
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -287,7 +309,7 @@ __device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int
   auto encode_vec = [&](const uint4& r, int q) {
     float x[EPV];
     unpack(r, x);
-    const int e = q * EPV, t = e >> ld, d0 = e & (D - 1);
+    const int e = q * EPV, t = row0 + (e >> ld), d0 = e & (D - 1);
     uint32_t w[EPV / 4] = {};
 #pragma unroll
     for (int j = 0; j < EPV; ++j) {
@@ -295,7 +317,10 @@ __device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int
       qm = max(qm, abs((int)c));
       if (kv) {
         // V byte (t, d0 + j): consecutive dims are d/4 bytes apart in a lane slice
-        stage[v_tile_offset(t, d0, D) + j * (D >> 2)] = (uint8_t)(c ^ (int8_t)0x80);
+        const int64_t o = v_tile_offset(t, d0, D) + j * (D >> 2);
+        const uint8_t b = (uint8_t)(c ^ (int8_t)0x80);
+        if constexpr (WHOLE) stage[o] = b;
+        else tile[o] = (int8_t)b;
       } else {
         w[j >> 2] |= (uint32_t)(uint8_t)c << (8 * (j & 3));
       }
@@ -307,16 +332,16 @@ __device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int
   };
 #pragma unroll
   for (int u = 0; u < G; ++u)
-    if (u < per) encode_vec(r0[u], u * 64 + lane);
+    if (u < per && (WHOLE || in_run(u * 64 + lane))) encode_vec(r0[u], u * 64 + lane);
   for (int g = G; g < per; g += G) {
     uint4 r[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) r[u] = g + u < per ? *addr((g + u) * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < G; ++u) r[u] = load((g + u) * 64 + lane);
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      if (g + u < per) encode_vec(r[u], (g + u) * 64 + lane);
+      if (g + u < per && (WHOLE || in_run((g + u) * 64 + lane))) encode_vec(r[u], (g + u) * 64 + lane);
   }
-  if (kv) {
+  if (staged) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -324,9 +349,10 @@ __device__ __forceinline__ void append_i8_whole(const LayerView& lv, int kv, int
   }
   qm = wave_max_int(qm);
   if (lane == 0) {
-    (kv ? lv.v_scales : lv.k_scales)[(size_t)blk * hkv + h] = sc;
-    (kv ? lv.v_qmax : lv.k_qmax)[(size_t)blk * hkv + h] = qm;
+    *sp = sc;
+    *qp = row0 == 0 ? qm : max(q_old, qm);
   }
+  return true;
 }
 
 // The runs of a call -- maximal groups of consecutive tokens whose slots lie
@@ -484,12 +510,19 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
   WindowRuns wr;
   wr.init(lv, slots, n, base, split, splits);
   const void* src = kv ? v : k;
-  auto whole = [&](const Run& r) { return vec && r.row0 == 0 && (r.nr & 15) == 0; };
-  Run a, b;
+  auto vec_run = [&](const Run& r) { return vec && r.nr > 1; };
+  Run a;
   bool have = wr.next(a);
   while (have) {
-    if (whole(a)) {
-      append_i8_whole<IN>(lv, kv, h, a.blk, a.nr, src, a.i, stage[threadIdx.x >> 6]);
+    if (vec_run(a)) {
+      const bool done = a.row0 == 0 && (a.nr & 15) == 0
+                            ? append_i8_vec<IN, true>(lv, kv, h, a.blk, 0, a.nr, src, a.i, stage[threadIdx.x >> 6])
+                            : append_i8_vec<IN, false>(lv, kv, h, a.blk, a.row0, a.nr, src, a.i, nullptr);
+      if (!done) {
+        I8Append<IN> p;  // the block's max grows: old codes re-encoded
+        p.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
+        (void)p.finish();
+      }
       have = wr.next(a);
       continue;
     }
@@ -522,21 +555,10 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
       }
       continue;
     }
-    // two short runs at a time: the second's loads are in flight while the
-    // first finishes
-    I8Append<IN> p0;
-    p0.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
-    have = wr.next(b);
-    if (have && !whole(b)) {
-      I8Append<IN> p1;
-      p1.issue(lv, kv, h, b.blk, b.row0, b.nr, src, b.i);
-      (void)p0.finish();
-      (void)p1.finish();
-      have = wr.next(a);
-    } else {
-      (void)p0.finish();
-      a = b;
-    }
+    I8Append<IN> p;  // unaligned K/V
+    p.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
+    (void)p.finish();
+    have = wr.next(a);
   }
 }
 

@@ -136,18 +136,23 @@ class _OffsetInputs:
 
 
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("bs", [16, 64])
-def test_append_offset_inputs(gpu, in_dtype, bs):
-    """Prompt appends (whole blocks from row 0, a partial last block) with K/V
-    that are not 16-byte aligned: codes and scales bit-exact with the oracle."""
+@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_append_runs(gpu, in_dtype, bs, aligned):
+    """Prompt appends (whole blocks from row 0, a partial last block), then
+    multi-token and single-token appends into partly filled blocks, whose
+    scales are kept or grow (outliers of +-20), with K/V 16-byte aligned or
+    not: codes and scales bit-exact with the oracle."""
     import torch
-    lens = [1, 33, 300, 129]
-    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + 3,
-                 kv_dtype=orc.I8, in_dtype=in_dtype, q_dtype="f32", sigma_kv="per_head", outlier_p=0.01)
-    case = H.Case(sh, 62190 + bs, [("allocate", s, n) for s, n in enumerate(lens)] + [("append", [1, 3], [40, 17])],
-                  decode_seqs=list(range(len(lens))))
+    lens = [1, 33, 300, 129, 72]
+    script = [("allocate", s, n) for s, n in enumerate(lens)]
+    script += [("append", [1, 3, 4], [40, 17, 9]), ("append", [0, 2, 3], [5, 33, 2]), ("append", [0, 1, 2, 3, 4], [1] * 5)]
+    grow = sum(n for op in script[len(lens):] for n in op[2])
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + grow // bs + 8,
+                 kv_dtype=orc.I8, in_dtype=in_dtype, q_dtype="f32", sigma_kv="per_head", outlier_p=0.02)
+    case = H.Case(sh, 62190 + bs + (0 if aligned else 7), script, decode_seqs=list(range(len(lens))))
     pool = H.make_gpu_pool(case)
-    o = H.replay(case, _OffsetInputs(pool))
+    o = H.replay(case, pool if aligned else _OffsetInputs(pool))
     torch.cuda.synchronize()
     maxb = max((int(pool.length(s)) + bs - 1) // bs for s in case.decode_seqs)
     H.compare_caches(case, o, pool, case.decode_seqs, maxb)
