@@ -376,7 +376,8 @@ struct Run {
 struct WindowRuns {
   int64_t sa, sb, base;
   int lbs, bs;
-  uint64_t mine;  // window positions that start this wavefront's runs
+  uint64_t starts;  // window positions that start a run
+  uint64_t mine;    // those that start this wavefront's runs
 
   __device__ __forceinline__ void init(const LayerView& lv, const int64_t* slots, int32_t n, int64_t base_,
                                        int split, int splits) {
@@ -393,7 +394,7 @@ struct WindowRuns {
     const int64_t up = ((int64_t)__shfl_up((int)(sa >> 32), 1) << 32) | (uint32_t)__shfl_up((int)sa, 1);
     const int64_t pa = lane == 0 ? sprev : up;
     const bool in_pool = sa >= 0 && (sa >> lbs) < lv.num_blocks;
-    const uint64_t starts = __ballot(in_pool && (base + lane == 0 || (pa >> lbs) != (sa >> lbs)));
+    starts = __ballot(in_pool && (base + lane == 0 || (pa >> lbs) != (sa >> lbs)));
     const int per = 64 / ways;  // window positions per wavefront (ways is a power of two)
     mine = starts & (((uint64_t(1) << per) - 1) << (wave * per));  // per <= 16
   }
@@ -403,6 +404,12 @@ struct WindowRuns {
     if (mine == 0) return false;
     const int j = __builtin_ctzll(mine);
     mine &= mine - 1;
+    at(j, run);
+    return true;
+  }
+
+  // The run that starts at window position j (a bit of starts).
+  __device__ __forceinline__ void at(int j, Run& run) const {
     const int64_t slot0 = ((int64_t)__builtin_amdgcn_readlane((int)(sa >> 32), j) << 32) |
                           (uint32_t)__builtin_amdgcn_readlane((int)sa, j);
     const int64_t blk = slot0 >> lbs;
@@ -415,9 +422,114 @@ struct WindowRuns {
     run.blk = blk;
     run.row0 = (int)(slot0 & (bs - 1));
     run.nr = min(len, bs - run.row0);  // rows stay inside the tile even for malformed slots
-    return true;
+  }
+
+  // Starts with no other start in the 31 positions after them in the window:
+  // the only ones whose runs can be 32 tokens or longer.
+  __device__ __forceinline__ uint64_t long_candidates() const {
+    uint64_t y = starts >> 1;  // OR of starts >> 1 .. 31, spread by doubling
+    y |= y >> 1;
+    y |= y >> 2;
+    y |= y >> 4;
+    y |= y >> 8;
+    y |= y >> 15;
+    return starts & ~y;
   }
 };
+
+// A run from row 0 of at least 32 tokens, a multiple of 16 (a prompt's full
+// 64-token blocks, or 32 or 48 rows of one), by a team of `size` wavefronts of the workgroup
+// (four, or two when two such runs of 32 tokens go side by side), wavefronts
+// first .. first + size - 1: each takes an equal share of the run's 16-byte
+// vectors (whole rows: a share holds nr/size >= 8 rows), the maxima meet in
+// LDS, and the V codes are gathered in the team's stage tile, which its
+// threads store as 16-byte chunks. Scale and codes as in append_i8_vec.
+// Every thread of the workgroup makes one such call (two barriers), for its
+// team's run. K/V must be 16-byte aligned; a share is at most kMaxPer loads
+// per lane (size 4 for 64-token runs).
+template <int IN>
+__device__ __forceinline__ void append_i8_coop(const LayerView& lv, int kv, int h, const Run& run, const void* src,
+                                               int first, int size, uint8_t* stage, float* red, int* redq) {
+  constexpr int EPV = IN == kF32 ? 4 : 8;  // elements per 16-byte load
+  constexpr int kMaxPer = IN == kF32 ? 8 : 4;  // loads per lane for a 64 x 128 tile over four wavefronts
+  const int lane = threadIdx.x & 63, w = (threadIdx.x >> 6) - first;  // rank in the team
+  const int hkv = lv.num_kv_heads, D = lv.head_dim, ld = __builtin_ctz(D);
+  const int nr = run.nr;
+  const int64_t i = run.i;
+  const int qw = nr * D / EPV / size;  // vectors per wavefront (a multiple of 32), at most kMaxPer * 64
+  auto addr = [&](int q) {  // vector q of the run: row (q*EPV) / D, dims (q*EPV) % D ..
+    const int e = q * EPV;
+    return (const uint4*)src + ((((size_t)(i + (e >> ld)) * hkv + h) << ld) + (e & (D - 1))) / EPV;
+  };
+  auto unpack = [&](const uint4& r, float* x) {
+    const uint32_t u32[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (IN == kF32) {
+        x[j] = __uint_as_float(u32[j]);
+      } else if constexpr (IN == kF16) {
+        x[2 * j] = f16_to_f32(u32[j] & 0xFFFFu);
+        x[2 * j + 1] = f16_to_f32(u32[j] >> 16);
+      } else {
+        x[2 * j] = bf16_to_f32(u32[j] & 0xFFFFu);
+        x[2 * j + 1] = bf16_to_f32(u32[j] >> 16);
+      }
+    }
+  };
+  uint4 r[kMaxPer];
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u)
+    r[u] = u * 64 + lane < qw ? *addr(w * qw + u * 64 + lane) : make_uint4(0u, 0u, 0u, 0u);
+  float mx = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    float x[EPV];
+    unpack(r[u], x);
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) mx = fmaxf(mx, fabsf(x[j]));
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[first + w] = mx;
+  __syncthreads();
+  float m_all = red[first];
+  for (int t = 1; t < size; ++t) m_all = fmaxf(m_all, red[first + t]);
+  const float sc = uniform_f(scale_of(m_all));
+  const size_t at = (size_t)run.blk * hkv + h;
+  int8_t* tile = (int8_t*)(kv ? lv.v_codes : lv.k_codes) + at * lv.block_size * D;
+  int qm = 0;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    if (u * 64 + lane < qw) {
+      float x[EPV];
+      unpack(r[u], x);
+      const int e = (w * qw + u * 64 + lane) * EPV, t = e >> ld, d0 = e & (D - 1);
+      uint32_t wd[EPV / 4] = {};
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) {
+        const int8_t c = encode(x[j], sc);
+        qm = max(qm, abs((int)c));
+        if (kv) stage[v_tile_offset(t, d0, D) + j * (D >> 2)] = (uint8_t)(c ^ (int8_t)0x80);
+        else wd[j >> 2] |= (uint32_t)(uint8_t)c << (8 * (j & 3));
+      }
+      if (!kv) {
+        if constexpr (EPV == 8) *(uint2*)(tile + k_tile_offset(t, d0, D)) = make_uint2(wd[0], wd[1]);
+        else *(uint32_t*)(tile + k_tile_offset(t, d0, D)) = wd[0];
+      }
+    }
+  }
+  qm = wave_max_int(qm);
+  if (lane == 0) redq[first + w] = qm;
+  __syncthreads();
+  const int tid = w * 64 + lane;  // thread rank in the team
+  if (kv)
+    for (int c = tid; c < (nr * D) >> 4; c += 64 * size) *(uint4*)(tile + 16 * c) = *(const uint4*)(stage + 16 * c);
+  if (tid == 0) {
+    int q_all = redq[first];
+    for (int t = 1; t < size; ++t) q_all = max(q_all, redq[first + t]);
+    (kv ? lv.v_scales : lv.k_scales)[at] = sc;
+    (kv ? lv.v_qmax : lv.k_qmax)[at] = q_all;
+  }
+}
 
 // Maximum over each 16-lane row of the wavefront, in every lane of the row.
 __device__ __forceinline__ float row16_max(float x) {
@@ -507,9 +619,49 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
   const int kv = (int)((blockIdx.x / hkv) & 1);
   const int split = (int)((blockIdx.x / hkv / 2) % splits);
   const int64_t base = (w0 + (int64_t)(blockIdx.x / hkv / 2 / splits)) * 64;
+  __shared__ float red[4];
+  __shared__ int redq[4];
   WindowRuns wr;
   wr.init(lv, slots, n, base, split, splits);
   const void* src = kv ? v : k;
+  if (vec && lv.block_size == 64) {
+    // In 64-token blocks, whole runs of 32 or more tokens from row 0 (at most
+    // two start in a window): the window's k-th such run goes to split
+    // k % splits, where the workgroup's four wavefronts take it together; two
+    // runs of 32 tokens in one workgroup go side by side, two wavefronts each.
+    // Every wavefront finds the same runs, so all take the same barriers.
+    // (In 32-token blocks the runs of a window already keep two wavefronts
+    // busy, and working them jointly measured slower on a serving workload.)
+    uint64_t coop = 0;
+    int k_long = 0, mine_n = 0;
+    Run r0, r1;
+    for (uint64_t m = wr.long_candidates(); m != 0; m &= m - 1) {
+      const int j = __builtin_ctzll(m);
+      Run r;
+      wr.at(j, r);
+      if (r.row0 == 0 && (r.nr & 15) == 0 && r.nr >= 32) {
+        coop |= uint64_t(1) << j;
+        if (k_long % splits == split) {
+          if (mine_n == 0) r0 = r;
+          else r1 = r;
+          ++mine_n;
+        }
+        ++k_long;
+      }
+    }
+    uint8_t* st = &stage[0][0];
+    const int w = threadIdx.x >> 6;
+    if (mine_n == 2 && r0.nr == 32 && r1.nr == 32) {
+      append_i8_coop<IN>(lv, kv, h, w < 2 ? r0 : r1, src, w & 2, 2, w < 2 ? st : st + 2 * kStageBytes, red, redq);
+    } else {
+      if (mine_n >= 1) append_i8_coop<IN>(lv, kv, h, r0, src, 0, 4, st, red, redq);
+      if (mine_n >= 2) append_i8_coop<IN>(lv, kv, h, r1, src, 0, 4, st, red, redq);
+    }
+    if (coop != 0) {
+      wr.mine &= ~coop;
+      __syncthreads();  // the stage is read to its end before any wavefront writes its own part again
+    }
+  }
   auto vec_run = [&](const Run& r) { return vec && r.nr > 1; };
   Run a;
   bool have = wr.next(a);
