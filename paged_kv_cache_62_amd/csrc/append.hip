@@ -10,52 +10,101 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // H1 (binary16 cache): one thread per (token, head, K|V, 8-element chunk);
-// each value rounded to binary16, ties to even.
+// each value rounded to binary16, ties to even. The token index is the
+// fastest, so the four lanes of a quad hold four consecutive tokens of one
+// chunk. 16-bit input is read with one 16-byte load per thread when K/V are
+// 16-byte aligned. A K chunk is one 16-byte store. When a quad's four slots
+// are the rows 4m .. 4m+3 of one block (a prompt's tokens), the V values of
+// one dim for the four tokens are adjacent in the tile (its token index
+// 4tg + ti is fastest): the quad exchanges its values with DPP broadcasts and
+// each lane stores two dims as 8-byte words. Otherwise each lane stores its
+// token's V values two bytes at a time.
 // ---------------------------------------------------------------------------
-// Chunk ch (8 elements) of token i's row of head h, K (kv 0) or V (kv 1),
-// into row `row` of block blk.
-template <int IN>
-__device__ __forceinline__ void append_f16_chunk(const LayerView& lv, int kv, int h, int64_t blk, int row,
-                                                 const void* src, int64_t i, int ch) {
-  const int D = lv.head_dim;
-  const int hkv = lv.num_kv_heads;
-  const size_t sbase = ((size_t)i * hkv + h) * D + ch * 8;
-  uint16_t hv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    hv[e] = __builtin_bit_cast(uint16_t, (_Float16)load_elem<IN>(src, sbase + e));
-  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) +
-                   ((size_t)blk * hkv + h) * lv.block_size * D;
-  if (kv == 0) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)hv[2 * e] | ((uint32_t)hv[2 * e + 1] << 16);
-    *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[v_tile_offset(row, ch * 8 + e, D)] = hv[e];
-  }
+template <int P>  // value of lane P of the quad, in all four lanes
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)dpp_i<P | (P << 2) | (P << 4) | (P << 6)>((int)x);
 }
 
 template <int IN>
 __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, const void* k,
                                                          const void* v, const int64_t* slots,
-                                                         int32_t n) {
-  const int hkv = lv.num_kv_heads;
-  const int chunks = lv.head_dim / 8;
+                                                         int32_t n, int vec) {
+  const int hkv = lv.num_kv_heads, D = lv.head_dim;
+  const int lc = __builtin_ctz(D / 8);          // chunks per row: a power of two
+  const int lbs = __builtin_ctz(lv.block_size);  // block sizes are powers of two
+  const int64_t groups = ((int64_t)n + 3) / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n * hkv * 2 * chunks) return;
-  const int ch = (int)(idx % chunks);
-  int64_t rest = idx / chunks;
-  const int h = (int)(rest % hkv);
-  rest /= hkv;
-  const int kv = (int)(rest & 1);
-  const int64_t i = rest >> 1;
-  const int64_t slot = slots[i];
-  const int64_t blk = slot / lv.block_size;
-  const int row = (int)(slot % lv.block_size);
-  if (slot < 0 || blk >= lv.num_blocks) return;  // not a slot of this pool
-  append_f16_chunk<IN>(lv, kv, h, blk, row, kv ? v : k, i, ch);
+  if (idx >= ((groups * hkv * 2) << (lc + 2))) return;  // whole quads leave together
+  const int ti = (int)(idx & 3);
+  const int ch = (int)((idx >> 2) & ((1 << lc) - 1));
+  const uint32_t rest = (uint32_t)(idx >> (lc + 2));  // (group, K|V, head) < 2^32, checked on the host
+  const int h = (int)(rest % (uint32_t)hkv);
+  const int kv = (int)((rest / (uint32_t)hkv) & 1);
+  const int64_t i = (int64_t)(rest / (uint32_t)hkv >> 1) * 4 + ti;
+  const void* src = kv ? v : k;
+  const int64_t slot = i < n ? slots[i] : -1;
+  const bool ok = slot >= 0 && (slot >> lbs) < lv.num_blocks;  // a slot of this pool
+  const size_t e0 = ((size_t)i * hkv + h) * D + ch * 8;
+  float x[8] = {};
+  if (ok) {
+    if (vec && IN != kF32) {
+      const uint4 r = *((const uint4*)src + e0 / 8);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = IN == kF16 ? f16_to_f32(w[j] & 0xFFFFu) : bf16_to_f32(w[j] & 0xFFFFu);
+        x[2 * j + 1] = IN == kF16 ? f16_to_f32(w[j] >> 16) : bf16_to_f32(w[j] >> 16);
+      }
+    } else if (vec) {
+      const uint4 r0 = *((const uint4*)src + e0 / 4), r1 = *((const uint4*)src + e0 / 4 + 1);
+      const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(w[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = load_elem<IN>(src, e0 + j);
+    }
+  }
+  uint32_t d[4];  // the chunk as binary16 pairs: dims 2j (low half), 2j + 1
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    d[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[2 * j]) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[2 * j + 1]) << 16);
+  const int row = (int)(slot & (lv.block_size - 1));
+  uint16_t* tile = (uint16_t*)(kv ? lv.v_codes : lv.k_codes) + (((size_t)(slot >> lbs) * hkv + h) << lbs) * D;
+  if (kv == 0) {
+    if (ok) *(uint4*)(tile + k_tile_offset(row, ch * 8, D)) = make_uint4(d[0], d[1], d[2], d[3]);
+    return;
+  }
+  // rows 4m .. 4m+3 of one block in lanes 0..3 of the quad (block sizes are multiples of 4)
+  const uint32_t lo0 = quad_bcast<0>((uint32_t)slot), hi0 = quad_bcast<0>((uint32_t)(slot >> 32));
+  const int64_t base = (int64_t)(((uint64_t)hi0 << 32) | lo0);
+  const int mine = ok && slot == base + ti && (base & 3) == 0;
+  const int all = mine & (int)quad_bcast<0>((uint32_t)mine) & (int)quad_bcast<1>((uint32_t)mine) &
+                  (int)quad_bcast<2>((uint32_t)mine) & (int)quad_bcast<3>((uint32_t)mine);
+  if (all) {
+    // lane ti stores dims 2 ti and 2 ti + 1 of the four tokens
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v0 = quad_bcast<0>(d[j]), v1 = quad_bcast<1>(d[j]), v2 = quad_bcast<2>(d[j]),
+                     v3 = quad_bcast<3>(d[j]);
+      if (j == ti) {
+        b[0] = (v0 & 0xFFFFu) | (v1 << 16);
+        b[1] = (v2 & 0xFFFFu) | (v3 << 16);
+        b[2] = (v0 >> 16) | (v1 & 0xFFFF0000u);
+        b[3] = (v2 >> 16) | (v3 & 0xFFFF0000u);
+      }
+    }
+    *(uint2*)(tile + v_tile_offset(row - ti, ch * 8 + 2 * ti, D)) = make_uint2(b[0], b[1]);
+    *(uint2*)(tile + v_tile_offset(row - ti, ch * 8 + 2 * ti + 1, D)) = make_uint2(b[2], b[3]);
+  } else if (ok) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[v_tile_offset(row, ch * 8 + 2 * j, D)] = (uint16_t)(d[j] & 0xFFFFu);
+      tile[v_tile_offset(row, ch * 8 + 2 * j + 1, D)] = (uint16_t)(d[j] >> 16);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -69,8 +118,9 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
 
 // One wavefront appends tokens i .. i+nr-1 (rows of src [token][Hkv][d]) of
 // head h, K (kv 0) or V (kv 1), at rows row0 .. row0+nr-1 of block blk:
-// grow-only scale, old rows re-encoded when it grows (P5 section 3 plus the
-// rule for partly filled blocks). issue() sends its loads without waiting
+// grow-only scale, old rows re-encoded when it grows (the §三 quantizer named
+// at the top of this file, plus the rule for partly filled blocks). issue()
+// sends its loads without waiting
 // (the block's scale and the largest |code| of its old rows; up to kPre new
 // values per lane); finish() does the rest and returns the new scale. The old
 // codes are read only when the max grows, 16 bytes per load and kOcBatch
@@ -80,7 +130,7 @@ __global__ __launch_bounds__(256) void append_f16_kernel(const LayerView lv, con
 template <int IN>
 struct I8Append {
   static constexpr int kOcBatch = 2;  // old-code chunks per lane in flight (a tile is at most 8 per lane)
-  static constexpr int kPre = 2;        // new values held per lane (one row of d <= 128)
+  static constexpr int kPre = 2;      // new values held per lane (one row of d <= 128)
   const LayerView* lv;
   int kv, h, row0, nr;
   int64_t i;
@@ -783,13 +833,16 @@ __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, co
 hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int in_dtype,
                          const int64_t* slots, int32_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
+  const int vec = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;  // 16-byte loads
   if (lv.kv_dtype == kF16) {
-    const int64_t total = (int64_t)n * lv.num_kv_heads * 2 * (lv.head_dim / 8);
+    const int64_t units = ((int64_t)n + 3) / 4 * lv.num_kv_heads * 2;  // (group of 4 tokens, K|V, head)
+    if (units >> 32) return hipErrorInvalidValue;  // more than any device holds
+    const int64_t total = units * (lv.head_dim / 8) * 4;
     const dim3 grid((unsigned)((total + 255) / 256));
     switch (in_dtype) {
-      case kF32: hipLaunchKernelGGL(append_f16_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kF16: hipLaunchKernelGGL(append_f16_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
-      case kBF16: hipLaunchKernelGGL(append_f16_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n); break;
+      case kF32: hipLaunchKernelGGL(append_f16_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n, vec); break;
+      case kF16: hipLaunchKernelGGL(append_f16_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, vec); break;
+      case kBF16: hipLaunchKernelGGL(append_f16_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, vec); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -801,7 +854,6 @@ hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int 
     int splits = 1;  // 1, 2 or 4
     while (splits < 4 && 2 * splits * windows * per_window <= kAppendGroups) splits *= 2;
     const int64_t chunk = std::max<int64_t>(1, kAppendMaxGrid / (splits * per_window));
-    const int vec = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;  // 16-byte loads of whole runs
     for (int64_t w0 = 0; w0 < windows; w0 += chunk) {
       const dim3 grid((unsigned)(std::min(chunk, windows - w0) * splits * per_window));
       if (lv.seal) {
