@@ -284,7 +284,8 @@ struct I8Append {
 // byte by byte.
 constexpr int kStageBytes = 64 * 128;  // the largest tile: bs 64 x d 128 codes
 
-template <int IN, bool WHOLE>  // WHOLE: row0 == 0 and nr a multiple of 16
+template <int IN, bool WHOLE, bool F16R = false>  // WHOLE: row0 == 0 and nr a multiple of 16;
+                                                  // F16R: values rounded to binary16 first (sealing)
 __device__ __forceinline__ bool append_i8_vec(const LayerView& lv, int kv, int h, int64_t blk, int row0, int nr,
                                               const void* src, int64_t i, uint8_t* stage) {
   constexpr int EPV = IN == kF32 ? 4 : 8;  // elements per 16-byte load
@@ -316,6 +317,10 @@ __device__ __forceinline__ bool append_i8_vec(const LayerView& lv, int kv, int h
         x[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
         x[2 * j + 1] = bf16_to_f32(w[j] >> 16);
       }
+    }
+    if constexpr (F16R) {
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) x[j] = (float)(_Float16)x[j];
     }
   };
   auto absmax = [&](const uint4& r, float m) {
@@ -767,17 +772,20 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
 // ---------------------------------------------------------------------------
 // H1 for a seal-on-full INT8 layer (lazy quantization, "轻量级推理引擎实战"
 // §三, third design note): runs found and dealt to wavefronts as above, one
-// run at a time per wavefront. A run that leaves its block partly filled is stored as binary16
-// rows in the block's FP16 staging tile. The run that writes the block's last
-// row quantizes the whole block -- its staged rows and the run's own, all as
-// binary16 values -- with the section's quantize_block: one scale max|x|/127
-// (1.0 for an all-zero head), codes round(x / scale) to even, clamped to
-// [-127, 127]; it stores the codes, the scale and the largest |code|.
+// run at a time per wavefront. A run that leaves its block partly filled is
+// stored as binary16 rows in the block's FP16 staging tile. The run that
+// writes the block's last row quantizes the whole block -- its staged rows and
+// the run's own, all as binary16 values -- with the section's quantize_block:
+// one scale max|x|/127 (1.0 for an all-zero head), codes round(x / scale) to
+// even, clamped to [-127, 127]; it stores the codes, the scale and the largest
+// |code|. A run that fills a whole block from row 0 (a prompt's full blocks)
+// has no staged rows: it takes the 16-byte-load path of the INT8 append with
+// its values rounded to binary16 first, which is the same arithmetic.
 // ---------------------------------------------------------------------------
 template <int IN>
 __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, const void* k,
                                                           const void* v, const int64_t* slots,
-                                                          int32_t n, int64_t w0, int splits) {
+                                                          int32_t n, int64_t w0, int splits, int vec) {
   // workgroup: (window w0 + .. of 64 tokens, split, K|V, head)
   const int lane = threadIdx.x & 63;
   const int hkv = lv.num_kv_heads;
@@ -786,6 +794,7 @@ __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, co
   const int split = (int)((blockIdx.x / hkv / 2) % splits);
   const int64_t base = (w0 + (int64_t)(blockIdx.x / hkv / 2 / splits)) * 64;
   const int bs = lv.block_size;
+  __shared__ __align__(16) uint8_t stage[4][kStageBytes];
   WindowRuns wr;
   wr.init(lv, slots, n, base, split, splits);
   for (Run r; wr.next(r);) {
@@ -793,6 +802,10 @@ __global__ __launch_bounds__(256) void append_seal_kernel(const LayerView lv, co
     const int row0 = r.row0, nr = r.nr;
     const int D = lv.head_dim, ld = __builtin_ctz(D);
     const void* src = kv ? v : k;
+    if (vec && row0 == 0 && nr == bs) {  // a whole block from row 0: no staged rows
+      (void)append_i8_vec<IN, true, true>(lv, kv, h, blk, 0, nr, src, i, stage[threadIdx.x >> 6]);
+      continue;
+    }
     uint16_t* t16 = (uint16_t*)(kv ? lv.tail_v : lv.tail_k) + ((size_t)blk * hkv + h) * bs * D;
     auto off = [&](int t, int dd) { return kv ? v_tile_offset(t, dd, D) : k_tile_offset(t, dd, D); };
     // element e of the run (row e >> ld, dim e % D) as binary16 bits
@@ -858,9 +871,9 @@ hipError_t launch_append(const LayerView& lv, const void* k, const void* v, int 
       const dim3 grid((unsigned)(std::min(chunk, windows - w0) * splits * per_window));
       if (lv.seal) {
         switch (in_dtype) {
-          case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
-          case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
-          case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits); break;
+          case kF32: hipLaunchKernelGGL(append_seal_kernel<kF32>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
+          case kF16: hipLaunchKernelGGL(append_seal_kernel<kF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
+          case kBF16: hipLaunchKernelGGL(append_seal_kernel<kBF16>, grid, dim3(256), 0, stream, lv, k, v, slots, n, w0, splits, vec); break;
           default: return hipErrorInvalidValue;
         }
       } else {
