@@ -226,8 +226,8 @@ struct I8Append {
               uint32_t ws[4] = {oc[u].x ^ bias4, oc[u].y ^ bias4, oc[u].z ^ bias4, oc[u].w ^ bias4};
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
+#pragma unroll 1
+                for (int b = 0; b < 4; ++b) {  // rolled: this path runs only when a scale grows
                   if (wm & (0xFFu << (8 * b))) {
                     const int code = (int)(int8_t)(ws[w] >> (8 * b));
                     const int8_t qn = encode((float)code * s_old, sc);
@@ -385,13 +385,15 @@ __device__ __forceinline__ bool append_i8_vec(const LayerView& lv, int kv, int h
       else *(uint32_t*)(tile + k_tile_offset(t, d0, D)) = w[0];
     }
   };
-#pragma unroll
-  for (int u = 0; u < G; ++u)
-    if (u < per && (WHOLE || in_run(u * 64 + lane))) encode_vec(r0[u], u * 64 + lane);
-  for (int g = G; g < per; g += G) {
+  for (int g = 0; g < per; g += G) {  // the held first group, then groups read again
     uint4 r[G];
+    if (g == 0) {
 #pragma unroll
-    for (int u = 0; u < G; ++u) r[u] = load((g + u) * 64 + lane);
+      for (int u = 0; u < G; ++u) r[u] = r0[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < G; ++u) r[u] = load((g + u) * 64 + lane);
+    }
 #pragma unroll
     for (int u = 0; u < G; ++u)
       if (g + u < per && (WHOLE || in_run((g + u) * 64 + lane))) encode_vec(r[u], (g + u) * 64 + lane);
@@ -664,7 +666,7 @@ __device__ __forceinline__ unsigned append_i8_rows(const LayerView& lv, int kv, 
 }
 
 template <int IN>
-__global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, const void* k,
+__global__ __launch_bounds__(256, 4) void append_i8_kernel(const LayerView lv, const void* k,
                                                         const void* v, const int64_t* slots,
                                                         int32_t n, int64_t w0, int splits, int vec) {
   // workgroup: (window w0 + .. of 64 tokens, split, K|V, head)
@@ -706,36 +708,30 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
     }
     uint8_t* st = &stage[0][0];
     const int w = threadIdx.x >> 6;
-    if (mine_n == 2 && r0.nr == 32 && r1.nr == 32) {
-      append_i8_coop<IN>(lv, kv, h, w < 2 ? r0 : r1, src, w & 2, 2, w < 2 ? st : st + 2 * kStageBytes, red, redq);
-    } else {
-      if (mine_n >= 1) append_i8_coop<IN>(lv, kv, h, r0, src, 0, 4, st, red, redq);
-      if (mine_n >= 2) append_i8_coop<IN>(lv, kv, h, r1, src, 0, 4, st, red, redq);
+    const bool pair = mine_n == 2 && r0.nr == 32 && r1.nr == 32;  // side by side, two wavefronts each
+    for (int c = 0; c < (pair ? 1 : mine_n); ++c) {
+      const bool second = pair ? w >= 2 : c == 1;
+      append_i8_coop<IN>(lv, kv, h, second ? r1 : r0, src, pair ? (w & 2) : 0, pair ? 2 : 4,
+                         pair && second ? st + 2 * kStageBytes : st, red, redq);
     }
     if (coop != 0) {
       wr.mine &= ~coop;
       __syncthreads();  // the stage is read to its end before any wavefront writes its own part again
     }
   }
-  auto vec_run = [&](const Run& r) { return vec && r.nr > 1; };
   Run a;
   bool have = wr.next(a);
   while (have) {
-    if (vec_run(a)) {
+    // runs for the general path (I8Append), as a mask over q0 .. q3
+    Run q0 = a, q1 = a, q2 = a, q3 = a;
+    unsigned general;
+    if (vec && a.nr > 1) {
       const bool done = a.row0 == 0 && (a.nr & 15) == 0
                             ? append_i8_vec<IN, true>(lv, kv, h, a.blk, 0, a.nr, src, a.i, stage[threadIdx.x >> 6])
                             : append_i8_vec<IN, false>(lv, kv, h, a.blk, a.row0, a.nr, src, a.i, nullptr);
-      if (!done) {
-        I8Append<IN> p;  // the block's max grows: old codes re-encoded
-        p.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
-        (void)p.finish();
-      }
+      general = done ? 0u : 1u;  // the block's max grows: old codes re-encoded
       have = wr.next(a);
-      continue;
-    }
-    if (a.nr == 1) {  // up to four consecutive single-token runs together
-      const Run q0 = a;
-      Run q1 = a, q2 = a, q3 = a;
+    } else if (a.nr == 1) {  // up to four consecutive single-token runs together
       int cnt = 1;
       have = wr.next(a);
       if (have && a.nr == 1) {
@@ -753,19 +749,18 @@ __global__ __launch_bounds__(256) void append_i8_kernel(const LayerView lv, cons
           }
         }
       }
-      for (unsigned m = append_i8_rows<IN>(lv, kv, h, q0, q1, q2, q3, cnt, src); m != 0; m &= m - 1) {
-        const int g = __builtin_ctz(m);
-        const Run r = g == 0 ? q0 : g == 1 ? q1 : g == 2 ? q2 : q3;
-        I8Append<IN> p;
-        p.issue(lv, kv, h, r.blk, r.row0, r.nr, src, r.i);
-        (void)p.finish();
-      }
-      continue;
+      general = append_i8_rows<IN>(lv, kv, h, q0, q1, q2, q3, cnt, src);  // those whose max grows
+    } else {
+      general = 1u;  // unaligned K/V
+      have = wr.next(a);
     }
-    I8Append<IN> p;  // unaligned K/V
-    p.issue(lv, kv, h, a.blk, a.row0, a.nr, src, a.i);
-    (void)p.finish();
-    have = wr.next(a);
+    for (unsigned m = general; m != 0; m &= m - 1) {
+      const int g = __builtin_ctz(m);
+      const Run r = g == 0 ? q0 : g == 1 ? q1 : g == 2 ? q2 : q3;
+      I8Append<IN> p;
+      p.issue(lv, kv, h, r.blk, r.row0, r.nr, src, r.i);
+      (void)p.finish();
+    }
   }
 }
 
