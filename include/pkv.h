@@ -176,8 +176,10 @@ pkv_status pkv_pool_free_queue(const pkv_pool* pool, int32_t* out, int32_t cap, 
  * contiguous. slot_mapping: [n_tokens] int64 (device). Tokens that map to
  * one block must be adjacent in the token order with consecutive rows, the
  * first of them at row r meaning the block already holds rows [0, r) -- as
- * produced by pkv_seq_allocate / pkv_seq_append_slots. Slots are not
- * otherwise checked on the device.
+ * produced by pkv_seq_allocate / pkv_seq_append_slots. A slot outside
+ * [0, num_blocks * block_size), e.g. -1 for a padding token, stores nothing;
+ * it must not sit between two tokens of one block (that would split their
+ * run). Slots are not otherwise checked on the device.
  *   F16 cache: each value is rounded to binary16, ties to even.
  *   I8 cache: for each touched (block, head, K|V) with new values X and r
  *   rows already present: if r == 0 the scale is max|X|/127 (1.0 when

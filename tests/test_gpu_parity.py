@@ -163,6 +163,59 @@ def test_append_runs(gpu, kv, in_dtype, bs, aligned):
     pool.close()
 
 
+class _PaddedSlots:
+    """A pool whose pkv_append_kv gets padding tokens (slot -1, random K/V)
+    before the first token, after the last and wherever the block changes."""
+
+    def __init__(self, pool, seed):
+        self._pool = pool
+        self._rng = np.random.default_rng(seed)
+
+    def __getattr__(self, name):
+        return getattr(self._pool, name)
+
+    def append_kv(self, layer, k, v, slot_mapping, stream=None):
+        import torch
+        sl = slot_mapping.cpu().numpy()
+        bs = self._pool.block_size
+        rows, slots = [], []
+        for j, s in enumerate(sl):
+            if j == 0 or s // bs != sl[j - 1] // bs:
+                pad = int(self._rng.integers(1, 3))
+                rows += [-1] * pad
+                slots += [-1] * pad
+            rows.append(j)
+            slots.append(int(s))
+        rows.append(-1)
+        slots.append(-1)
+        idx = torch.tensor([max(r, 0) for r in rows], device=k.device)
+        noise = torch.tensor([r < 0 for r in rows], device=k.device)[:, None, None]
+        kp = torch.where(noise, torch.randn_like(k[idx].float()).to(k.dtype) * 30, k[idx]).contiguous()
+        vp = torch.where(noise, torch.randn_like(v[idx].float()).to(v.dtype) * 30, v[idx]).contiguous()
+        st = torch.tensor(slots, dtype=torch.int64, device=k.device)
+        self._pool.append_kv(layer, kp, vp, st, stream)
+
+
+@pytest.mark.parametrize("kv", [orc.I8, orc.F16])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_append_padding_slots(gpu, kv, bs):
+    """Padding tokens (slot -1) between runs store nothing: the cache is
+    bit-exact with the oracle's, which never sees them."""
+    import torch
+    lens = [32, 32, 1, 33, 300, 129, 72]
+    script = [("allocate", s, n) for s, n in enumerate(lens)]
+    script += [("append", [3, 5, 6], [40, 17, 9]), ("append", [0, 1, 2, 3], [1] * 4)]
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + 12,
+                 kv_dtype=kv, in_dtype="bf16", q_dtype="f32", sigma_kv="per_head", outlier_p=0.02)
+    case = H.Case(sh, 62290 + bs, script, decode_seqs=list(range(len(lens))))
+    pool = H.make_gpu_pool(case)
+    o = H.replay(case, _PaddedSlots(pool, 62290 + bs))
+    torch.cuda.synchronize()
+    maxb = max((int(pool.length(s)) + bs - 1) // bs for s in case.decode_seqs)
+    H.compare_caches(case, o, pool, case.decode_seqs, maxb)
+    pool.close()
+
+
 SHAPES = [
     # (hq, hkv, dim, bs, lens)
     (2, 2, 128, 16, [1, 33, 300, 1000]),
