@@ -609,7 +609,7 @@ __device__ __forceinline__ int row16_max_int(int x) {  // x >= 0
 // its bit is set in the returned mask and I8Append does it whole.
 template <int IN>
 __device__ __forceinline__ unsigned append_i8_rows(const LayerView& lv, int kv, int h, const Run& q0, const Run& q1,
-                                                   const Run& q2, const Run& q3, int cnt, const void* src) {
+                                                   const Run& q2, const Run& q3, int cnt, const void* src, int vec) {
   constexpr int kMaxE = 8;  // d / 16 for d <= 128
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int hkv = lv.num_kv_heads, D = lv.head_dim, E = D >> 4;
@@ -623,10 +623,21 @@ __device__ __forceinline__ unsigned append_i8_rows(const LayerView& lv, int kv, 
   const float s_old = act && row0 > 0 ? *sp : 1.f;
   const int q_old = act && row0 > 0 ? *qp : 0;
   const int d0 = (lane & 15) * E;
-  float x[kMaxE];
+  float x[kMaxE] = {};
+  const size_t e0 = ((size_t)i * hkv + h) * D + d0;
+  if (act && vec && IN != kF32 && E == 8) {  // the lane's 8 values in one 16-byte load
+    const uint4 r = *((const uint4*)src + e0 / 8);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-  for (int e = 0; e < kMaxE; ++e)
-    x[e] = act && e < E ? load_elem<IN>(src, ((size_t)i * hkv + h) * D + d0 + e) : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = IN == kF16 ? f16_to_f32(w[j] & 0xFFFFu) : bf16_to_f32(w[j] & 0xFFFFu);
+      x[2 * j + 1] = IN == kF16 ? f16_to_f32(w[j] >> 16) : bf16_to_f32(w[j] >> 16);
+    }
+  } else if (act) {
+#pragma unroll
+    for (int e = 0; e < kMaxE; ++e)
+      if (e < E) x[e] = load_elem<IN>(src, e0 + e);
+  }
   float mx = 0.f;
 #pragma unroll
   for (int e = 0; e < kMaxE; ++e) mx = fmaxf(mx, fabsf(x[e]));
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(256, 4) void append_i8_kernel(const LayerView lv, c
           }
         }
       }
-      general = append_i8_rows<IN>(lv, kv, h, q0, q1, q2, q3, cnt, src);  // those whose max grows
+      general = append_i8_rows<IN>(lv, kv, h, q0, q1, q2, q3, cnt, src, vec);  // those whose max grows
     } else {
       general = 1u;  // unaligned K/V
       have = wr.next(a);
