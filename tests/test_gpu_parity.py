@@ -139,7 +139,8 @@ class _OffsetInputs:
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("bs", [16, 32, 64])
 @pytest.mark.parametrize("aligned", [True, False])
-def test_append_runs(gpu, kv, in_dtype, bs, aligned):
+@pytest.mark.parametrize("dim", [128, 64])
+def test_append_runs(gpu, kv, in_dtype, bs, aligned, dim):
     """Prompt appends (whole blocks from row 0, done by one wavefront or, at
     32 tokens and more, by a workgroup; a partial last block), then
     multi-token and single-token appends into partly filled blocks, whose
@@ -152,7 +153,7 @@ def test_append_runs(gpu, kv, in_dtype, bs, aligned):
     script = [("allocate", s, n) for s, n in enumerate(lens)]
     script += [("append", [3, 5, 6], [40, 17, 9]), ("append", [2, 4, 5], [5, 33, 2]), ("append", [2, 3, 4, 5, 6], [1] * 5)]
     grow = sum(n for op in script[len(lens):] for n in op[2])
-    sh = H.Shape(layers=1, hq=4, hkv=2, dim=128, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + grow // bs + 8,
+    sh = H.Shape(layers=1, hq=4, hkv=2, dim=dim, bs=bs, nblocks=sum((n + bs - 1) // bs for n in lens) + grow // bs + 8,
                  kv_dtype=kv, in_dtype=in_dtype, q_dtype="f32", sigma_kv="per_head", outlier_p=0.02)
     case = H.Case(sh, 62190 + bs + (0 if aligned else 7), script, decode_seqs=list(range(len(lens))))
     pool = H.make_gpu_pool(case)
