@@ -113,6 +113,9 @@ def parse():
     ap.add_argument("--calibrate-read", type=float, default=0.0, metavar="MIB",
                     help="only time pkv_stream_read of MIB-sized buffers (rotated past the 256 MB MALL) at "
                          "several grid sizes: the practical HBM read floor for a launch of that many bytes")
+    ap.add_argument("--append-timing", action="store_true",
+                    help="only time pkv_append_kv calls (prompts and a decode step's single tokens) into "
+                         "INT8, seal-on-full INT8 and FP16 layers, bf16 input, 8 KV heads, d 128")
     ap.add_argument("--extra", default="auto",
                     help="comma-separated decode workloads also timed in this run and reported under "
                          "'extra_workloads' (no CPU baseline); 'auto' = llama29,llama128 after the default "
@@ -465,6 +468,9 @@ def main():
     if args.calibrate_read:
         print(json.dumps(calibrate_read(args.calibrate_read)), flush=True)
         return
+    if args.append_timing:
+        print(json.dumps(append_timing()), flush=True)
+        return
     stream = torch.cuda.Stream()  # graphs are captured on (and replayed to) a side stream
     with torch.cuda.stream(stream):
         res = (run_serve if args.config in SERVE_CONFIGS else
@@ -492,6 +498,51 @@ def main():
                   file=sys.stderr, flush=True)
             del r
     print(json.dumps(res), flush=True)
+
+
+def append_timing():
+    """pkv_append_kv on its own: for each layer kind, block size and call shape
+    (tokens per sequence x sequences, each sequence allocated to that length
+    and written again every call), 20 calls captured in a HIP graph and
+    replayed between two events; per call time. bf16 K/V, 8 KV heads, d 128."""
+    import torch
+    from paged_kv_cache_62_amd import pkv
+    kinds = [("int8", pkv.PKV_I8, False), ("int8_seal", pkv.PKV_I8, True), ("fp16", pkv.PKV_F16, False)]
+    shapes = [(4096, 1), (500, 8), (512, 4), (300, 16), (64, 16), (1, 4), (1, 32), (1, 128), (1, 512)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(62062)
+    stream = torch.cuda.Stream()
+    rows = []
+    for name, kvd, seal in kinds:
+        for bs in (16, 32, 64):
+            for n, seqs in shapes:
+                pool = pkv.Pool(1, 8, 128, bs, 8192, kvd, seal_on_full=seal)
+                slots = np.concatenate([pool.allocate(s, n) for s in range(seqs)])
+                sl = torch.from_numpy(np.ascontiguousarray(slots)).to("cuda")
+                k = torch.randn(n * seqs, 8, 128, generator=gen, device="cuda").to(torch.bfloat16)
+                v = torch.randn(n * seqs, 8, 128, generator=gen, device="cuda").to(torch.bfloat16)
+                calls = 20
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(stream):
+                    pool.append_kv(0, k, v, sl, stream)
+                    with torch.cuda.graph(g, stream=stream):
+                        for _ in range(calls):
+                            pool.append_kv(0, k, v, sl, stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    g.replay()
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    for _ in range(5):
+                        g.replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                rows.append({"layer": name, "block_size": bs, "tokens_per_seq": n, "seqs": seqs,
+                             "avg_call_us": e0.elapsed_time(e1) * 1e3 / (5 * calls)})
+                del g
+                pool.close()
+    return {"append_timing": rows,
+            "timing": "HIP events around graph replays of 20 pkv_append_kv calls; bf16 K/V, 8 KV heads, d 128"}
 
 
 def calibrate_read(mib):
